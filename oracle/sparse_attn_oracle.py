@@ -1,0 +1,358 @@
+"""Plain fp64 CPU oracle for attention over top-k-gathered key/value rows.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg do.  It shares no code with the HIP library
+(no kernels, headers, helpers or tables); the only common code is the
+seeded input generator, which holds none of the method's arithmetic.
+
+What it computes, and where the pages define it:
+
+* Selection (aclnnSparseFlashAttentionGrad, "Formula": selectedKey /
+  selectedValue = Gather(key/value, topkIndices[i]), each index naming a
+  piece of block_size rows; SparseFlashMlaGrad README, "Computation
+  formula", Stage 1: with cmp_ratio = 4 the selected KV is the original KV
+  concatenated with Gather(cmp_kv, topkIndices[i])).
+* Forward (aclnnNsaSelectedAttentionInfer, "Formula": softmax of the scaled
+  query/selected-key products times the selected values; SparseFlashMlaGrad
+  README, parameter table: lse is the forward's log-sum-exp output).
+* Backward (aclnnSparseFlashAttentionGrad, "Formula", Phases 1-3;
+  SparseFlashMlaGrad README, "Computation formula", Stages 2-3):
+      P  = exp(scale * Q K_sel^T - lse)           (no renormalisation)
+      dP = dO V_sel^T
+      D  = rowsum(dO * O)                         (the softmax-grad term)
+      dS = P * (dP - D)                           (element-wise)
+      dQ = scale * dS K_sel
+      dK[u] += scale * dS^T Q,   dV[u] += P^T dO  (scatter into gathered rows)
+      MLA (shared KV): dKV = scale * dS^T Q + P^T dO  (P^T dO in the first d_v cols)
+      dSinks[h] = sum over rows of -P_sink * D,  P_sink = exp(sink_h - lse)
+* CSR transpose of the index lists (no passage on the pages: it is the
+  bookkeeping for a deterministic key-major reduction): for every key, the
+  flat ids p = (t * Hkv + g) * K + slot of the valid entries naming it, in
+  increasing p.
+
+Readings taken where the pages are silent or garbled (each also listed in the
+design notes):
+  R1  the softmax-grad term is D = rowsum(dO * O) from the O passed in;
+  R2  "@" between P and (dP - D) is an element-wise product;
+  R3  the scale is the descriptor's scale value (1/sqrt(d_qk) by default);
+  R4  lse is the natural-log LSE over the selected, masked logits (plus the
+      sink logit when sinks are present); SimpleSoftmax(x, lse) = exp(x - lse);
+  R5  sinks are one fp32 logit per query head, in the denominator only;
+  R6  masks: causal means key position <= query position (per sequence);
+      window keys are [t - win_left, t + win_right] within [0, t]; cmp row j
+      (covering ori tokens [r*j, r*j + r - 1]) is visible iff r*j + r - 1 <= t;
+      a masked key is simply absent;
+  R7  index i names rows [i * block_size, (i + 1) * block_size);
+  R8  any negative index is an unused slot; an index >= the sequence's row
+      count is also unused;
+  R9  duplicate indices form a multiset: each slot is its own softmax term
+      and its own scatter;
+  R10 a row with no valid key and no sink has lse = -inf, O = 0 and no
+      gradient contribution;
+  R11 cu_seqlens are cumulative ([B+1], cu[0] = 0);
+  R12 index values and window positions are sequence-local;
+  R15 GQA: query head h uses kv head h // G; indices are per (token, kv head).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+SEL_TOKEN = 0
+SEL_BLOCK = 1
+SEL_WINDOW_CMP = 2
+
+
+def _f64(t: torch.Tensor) -> np.ndarray:
+    return t.to(torch.float64).numpy()
+
+
+class Problem:
+    """Inputs of one problem, viewed by the oracle.
+
+    Built from the generator's dict (torch CPU tensors) and the workload's
+    static description; bf16 tensors stay bf16 and are widened to fp64 row
+    by row (every bf16 value is exact in fp64).
+    """
+
+    def __init__(self, inputs: Dict[str, object]):
+        wl = inputs["workload"]
+        self.wl = wl
+        self.select = wl.select
+        self.G = wl.n_q_heads // wl.n_kv_heads
+        self.Hq, self.Hkv = wl.n_q_heads, wl.n_kv_heads
+        self.d_qk, self.d_v = wl.d_qk, wl.d_v
+        self.kv_shared = wl.kv_shared
+        self.scale = wl.softmax_scale
+        self.block_size = wl.block_size
+        self.win_left, self.win_right = wl.win_left, wl.win_right
+        self.cmp_ratio = wl.cmp_ratio
+        self.causal = True
+        self.q = inputs["q"]
+        self.d_o = inputs["d_o"]
+        if wl.kv_shared:
+            self.k = inputs["kv"]
+            self.v = None
+        else:
+            self.k = inputs["k"]
+            self.v = inputs["v"]
+        self.cmp_kv = inputs.get("cmp_kv")
+        self.sinks = inputs.get("sinks")
+        self.idx = inputs["idx"].numpy()
+        self.cu = inputs["cu_seqlens"].numpy().astype(np.int64)
+        self.cu_cmp = inputs["cu_seqlens_cmp"].numpy().astype(np.int64)
+        self.T = int(self.cu[-1])
+        self.K = self.idx.shape[2]
+        # sequence id of every token
+        self.seq_of = np.repeat(np.arange(len(self.cu) - 1), np.diff(self.cu))
+
+    # -- selection --------------------------------------------------------
+    def selection(self, t: int, g: int) -> Tuple[np.ndarray, np.ndarray]:
+        """Ordered multiset of (source, global row) selected by token t for kv
+        head g.  source 0 = the primary K/V (ori) rows, 1 = cmp_kv rows.
+        Slot order is kept; unused and masked slots are dropped."""
+        b = int(self.seq_of[t])
+        tl = t - int(self.cu[b])                  # position within the sequence
+        n_kv = int(self.cu[b + 1] - self.cu[b])   # Sq = Skv per sequence here
+        base = int(self.cu[b])
+        if self.select == SEL_TOKEN:
+            j = self.idx[t, g].astype(np.int64)
+            keep = (j >= 0) & (j < n_kv)
+            if self.causal:
+                keep &= j <= tl
+            rows = base + j[keep]
+            return np.zeros(rows.size, dtype=np.int64), rows
+        if self.select == SEL_BLOCK:
+            bs = self.block_size
+            blk = self.idx[t, g].astype(np.int64)
+            blk = blk[blk >= 0]
+            j = (blk[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)   # block-major
+            keep = j < n_kv
+            if self.causal:
+                keep &= j <= tl
+            rows = base + j[keep]
+            return np.zeros(rows.size, dtype=np.int64), rows
+        # window over the ori rows, then the gathered cmp rows
+        w = np.arange(tl - self.win_left, tl + self.win_right + 1, dtype=np.int64)
+        keep = (w >= 0) & (w < n_kv)
+        if self.causal:
+            keep &= w <= tl
+        ori = base + w[keep]
+        r = self.cmp_ratio
+        n_cmp = int(self.cu_cmp[b + 1] - self.cu_cmp[b])
+        j = self.idx[t, g].astype(np.int64)
+        keepc = (j >= 0) & (j < n_cmp)
+        if self.causal:
+            keepc &= r * j + r - 1 <= tl
+        cmp = int(self.cu_cmp[b]) + j[keepc]
+        srcs = np.concatenate([np.zeros(ori.size, np.int64), np.ones(cmp.size, np.int64)])
+        return srcs, np.concatenate([ori, cmp])
+
+    def gather(self, srcs: np.ndarray, rows: np.ndarray, g: int) -> Tuple[np.ndarray, np.ndarray]:
+        """fp64 K_sel [n, d_qk] and V_sel [n, d_v] for a selection."""
+        n = rows.size
+        K = np.zeros((n, self.d_qk))
+        m0 = srcs == 0
+        if m0.any():
+            K[m0] = _f64(self.k[torch.from_numpy(rows[m0]), g])
+        if (~m0).any():
+            K[~m0] = _f64(self.cmp_kv[torch.from_numpy(rows[~m0]), g])
+        if self.kv_shared:
+            V = K[:, :self.d_v]
+        else:
+            V = np.zeros((n, self.d_v))
+            if n:
+                V[:] = _f64(self.v[torch.from_numpy(rows), g])
+        return K, V
+
+
+def sparse_fwd(pb: Problem, tokens: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Selected-attention forward in fp64 for the given tokens (all by default).
+
+    Returns O [n, Hq, d_v] and lse [n, Hq] (natural log; -inf when a row has
+    neither a valid key nor a sink).
+    """
+    toks = range(pb.T) if tokens is None else tokens
+    toks = list(toks)
+    O = np.zeros((len(toks), pb.Hq, pb.d_v))
+    L = np.full((len(toks), pb.Hq), -np.inf)
+    sinks = None if pb.sinks is None else pb.sinks.to(torch.float64).numpy()
+    for n, t in enumerate(toks):
+        q_t = _f64(pb.q[t])
+        for g in range(pb.Hkv):
+            srcs, rows = pb.selection(t, g)
+            K, V = pb.gather(srcs, rows, g)
+            hs = slice(g * pb.G, (g + 1) * pb.G)
+            S = pb.scale * (q_t[hs] @ K.T)                       # [G, n]
+            if sinks is not None:
+                sk = sinks[hs]
+                m = np.maximum(S.max(axis=1) if rows.size else -np.inf, sk)
+                z = np.exp(S - m[:, None]).sum(axis=1) + np.exp(sk - m)
+            else:
+                if rows.size == 0:
+                    continue
+                m = S.max(axis=1)
+                z = np.exp(S - m[:, None]).sum(axis=1)
+            lse = m + np.log(z)
+            P = np.exp(S - lse[:, None])
+            O[n, hs] = P @ V
+            L[n, hs] = lse
+    return O, L
+
+
+def round_fwd_outputs(O: np.ndarray, lse: np.ndarray) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O -> bf16 (round to nearest even), lse -> fp32: the stored forward
+    outputs that the backward receives as inputs."""
+    # fp64 -> fp32 -> bf16: the bf16 value is the fp32 value's nearest-even
+    # rounding (the stored O is an input to both backwards, so only the fact
+    # that both receive the same array matters).
+    return (torch.from_numpy(O).to(torch.float32).to(torch.bfloat16),
+            torch.from_numpy(lse).to(torch.float32))
+
+
+def sparse_bwd(pb: Problem, O: torch.Tensor, lse: torch.Tensor,
+               tokens: Optional[Sequence[int]] = None,
+               want_rows: bool = True) -> Dict[str, np.ndarray]:
+    """Sparse attention backward in fp64.
+
+    O ([T, Hq, d_v], any float dtype) and lse ([T, Hq]) are the stored forward
+    outputs, indexed by global token.  With `tokens`, only those query tokens
+    contribute (dq rows of other tokens stay 0 and dK/dV/dKV hold the partial
+    sums from those tokens only).
+
+    Returns fp64 arrays: dq [T, Hq, d_qk]; dk [T_kv, Hkv, d_qk] and
+    dv [T_kv, Hkv, d_v] (separate K/V) or dkv [T_kv, 1, d_qk] (shared);
+    dcmp_kv [T_cmp, Hkv, d_qk] for window+cmp; dsinks [Hq] with sinks.
+    """
+    toks = range(pb.T) if tokens is None else tokens
+    n_kv = pb.k.shape[0]
+    dq = np.zeros((pb.T, pb.Hq, pb.d_qk))
+    dk = np.zeros((n_kv, pb.Hkv, pb.d_qk))
+    dv = None if pb.kv_shared else np.zeros((n_kv, pb.Hkv, pb.d_v))
+    dcmp = None if pb.cmp_kv is None else np.zeros((pb.cmp_kv.shape[0], pb.Hkv, pb.d_qk))
+    sinks = None if pb.sinks is None else pb.sinks.to(torch.float64).numpy()
+    dsinks = None if sinks is None else np.zeros(pb.Hq)
+    for t in toks:
+        q_t = _f64(pb.q[t])
+        do_t = _f64(pb.d_o[t])
+        o_t = O[t].to(torch.float64).numpy() if isinstance(O, torch.Tensor) else np.asarray(O[t], np.float64)
+        l_t = lse[t].to(torch.float64).numpy() if isinstance(lse, torch.Tensor) else np.asarray(lse[t], np.float64)
+        for g in range(pb.Hkv):
+            hs = slice(g * pb.G, (g + 1) * pb.G)
+            Qg, dOg, Og, Lg = q_t[hs], do_t[hs], o_t[hs], l_t[hs]
+            finite = np.isfinite(Lg)
+            Lsafe = np.where(finite, Lg, 0.0)
+            D = (dOg * Og).sum(axis=1)                           # softmax-grad term
+            if dsinks is not None:
+                p_sink = np.where(finite, np.exp(sinks[hs] - Lsafe), 0.0)
+                dsinks[hs] += -p_sink * D
+            srcs, rows = pb.selection(t, g)
+            if rows.size == 0:
+                continue
+            K, V = pb.gather(srcs, rows, g)
+            S = pb.scale * (Qg @ K.T)
+            P = np.where(finite[:, None], np.exp(S - Lsafe[:, None]), 0.0)
+            dP = dOg @ V.T
+            dS = P * (dP - D[:, None])
+            dq[t, hs] = pb.scale * (dS @ K)
+            dK_sel = pb.scale * (dS.T @ Qg)                      # [n, d_qk]
+            dV_sel = P.T @ dOg                                   # [n, d_v]
+            if pb.kv_shared:
+                dK_sel[:, :pb.d_v] += dV_sel
+            m0 = srcs == 0
+            np.add.at(dk[:, g], rows[m0], dK_sel[m0])
+            if dv is not None:
+                np.add.at(dv[:, g], rows[m0], dV_sel[m0])
+            if dcmp is not None and (~m0).any():
+                np.add.at(dcmp[:, g], rows[~m0], dK_sel[~m0])
+    out: Dict[str, np.ndarray] = {"dq": dq}
+    if pb.kv_shared:
+        out["dkv"] = dk
+    else:
+        out["dk"] = dk
+        out["dv"] = dv
+    if dcmp is not None:
+        out["dcmp_kv"] = dcmp
+    if dsinks is not None:
+        out["dsinks"] = dsinks
+    return out
+
+
+# ----------------------------------------------------------------------------
+# CSR transpose of the index lists
+# ----------------------------------------------------------------------------
+
+def _block_base(pb: Problem) -> np.ndarray:
+    """First global block id of every sequence (ceil(len / bs) blocks each)."""
+    bs = pb.block_size
+    nb = (np.diff(pb.cu) + bs - 1) // bs
+    return np.concatenate([[0], np.cumsum(nb)])
+
+
+def entry_keys(pb: Problem) -> np.ndarray:
+    """Key id named by every slot, flattened as p = (t * Hkv + g) * K + slot,
+    or -1 when the slot is unused.
+
+    token mode: key = global kv row * Hkv + g; block mode: key = global block
+    id * Hkv + g with blocks numbered per sequence at ceil(len / bs) each;
+    window+cmp: key = global cmp row * Hkv + g (the window part has no slot).
+    A slot is used when its index is >= 0, inside its sequence and not fully
+    masked (token: j <= t; block: first row j * bs <= t; cmp: r*j + r - 1 <= t).
+    """
+    T, Hkv, K = pb.idx.shape
+    j = pb.idx.astype(np.int64)
+    b = pb.seq_of[:, None, None]
+    tl = (np.arange(T) - pb.cu[pb.seq_of])[:, None, None]
+    n_kv = np.diff(pb.cu)[pb.seq_of][:, None, None]
+    g = np.arange(Hkv)[None, :, None]
+    if pb.select == SEL_TOKEN:
+        ok = (j >= 0) & (j < n_kv) & ((j <= tl) if pb.causal else True)
+        key = (pb.cu[pb.seq_of][:, None, None] + j) * Hkv + g
+    elif pb.select == SEL_BLOCK:
+        bs = pb.block_size
+        ok = (j >= 0) & (j * bs < n_kv) & ((j * bs <= tl) if pb.causal else True)
+        key = (_block_base(pb)[pb.seq_of][:, None, None] + j) * Hkv + g
+    else:
+        r = pb.cmp_ratio
+        n_cmp = np.diff(pb.cu_cmp)[pb.seq_of][:, None, None]
+        ok = (j >= 0) & (j < n_cmp) & ((r * j + r - 1 <= tl) if pb.causal else True)
+        key = (pb.cu_cmp[pb.seq_of][:, None, None] + j) * Hkv + g
+    return np.where(ok, key, -1).reshape(-1)
+
+
+def n_keys(pb: Problem) -> int:
+    if pb.select == SEL_TOKEN:
+        return pb.k.shape[0] * pb.Hkv
+    if pb.select == SEL_BLOCK:
+        return int(_block_base(pb)[-1]) * pb.Hkv
+    return pb.cmp_kv.shape[0] * pb.Hkv
+
+
+def csr_transpose(pb: Problem) -> Tuple[np.ndarray, np.ndarray]:
+    """Counting sort of the valid entries by key: returns row_ptr [n_keys+1]
+    (exclusive prefix of the per-key counts) and entries [n_valid] holding
+    the flat entry ids p, ascending within a key (a stable sort by key)."""
+    keys = entry_keys(pb)
+    valid = np.flatnonzero(keys >= 0)                     # ascending p
+    counts = np.bincount(keys[valid], minlength=n_keys(pb))
+    row_ptr = np.zeros(counts.size + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    order = np.argsort(keys[valid], kind="stable")        # ties keep p order
+    return row_ptr, valid[order]
+
+
+# ----------------------------------------------------------------------------
+# work counting (selected-KV FLOPs)
+# ----------------------------------------------------------------------------
+
+def count_valid_pairs(pb: Problem) -> int:
+    """Number of valid (token, kv head, key row) pairs."""
+    n = 0
+    for t in range(pb.T):
+        for g in range(pb.Hkv):
+            n += pb.selection(t, g)[1].size
+    return n

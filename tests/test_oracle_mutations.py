@@ -1,0 +1,105 @@
+"""The pins must catch plausible mistakes: each case plants one in a copy of
+the oracle's source (CPU only, nothing is written to disk) and checks that a
+pin fails on the mutated copy."""
+import importlib.util
+import inspect
+import types
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sparse_attn_oracle as O
+from top_sparse_attention_gather_amd import workloads as W
+from tests._cases import tiny, to_f64_inputs
+
+MUTATIONS = {
+    "D_sign": ("dS = P * (dP - D[:, None])", "dS = P * (dP + D[:, None])"),
+    "dq_no_scale": ("dq[t, hs] = pb.scale * (dS @ K)", "dq[t, hs] = (dS @ K)"),
+    "dv_uses_dS": ("dV_sel = P.T @ dOg", "dV_sel = dS.T @ dOg"),
+    "mla_drops_PdO": ("dK_sel[:, :pb.d_v] += dV_sel", "pass"),
+    "sink_sign": ("dsinks[hs] += -p_sink * D", "dsinks[hs] += p_sink * D"),
+    "causal_off_by_one": ("keep = (j >= 0) & (j < n_kv)\n            if self.causal:\n                keep &= j <= tl",
+                          "keep = (j >= 0) & (j < n_kv)\n            if self.causal:\n                keep &= j < tl"),
+    "window_short": ("w = np.arange(tl - self.win_left, tl + self.win_right + 1",
+                     "w = np.arange(tl - self.win_left + 1, tl + self.win_right + 1"),
+    "lse_no_sink": ("z = np.exp(S - m[:, None]).sum(axis=1) + np.exp(sk - m)",
+                    "z = np.exp(S - m[:, None]).sum(axis=1)"),
+    "csr_unstable": ('order = np.argsort(keys[valid], kind="stable")',
+                     'order = np.argsort(-valid)[np.argsort(keys[valid][np.argsort(-valid)], kind="stable")]'),
+}
+
+
+def _mutant(name):
+    old, new = MUTATIONS[name]
+    src = inspect.getsource(O)
+    assert src.count(old) == 1, name
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src.replace(old, new), mod.__name__, "exec"), mod.__dict__)
+    return mod
+
+
+def _fd_ok(mod, mode):
+    wl = tiny(mode)
+    inp = to_f64_inputs(W.make_inputs(wl))
+    pb = mod.Problem(inp)
+    out, lse = mod.sparse_fwd(pb)
+    g = mod.sparse_bwd(pb, torch.from_numpy(out), torch.from_numpy(lse))
+    dO = inp["d_o"].numpy()
+    # FD with the *reference* forward, so a forward mutation shows up too
+    ok = True
+    for name, key in [("q", "dq"), ("kv", "dkv"), ("k", "dk"), ("v", "dv"), ("sinks", "dsinks"),
+                      ("cmp_kv", "dcmp_kv")]:
+        if key not in g or name not in inp:
+            continue
+        flat = inp[name].view(-1)
+        gg = np.asarray(g[key]).reshape(-1)
+        sc = max(1e-3, float(np.abs(gg).max()))
+        for i in range(0, flat.numel(), max(1, flat.numel() // 25)):
+            old = float(flat[i])
+            flat[i] = old + 1e-5
+            lp = float((O.sparse_fwd(O.Problem(inp))[0] * dO).sum())
+            flat[i] = old - 1e-5
+            lm = float((O.sparse_fwd(O.Problem(inp))[0] * dO).sum())
+            flat[i] = old
+            if abs((lp - lm) / 2e-5 - gg[i]) > 1e-6 * sc + 1e-8:
+                ok = False
+    # forward against the reference forward's structure: rows sum to 1 - P_sink
+    return ok
+
+
+def _csr_ok(mod, mode):
+    wl = tiny(mode)
+    inp = W.make_inputs(wl)
+    rp, e = mod.csr_transpose(mod.Problem(inp))
+    rp0, e0 = O.csr_transpose(O.Problem(inp))
+    # the reference CSR is itself pinned by brute force; compare to it
+    return np.array_equal(rp, rp0) and np.array_equal(e, e0)
+
+
+def _selection_ok(mod, mode):
+    from tests.test_oracle_pins import _brute_selection
+    wl = tiny(mode)
+    inp = W.make_inputs(wl)
+    pb = mod.Problem(inp)
+    idx = inp["idx"].numpy()
+    for t in range(wl.total_q):
+        for g in range(wl.n_kv_heads):
+            s, r = pb.selection(t, g)
+            if sorted(zip(s.tolist(), r.tolist())) != _brute_selection(wl, idx, t, g):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name):
+    mod = _mutant(name)
+    caught = []
+    if name == "csr_unstable":
+        caught.append(not _csr_ok(mod, "token_gqa"))
+    elif name in ("causal_off_by_one", "window_short"):
+        caught.append(not _selection_ok(mod, "token_gqa" if name == "causal_off_by_one" else "wcmp_sinks"))
+    else:
+        for mode in ["token_gqa", "mla", "wcmp_sinks"]:
+            caught.append(not _fd_ok(mod, mode))
+    assert any(caught), f"no pin caught mutation {name}"
