@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-attention backward on one MI355X.
+
+One step = one sparse_attn_bwd call (every kernel of the backward: zero
+fill, D preprocess, the row kernel with the gathers and five MFMA products,
+dSinks, casts) over the MLA shared-KV token-sparse workload (B=1, S=8192,
+64 heads, latent KV 576 with V = first 512, top-2048 per query), inputs
+already resident in HBM.  O and lse come from the library's own forward,
+outside the timed region.
+
+Prints one JSON line: throughput in selected-KV TFLOP/s (sum over valid
+(query, head, key) triples of 2 * (3 * d_qk + 2 * d_v) FLOP), the
+roofline of the dominant kernel (timed on its own stream with HIP events
+recorded by the library around it), and the fp64 oracle timed on a
+bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from top_sparse_attention_gather_amd import binding as B  # noqa: E402
+from top_sparse_attention_gather_amd import workloads as W  # noqa: E402
+
+METRIC = "sparse-attn bwd TFLOP/s (selected-KV FLOPs) and % of bf16 MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def valid_pairs(wl: W.Workload, idx: np.ndarray) -> int:
+    """Valid (token, kv head, key row) pairs from the generated indices,
+    counted from the index lists (any negative slot is unused)."""
+    if wl.select == W.SEL_TOKEN:
+        return int((idx >= 0).sum())
+    return W.expected_pair_count(wl)
+
+
+def flops_per_pair(wl: W.Workload) -> int:
+    return wl.group * 2 * (3 * wl.d_qk + 2 * wl.d_v)
+
+
+def cpu_baseline(inputs, wl, budget_s: float = 15.0, min_tokens: int = 8):
+    """The fp64 oracle backward on the last query tokens (the longest
+    rows), as many as fit the time budget; TFLOP/s of that sample."""
+    from oracle import sparse_attn_oracle as O   # the oracle is only timed here
+    try:
+        import threadpoolctl
+        threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    pb = O.Problem(inputs)
+    T = wl.total_q
+    done, flops, spent = 0, 0, 0.0
+    chunk = min_tokens
+    while spent < budget_s and done < T:
+        toks = list(range(T - done - chunk, T - done))
+        out, lse = O.sparse_fwd(pb, toks)
+        Ob = torch.zeros(T, wl.n_q_heads, wl.d_v, dtype=torch.bfloat16)
+        Lb = torch.zeros(T, wl.n_q_heads, dtype=torch.float32)
+        ob, lb = O.round_fwd_outputs(out, lse)
+        Ob[toks], Lb[toks] = ob, lb
+        t0 = time.perf_counter()
+        O.sparse_bwd(pb, Ob, Lb, tokens=toks)
+        spent += time.perf_counter() - t0
+        pairs = sum(pb.selection(t, g)[1].size for t in toks for g in range(wl.n_kv_heads))
+        flops += pairs * flops_per_pair(wl)
+        done += chunk
+        chunk = min(2 * chunk, 64)
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle sparse_bwd on the last {done} of {T} query tokens of {wl.name} "
+                      f"({flops / 1e12:.3f} TFLOP in {spent:.1f} s, forward excluded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mla_token_8k", choices=W.WORKLOAD_ORDER)
+    ap.add_argument("--dkv-mode", default="atomic", choices=["atomic", "deterministic"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (see the design notes on "
+              "sharding); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    wl = W.WORKLOADS[args.workload]
+    mode = B.DKV_ATOMIC if args.dkv_mode == "atomic" else B.DKV_DETERMINISTIC
+    log(f"[bench] workload {wl.name}: generating inputs")
+    inputs = W.make_inputs(wl, threads=16)
+    idx = inputs["idx"].numpy()
+    pairs = valid_pairs(wl, idx)
+    flop = pairs * flops_per_pair(wl)
+    dev = B.device_tensors(inputs)
+    desc = B.make_desc(wl, mode)
+    log("[bench] forward (inputs O, lse)")
+    dev["o"], dev["lse"] = B.sparse_attn_fwd(desc, dev)
+    outputs = B.alloc_bwd_outputs(desc, dev)
+    ws = torch.empty(max(B.sparse_attn_bwd_workspace_size(desc), 256), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        B.sparse_attn_bwd(desc, dev, outputs, ws)
+    torch.cuda.synchronize()
+
+    ev = B.HipEvents(args.steps)
+    stream = torch.cuda.current_stream()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        B.sparse_attn_bwd(desc, dev, outputs, ws, stream=stream, events=ev.pairs[i])
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    ms = total_ms / args.steps
+    kern_ms = float(np.mean([ev.elapsed_ms(i) for i in range(args.steps)]))
+    ev.close()
+    for k, v in outputs.items():
+        if not torch.isfinite(v.float()).all():
+            raise RuntimeError(f"non-finite values in {k}")
+
+    tflops = flop / (ms * 1e-3) / 1e12
+    kern_tflops = flop / (kern_ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.3f} ms/step, main kernel {kern_ms:.3f} ms, {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(inputs, wl, budget_s=args.cpu_budget)
+        log(f"[bench] cpu baseline {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: B={wl.batch} S={wl.seqlens[0] if wl.batch == 1 else list(wl.seqlens)} "
+                        f"Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} d_qk={wl.d_qk} d_v={wl.d_v} "
+                        f"{'shared-KV ' if wl.kv_shared else ''}top-{wl.topk}",
+            "dkv_mode": args.dkv_mode,
+            "valid_pairs": pairs,
+            "selected_kv_tflop": round(flop / 1e12, 4),
+            "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "bwd_rows_kernel",
+            "bound": "mfma",
+            "achieved": round(kern_tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel_ms": round(kern_ms, 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/sparse_attn.h, the ctypes structures match the C
+layout, and phase-1 validation returns the documented status codes."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from top_sparse_attention_gather_amd import binding as B
+from top_sparse_attention_gather_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(sparse_attn_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_binding_names():
+    assert _declared() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", B.library_path()], capture_output=True, text=True).stdout
+    syms = set(re.findall(r"\bT (\w+)", out))
+    for name in _declared():
+        assert name in syms, name
+        assert hasattr(lib, name)
+
+
+def test_struct_layout_matches_c(tmp_path):
+    """Compile a C probe of the header with gcc and compare sizes/offsets."""
+    fields = {"sa_desc_t": B.SaDesc, "sa_bwd_args_t": B.SaBwdArgs, "sa_fwd_args_t": B.SaFwdArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "sparse_attn.h"', 'int main(void){']
+    for cname, cls in fields.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0;}")
+    c = tmp_path / "probe.c"
+    c.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(c), "-o", str(exe)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        a, b, v = ln.split()
+        got[(a, b)] = int(v)
+    for cname, cls in fields.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
+
+
+def _ws(desc):
+    n = ctypes.c_size_t(0)
+    return B.load().sparse_attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)), n.value
+
+
+def test_phase1_validation_codes():
+    wl = W.WORKLOADS["mla_token_8k"]
+    st, n = _ws(B.make_desc(wl))
+    assert st == 0 and n > 0
+    # fp32 D + fp32 dKV accumulator
+    assert n >= 8192 * 64 * 4 + 8192 * 576 * 4
+    assert _ws(B.make_desc(wl, n_q_heads=63))[0] == 0          # any head count with one kv head
+    cases = {
+        "bad layout": (dict(layout=5), 7),
+        "bad select": (dict(select=9), 7),
+        "bad mode": (dict(dkv_mode=3), 7),
+        "nan scale": (dict(scale=float("nan")), 7),
+        "heads not divisible": (dict(n_kv_heads=3), 2),
+        "d_v > d_qk shared": (dict(d_v=640), 2),
+        "unbuilt head dim": (dict(d_qk=96, d_v=96), 3),
+        "no batch": (dict(batch=0), 2),
+        "topk 0": (dict(topk=0), 2),
+    }
+    for name, (over, code) in cases.items():
+        if name == "heads not divisible":
+            d = B.make_desc(wl, n_q_heads=64, n_kv_heads=3)
+        else:
+            d = B.make_desc(wl, **over)
+        assert _ws(d)[0] == code, name
+    assert B.load().sparse_attn_bwd_workspace_size(None, None) == 1
+    st = B.load().sparse_attn_bwd_workspace_size(ctypes.byref(B.make_desc(wl)), None)
+    assert st == 1
+
+
+def test_window_cmp_requires_shared_kv():
+    wl = W.WORKLOADS["mla_cmp_sinks_varlen"]
+    assert _ws(B.make_desc(wl))[0] == 0
+    assert _ws(B.make_desc(wl, kv_shared=0))[0] == 3
+
+
+def test_empty_query_returns_ok_without_launch():
+    """T == 0: SA_OK and nothing enqueued (safe without a GPU)."""
+    wl = W.small_workload("tiny_token_gqa", seqlens=(0,))
+    d = B.make_desc(wl)
+    a = B.SaBwdArgs()
+    assert B.load().sparse_attn_bwd(ctypes.byref(d), ctypes.byref(a), None, 0, None) == 0
+    f = B.SaFwdArgs()
+    assert B.load().sparse_attn_fwd(ctypes.byref(d), ctypes.byref(f), None) == 0
+
+
+def test_status_strings():
+    for code in range(8):
+        s = B.sparse_attn_status_string(code)
+        assert s.startswith(B.STATUS_NAMES[code])

@@ -1,0 +1,293 @@
+// C ABI of the sparse-attention library: descriptor validation (phase 1),
+// workspace layout, and the launch sequence of each call on the caller's
+// stream (phase 2).  The two-phase shape (size query, then execute) and the
+// status-code returns follow the operator API pattern of the pages
+// (aclnnSparseFlashAttentionGrad, "Function prototype" / first-phase
+// parameter verification); the empty-query early return follows the same
+// page's "Constraints".
+#include <cmath>
+#include <cstring>
+
+#include "../../include/sparse_attn.h"
+#include "sa_launch.h"
+
+namespace {
+
+using sa::BwdBuffers;
+using sa::Params;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+long long total_q(const sa_desc_t* d) {
+  return d->layout == SA_LAYOUT_BSND ? (long long)d->batch * d->seqlen_q : (long long)d->total_q;
+}
+
+long long rows_kv(const sa_desc_t* d) {
+  return d->layout == SA_LAYOUT_BSND ? (long long)d->batch * d->seqlen_kv : (long long)d->total_kv;
+}
+
+long long rows_cmp(const sa_desc_t* d) { return d->select == SA_SEL_WINDOW_CMP ? (long long)d->total_cmp : 0; }
+
+// Phase-1 checks shared by every entry point.
+sa_status_t validate(const sa_desc_t* d) {
+  if (!d) return SA_ERR_NULL_PTR;
+  if (d->layout != SA_LAYOUT_BSND && d->layout != SA_LAYOUT_TND) return SA_ERR_BAD_ARG;
+  if (d->select < SA_SEL_TOKEN || d->select > SA_SEL_WINDOW_CMP) return SA_ERR_BAD_ARG;
+  if (d->dkv_mode != SA_DKV_ATOMIC && d->dkv_mode != SA_DKV_DETERMINISTIC) return SA_ERR_BAD_ARG;
+  if (d->kv_shared != 0 && d->kv_shared != 1) return SA_ERR_BAD_ARG;
+  if (d->mask_causal != 0 && d->mask_causal != 1) return SA_ERR_BAD_ARG;
+  if (d->has_sinks != 0 && d->has_sinks != 1) return SA_ERR_BAD_ARG;
+  if (!std::isfinite(d->scale)) return SA_ERR_BAD_ARG;
+  if (d->batch < 1 || d->n_q_heads < 0 || d->n_kv_heads < 1) return SA_ERR_BAD_SHAPE;
+  if (d->n_q_heads % d->n_kv_heads != 0) return SA_ERR_BAD_SHAPE;
+  if (d->d_qk <= 0 || d->d_v <= 0) return SA_ERR_BAD_SHAPE;
+  if (d->kv_shared && d->d_v > d->d_qk) return SA_ERR_BAD_SHAPE;
+  if (d->layout == SA_LAYOUT_BSND) {
+    if (d->seqlen_q < 0 || d->seqlen_kv < 0) return SA_ERR_BAD_SHAPE;
+  } else {
+    if (d->total_q < 0 || d->total_kv < 0) return SA_ERR_BAD_SHAPE;
+  }
+  if (d->select == SA_SEL_BLOCK) {
+    if (d->block_size < 1 || d->topk < 1) return SA_ERR_BAD_SHAPE;
+  } else if (d->select == SA_SEL_TOKEN) {
+    if (d->topk < 1) return SA_ERR_BAD_SHAPE;
+  } else {
+    if (!d->kv_shared) return SA_ERR_UNSUPPORTED;   // cmp_kv is one shared K(V) tensor
+    if (d->topk < 0 || d->cmp_ratio < 1 || d->win_left < 0 || d->win_right < 0 || d->total_cmp < 0)
+      return SA_ERR_BAD_SHAPE;
+  }
+  const long long T = total_q(d);
+  if (T > 0 && d->n_q_heads > 0 && rows_kv(d) < 1) return SA_ERR_BAD_SHAPE;
+  // row ids must stay below the cmp flag bit and T * n_kv_heads must fit a grid
+  if (rows_kv(d) >= (1LL << 30) || rows_cmp(d) >= (1LL << 30) || T * d->n_kv_heads >= (1LL << 31))
+    return SA_ERR_BAD_SHAPE;
+  const long long npos = d->select == SA_SEL_BLOCK ? (long long)d->topk * d->block_size
+                         : d->select == SA_SEL_TOKEN ? d->topk
+                                                     : (long long)d->win_left + 1 + d->win_right + d->topk;
+  if (npos >= (1LL << 30)) return SA_ERR_BAD_SHAPE;
+  return SA_OK;
+}
+
+struct BwdLayout {
+  size_t D, sink_term, acc_k, acc_v, acc_cmp, total;
+};
+
+BwdLayout bwd_layout(const sa_desc_t* d) {
+  const size_t T = (size_t)total_q(d), Hq = (size_t)d->n_q_heads, Hkv = (size_t)d->n_kv_heads;
+  BwdLayout L;
+  size_t off = 0;
+  L.D = off;
+  off += align_up(T * Hq * sizeof(float));
+  L.sink_term = off;
+  if (d->has_sinks) off += align_up(T * Hq * sizeof(float));
+  L.acc_k = off;
+  off += align_up((size_t)rows_kv(d) * Hkv * d->d_qk * sizeof(float));
+  L.acc_v = off;
+  if (!d->kv_shared) off += align_up((size_t)rows_kv(d) * Hkv * d->d_v * sizeof(float));
+  L.acc_cmp = off;
+  if (d->select == SA_SEL_WINDOW_CMP) off += align_up((size_t)rows_cmp(d) * Hkv * d->d_qk * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+Params make_params(const sa_desc_t* d) {
+  Params p;
+  std::memset(&p, 0, sizeof(p));
+  p.T = (int)total_q(d);
+  p.Hq = d->n_q_heads;
+  p.Hkv = d->n_kv_heads;
+  p.G = d->n_q_heads / d->n_kv_heads;
+  p.dqk = d->d_qk;
+  p.dv = d->d_v;
+  p.topk = d->topk;
+  p.bs = d->select == SA_SEL_BLOCK ? d->block_size : 1;
+  p.select = d->select;
+  p.causal = d->mask_causal;
+  p.win_left = d->win_left;
+  p.win_right = d->win_right;
+  p.cmp_ratio = d->cmp_ratio;
+  p.has_sinks = d->has_sinks;
+  p.shared = d->kv_shared;
+  p.layout = d->layout;
+  p.B = d->batch;
+  p.Sq = d->seqlen_q;
+  p.Skv = d->seqlen_kv;
+  p.scale = d->scale;
+  return p;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+#define SA_TRY_HIP(expr)                     \
+  do {                                       \
+    if ((expr) != hipSuccess) return SA_ERR_HIP; \
+  } while (0)
+
+// Pointer checks shared by forward and backward.
+sa_status_t check_inputs(const sa_desc_t* d, const void* q, const void* k, const void* v, const void* kv,
+                         const void* cmp_kv, const float* sinks, const int32_t* idx, const int32_t* cu_q,
+                         const int32_t* cu_kv, const int32_t* cu_cmp) {
+  if (!q) return SA_ERR_NULL_PTR;
+  if (d->kv_shared ? !kv : (!k || !v)) return SA_ERR_NULL_PTR;
+  if (d->topk > 0 && !idx) return SA_ERR_NULL_PTR;
+  if (d->layout == SA_LAYOUT_TND && (!cu_q || !cu_kv)) return SA_ERR_NULL_PTR;
+  if (d->select == SA_SEL_WINDOW_CMP && (!cmp_kv || !cu_cmp)) return SA_ERR_NULL_PTR;
+  if (d->has_sinks && !sinks) return SA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(d->kv_shared ? kv : k) || (!d->kv_shared && !aligned16(v)) ||
+      (cmp_kv && !aligned16(cmp_kv)))
+    return SA_ERR_MISALIGNED;
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status_t sparse_attn_bwd_workspace_size(const sa_desc_t* desc, size_t* bytes) {
+  if (!bytes) return SA_ERR_NULL_PTR;
+  sa_status_t st = validate(desc);
+  if (st != SA_OK) return st;
+  if (desc->dkv_mode == SA_DKV_DETERMINISTIC) return SA_ERR_UNSUPPORTED;
+  if (!sa::bwd_rows_supported(desc->d_qk, desc->d_v, desc->kv_shared)) return SA_ERR_UNSUPPORTED;
+  *bytes = bwd_layout(desc).total;
+  return SA_OK;
+}
+
+sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a, void* workspace,
+                                  size_t workspace_bytes, void* stream, void* ev_main_start,
+                                  void* ev_main_stop) {
+  size_t need = 0;
+  sa_status_t st = sparse_attn_bwd_workspace_size(desc, &need);
+  if (st != SA_OK) return st;
+  if (!a) return SA_ERR_NULL_PTR;
+  if (total_q(desc) == 0 || desc->n_q_heads == 0) return SA_OK;   // empty query: nothing to do
+  st = check_inputs(desc, a->q, a->k, a->v, a->kv, a->cmp_kv, a->sinks, a->topk_indices, a->cu_seqlens_q,
+                    a->cu_seqlens_kv, a->cu_seqlens_cmp);
+  if (st != SA_OK) return st;
+  if (!a->o || !a->d_o || !a->lse || !a->dq) return SA_ERR_NULL_PTR;
+  if (desc->kv_shared ? !a->dkv : (!a->dk || !a->dv)) return SA_ERR_NULL_PTR;
+  if (desc->select == SA_SEL_WINDOW_CMP && !a->d_cmp_kv) return SA_ERR_NULL_PTR;
+  if (desc->has_sinks && !a->dsinks) return SA_ERR_NULL_PTR;
+  if (!workspace) return SA_ERR_NULL_PTR;
+  if (workspace_bytes < need) return SA_ERR_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return SA_ERR_MISALIGNED;
+  if (!aligned16(a->o) || !aligned16(a->d_o)) return SA_ERR_MISALIGNED;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const BwdLayout L = bwd_layout(desc);
+  char* ws = static_cast<char*>(workspace);
+  Params p = make_params(desc);
+  p.q = static_cast<const bf16*>(a->q);
+  p.k = static_cast<const bf16*>(desc->kv_shared ? a->kv : a->k);
+  p.v = desc->kv_shared ? nullptr : static_cast<const bf16*>(a->v);
+  p.cmp = static_cast<const bf16*>(a->cmp_kv);
+  p.o = static_cast<const bf16*>(a->o);
+  p.dO = static_cast<const bf16*>(a->d_o);
+  p.lse = a->lse;
+  p.sinks = a->sinks;
+  p.idx = a->topk_indices;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_kv = a->cu_seqlens_kv;
+  p.cu_cmp = a->cu_seqlens_cmp;
+
+  BwdBuffers w;
+  w.D = reinterpret_cast<float*>(ws + L.D);
+  w.sink_term = desc->has_sinks ? reinterpret_cast<float*>(ws + L.sink_term) : nullptr;
+  w.acc_k = reinterpret_cast<float*>(ws + L.acc_k);
+  w.acc_v = desc->kv_shared ? nullptr : reinterpret_cast<float*>(ws + L.acc_v);
+  w.acc_cmp = desc->select == SA_SEL_WINDOW_CMP ? reinterpret_cast<float*>(ws + L.acc_cmp) : nullptr;
+  w.dq = static_cast<bf16*>(a->dq);
+  w.dsinks = a->dsinks;
+
+  const size_t Hkv = (size_t)desc->n_kv_heads;
+  const size_t nk = (size_t)rows_kv(desc) * Hkv * desc->d_qk;
+  const size_t nv = desc->kv_shared ? 0 : (size_t)rows_kv(desc) * Hkv * desc->d_v;
+  const size_t nc = (size_t)rows_cmp(desc) * Hkv * desc->d_qk;
+
+  SA_TRY_HIP(sa::launch_fill_zero(w.acc_k, nk, s));
+  if (nv) SA_TRY_HIP(sa::launch_fill_zero(w.acc_v, nv, s));
+  if (nc) SA_TRY_HIP(sa::launch_fill_zero(w.acc_cmp, nc, s));
+  SA_TRY_HIP(sa::launch_preprocess(p, w, s));
+  if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
+  SA_TRY_HIP(sa::launch_bwd_rows(p, w, s));
+  if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
+  if (desc->has_sinks) SA_TRY_HIP(sa::launch_dsinks(p, w, s));
+  SA_TRY_HIP(sa::launch_cast_bf16(w.acc_k, static_cast<bf16*>(desc->kv_shared ? a->dkv : a->dk), nk, s));
+  if (nv) SA_TRY_HIP(sa::launch_cast_bf16(w.acc_v, static_cast<bf16*>(a->dv), nv, s));
+  if (nc) SA_TRY_HIP(sa::launch_cast_bf16(w.acc_cmp, static_cast<bf16*>(a->d_cmp_kv), nc, s));
+  return SA_OK;
+}
+
+sa_status_t sparse_attn_bwd(const sa_desc_t* desc, const sa_bwd_args_t* a, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return sparse_attn_bwd_timed(desc, a, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+sa_status_t sparse_attn_fwd(const sa_desc_t* desc, const sa_fwd_args_t* a, void* stream) {
+  sa_status_t st = validate(desc);
+  if (st != SA_OK) return st;
+  if (!sa::fwd_rows_supported(desc->d_qk, desc->d_v, desc->kv_shared)) return SA_ERR_UNSUPPORTED;
+  if (!a) return SA_ERR_NULL_PTR;
+  if (total_q(desc) == 0 || desc->n_q_heads == 0) return SA_OK;
+  st = check_inputs(desc, a->q, a->k, a->v, a->kv, a->cmp_kv, a->sinks, a->topk_indices, a->cu_seqlens_q,
+                    a->cu_seqlens_kv, a->cu_seqlens_cmp);
+  if (st != SA_OK) return st;
+  if (!a->o || !a->lse) return SA_ERR_NULL_PTR;
+  Params p = make_params(desc);
+  p.q = static_cast<const bf16*>(a->q);
+  p.k = static_cast<const bf16*>(desc->kv_shared ? a->kv : a->k);
+  p.v = desc->kv_shared ? nullptr : static_cast<const bf16*>(a->v);
+  p.cmp = static_cast<const bf16*>(a->cmp_kv);
+  p.sinks = a->sinks;
+  p.idx = a->topk_indices;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_kv = a->cu_seqlens_kv;
+  p.cu_cmp = a->cu_seqlens_cmp;
+  SA_TRY_HIP(sa::launch_fwd_rows(p, static_cast<bf16*>(a->o), a->lse, reinterpret_cast<hipStream_t>(stream)));
+  return SA_OK;
+}
+
+sa_status_t sparse_attn_csr_size(const sa_desc_t* desc, const int32_t* host_cu_seqlens_kv, int64_t* n_keys,
+                                 size_t* workspace_bytes) {
+  (void)desc;
+  (void)host_cu_seqlens_kv;
+  (void)n_keys;
+  (void)workspace_bytes;
+  return SA_ERR_UNSUPPORTED;
+}
+
+sa_status_t sparse_attn_csr_transpose(const sa_desc_t* desc, const int32_t* topk_indices,
+                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                      int32_t* row_ptr, int32_t* entries, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  (void)desc;
+  (void)topk_indices;
+  (void)cu_seqlens_q;
+  (void)cu_seqlens_kv;
+  (void)row_ptr;
+  (void)entries;
+  (void)workspace;
+  (void)workspace_bytes;
+  (void)stream;
+  return SA_ERR_UNSUPPORTED;
+}
+
+const char* sparse_attn_status_string(sa_status_t status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_NULL_PTR: return "SA_ERR_NULL_PTR: a required pointer is NULL";
+    case SA_ERR_BAD_SHAPE: return "SA_ERR_BAD_SHAPE: inconsistent or non-positive sizes";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED: request outside the built kernels";
+    case SA_ERR_WORKSPACE_TOO_SMALL: return "SA_ERR_WORKSPACE_TOO_SMALL: workspace below the phase-1 size";
+    case SA_ERR_MISALIGNED: return "SA_ERR_MISALIGNED: pointer not 16-byte (workspace: 256-byte) aligned";
+    case SA_ERR_HIP: return "SA_ERR_HIP: a HIP launch or runtime call failed";
+    case SA_ERR_BAD_ARG: return "SA_ERR_BAD_ARG: invalid enum value, flag or scale";
+  }
+  return "unknown sa_status_t";
+}
+
+int32_t sparse_attn_version(void) { return 100; }
+
+}  // extern "C"

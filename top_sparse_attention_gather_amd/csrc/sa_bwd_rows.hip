@@ -1,0 +1,363 @@
+// Backward of attention over top-k-gathered KV rows: the row kernel and the
+// small kernels around it (preprocess, zero fill, dSinks reduce, cast).
+//
+// Formulas: aclnnSparseFlashAttentionGrad, "Formula" (Phase 1: dP = dO V^T
+// and dV[u] = P^T dO; Phase 2: dS = P * (dP - softmax-grad(dO, O)); Phase 3:
+// dQ = dS K[u] * scale, dK[u] = dS^T Q * scale) and SparseFlashMlaGrad
+// README, "Computation formula" (Stage 2: P = exp(scale Q KV^T - lse);
+// Stage 3: dKV = dS^T Q scale + P^T dO, dSinks = sum of -P dP softmax(sink)).
+//
+// Row kernel layout: one workgroup of 4 waves owns one (token, kv head)
+// row and a chunk of up to 16 of its query heads.  It compacts the row's
+// selected rows into LDS, then walks them in tiles of 32 keys: gather the
+// tile's K (and V) rows into LDS, S = Q K^T and dP = dO V^T on bf16 MFMA
+// (16x16x32), P and dS element-wise in fp32, dQ += dS K in registers, and
+// the tile's dK/dV (dKV) contributions on MFMA (16x16x16, the head sum is
+// the MFMA's inner dimension) added into fp32 accumulators with atomics.
+#include "sa_launch.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kNT = 32;        // keys per tile
+constexpr int kHC = 16;        // query heads per workgroup
+constexpr int kMaxPos = 2048;  // positions compacted per pass
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O) per (token, head); with sinks also the row's dSinks term
+// -exp(sink_h - lse) * D.  TPR threads per row, 8 bf16 per thread per step.
+template <int TPR>
+__global__ __launch_bounds__(kThreads) void preprocess_kernel(Params p, float* __restrict__ D,
+                                                              float* __restrict__ sink_term) {
+  const int rows = p.T * p.Hq;
+  const int row = blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
+  const int sub = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4* po = reinterpret_cast<const uint4*>(p.o + (size_t)row * p.dv);
+    const uint4* pd = reinterpret_cast<const uint4*>(p.dO + (size_t)row * p.dv);
+    for (int c = sub; c < p.dv / 8; c += TPR) {
+      uint4 a = po[c];
+      uint4 b = pd[c];
+      const bf16* ea = reinterpret_cast<const bf16*>(&a);
+      const bf16* eb = reinterpret_cast<const bf16*>(&b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += (float)ea[i] * (float)eb[i];
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
+  if (row < rows && sub == 0) {
+    D[row] = acc;
+    if (p.has_sinks) {
+      const float l = p.lse[row];
+      const float sk = p.sinks[row % p.Hq];
+      sink_term[row] = (l > -INFINITY) ? -__expf(sk - l) * acc : 0.f;
+    }
+  }
+}
+
+__global__ void fill_zero_kernel(float4* __restrict__ p, size_t n4) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n4;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__global__ void fill_zero_tail_kernel(float* __restrict__ p, size_t n) {
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// dSinks[h] = sum over tokens of sink_term[t][h], in a fixed order (each
+// thread a strided fp64 partial, then a fixed tree) so it is repeatable.
+__global__ __launch_bounds__(kThreads) void dsinks_kernel(Params p, const float* __restrict__ sink_term,
+                                                          float* __restrict__ dsinks) {
+  __shared__ double part[kThreads];
+  const int h = blockIdx.x;
+  double acc = 0.0;
+  for (int t = threadIdx.x; t < p.T; t += kThreads) acc += (double)sink_term[(size_t)t * p.Hq + h];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dsinks[h] = (float)part[0];
+}
+
+__global__ void cast_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = (bf16)src[i];
+}
+
+template <int DQK, int DV, bool SHARED>
+__global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers w) {
+  constexpr int QS = DQK + 8;   // LDS row stride (elements) of Q and K tiles
+  constexpr int VS = DV + 8;    // of dO and V tiles
+  constexpr int PS = kNT + 8;   // of P / dS  [head][key]
+  constexpr int TS = kHC + 4;   // of P^T / dS^T [key][head]
+  constexpr int NQB = DQK / 16; // 16-wide column blocks of dQ / dK
+  constexpr int NVB = DV / 16;
+  constexpr int NQB_W = (NQB + 3) / 4;
+  static_assert(DQK % 32 == 0 && DV % 32 == 0 && DV <= DQK, "head dims");
+
+  __shared__ __attribute__((aligned(16))) bf16 sQ[kHC * QS];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[kHC * VS];
+  __shared__ __attribute__((aligned(16))) bf16 sK[kNT * QS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[SHARED ? 8 : kNT * VS];
+  __shared__ float sS[kHC * kNT];
+  __shared__ float sdP[kHC * kNT];
+  __shared__ __attribute__((aligned(16))) bf16 sP[kHC * PS];
+  __shared__ __attribute__((aligned(16))) bf16 sdS[kHC * PS];
+  __shared__ __attribute__((aligned(16))) bf16 sPt[kNT * TS];
+  __shared__ __attribute__((aligned(16))) bf16 sdSt[kNT * TS];
+  __shared__ int sRows[kMaxPos];
+  __shared__ float sL[kHC], sD[kHC];
+  __shared__ int sWave[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int row = blockIdx.x;                 // (token, kv head)
+  const int t = row / p.Hkv, g = row - t * p.Hkv;
+  const int h0 = g * p.G + blockIdx.y * kHC;  // first query head of the chunk
+  const int Gc = min(kHC, p.G - blockIdx.y * kHC);
+  const SeqPos s = seq_pos(p, t);
+  const int* irow = p.idx + (size_t)row * p.topk;
+  const bf16* Kbase = SHARED ? p.k : p.k;
+  const bf16* Vbase = SHARED ? p.k : p.v;
+  const bf16 zero = (bf16)0.f;
+
+  // Q and dO of the chunk's heads (zero rows past Gc), lse and D.
+  for (int c = tid; c < kHC * (DQK / 8); c += kThreads) {
+    const int h = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (h < Gc) v = *reinterpret_cast<const uint4*>(p.q + ((size_t)t * p.Hq + h0 + h) * DQK + col);
+    *reinterpret_cast<uint4*>(&sQ[h * QS + col]) = v;
+  }
+  for (int c = tid; c < kHC * (DV / 8); c += kThreads) {
+    const int h = c / (DV / 8), col = (c % (DV / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (h < Gc) v = *reinterpret_cast<const uint4*>(p.dO + ((size_t)t * p.Hq + h0 + h) * DV + col);
+    *reinterpret_cast<uint4*>(&sdO[h * VS + col]) = v;
+  }
+  if (tid < kHC) {
+    const bool ok = tid < Gc;
+    sL[tid] = ok ? p.lse[(size_t)t * p.Hq + h0 + tid] : INFINITY;
+    sD[tid] = ok ? w.D[(size_t)t * p.Hq + h0 + tid] : 0.f;
+  }
+
+  f32x4 accQ[NQB_W];
+#pragma unroll
+  for (int i = 0; i < NQB_W; ++i) accQ[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int npos = n_positions(p);
+  for (int pos0 = 0; pos0 < npos; pos0 += kMaxPos) {
+    __syncthreads();
+    const int cnt = compact_positions(p, s, irow, pos0, min(kMaxPos, npos - pos0), sRows, sWave);
+    for (int k0 = 0; k0 < cnt; k0 += kNT) {
+      // ---- gather the tile's K (and V) rows into LDS -----------------------
+      for (int c = tid; c < kNT * (DQK / 8); c += kThreads) {
+        const int r = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (k0 + r < cnt) {
+          const int code = sRows[k0 + r];
+          const bf16* src = (code & kCmpFlag) ? p.cmp + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * DQK
+                                              : Kbase + ((size_t)code * p.Hkv + g) * DQK;
+          v = *reinterpret_cast<const uint4*>(src + col);
+        }
+        *reinterpret_cast<uint4*>(&sK[r * QS + col]) = v;
+      }
+      if (!SHARED) {
+        for (int c = tid; c < kNT * (DV / 8); c += kThreads) {
+          const int r = c / (DV / 8), col = (c % (DV / 8)) * 8;
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (k0 + r < cnt) {
+            const int code = sRows[k0 + r];
+            v = *reinterpret_cast<const uint4*>(Vbase + ((size_t)code * p.Hkv + g) * DV + col);
+          }
+          *reinterpret_cast<uint4*>(&sV[r * VS + col]) = v;
+        }
+      }
+      __syncthreads();
+
+      // ---- S = Q K^T (waves 0,1) and dP = dO V^T (waves 2,3) ---------------
+      {
+        const int kb = wv & 1;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (wv < 2) {
+#pragma unroll 2
+          for (int kk = 0; kk < DQK / 32; ++kk) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[l16 * QS + kk * 32 + lq * 8]);
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sK[(kb * 16 + l16) * QS + kk * 32 + lq * 8]);
+            acc = mfma16x16x32(a, b, acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sS[(lq * 4 + i) * kNT + kb * 16 + l16] = acc[i];
+        } else {
+          const bf16* vt = SHARED ? sK : sV;
+          constexpr int VT = SHARED ? QS : VS;
+#pragma unroll 2
+          for (int kk = 0; kk < DV / 32; ++kk) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sdO[l16 * VS + kk * 32 + lq * 8]);
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&vt[(kb * 16 + l16) * VT + kk * 32 + lq * 8]);
+            acc = mfma16x16x32(a, b, acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sdP[(lq * 4 + i) * kNT + kb * 16 + l16] = acc[i];
+        }
+      }
+      __syncthreads();
+
+      // ---- P = exp(scale S - lse), dS = P (dP - D) --------------------------
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int e = tid * 2 + e2;
+        const int h = e / kNT, j = e % kNT;
+        const float l = sL[h];
+        float pv = 0.f;
+        if (k0 + j < cnt && l > -INFINITY) pv = __expf(sS[e] * p.scale - l);
+        const float ds = pv * (sdP[e] - sD[h]);
+        const bf16 pb = (bf16)pv, db = (bf16)ds;
+        sP[h * PS + j] = pb;
+        sdS[h * PS + j] = db;
+        sPt[j * TS + h] = pb;
+        sdSt[j * TS + h] = db;
+      }
+      __syncthreads();
+
+      // ---- dQ += dS K (column blocks split over the 4 waves) ----------------
+      {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sdS[l16 * PS + lq * 8]);
+#pragma unroll
+        for (int i = 0; i < NQB_W; ++i) {
+          const int cb = wv + 4 * i;
+          if (cb < NQB) {
+            bf16x8 b;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) b[jj] = sK[(lq * 8 + jj) * QS + cb * 16 + l16];
+            accQ[i] = mfma16x16x32(a, b, accQ[i]);
+          }
+        }
+      }
+
+      // ---- dK / dV (dKV) tile contributions -> fp32 atomics -----------------
+      {
+        constexpr int NOB = SHARED ? 2 * NQB : 2 * (NQB + NVB);
+        for (int ob = wv; ob < NOB; ob += 4) {
+          const int kb = ob & 1;
+          int cb = ob >> 1;
+          const bool is_v = !SHARED && cb >= NQB;
+          if (is_v) cb -= NQB;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (!is_v) {
+            const i16x4 a = *reinterpret_cast<const i16x4*>(&sdSt[(kb * 16 + l16) * TS + lq * 4]);
+            i16x4 b;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) b[jj] = bf16_bits(sQ[(lq * 4 + jj) * QS + cb * 16 + l16]);
+            acc = mfma16x16x16(a, b, acc);
+            acc *= p.scale;
+          }
+          if (is_v || (SHARED && cb < NVB)) {
+            const i16x4 a = *reinterpret_cast<const i16x4*>(&sPt[(kb * 16 + l16) * TS + lq * 4]);
+            i16x4 b;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) b[jj] = bf16_bits(sdO[(lq * 4 + jj) * VS + cb * 16 + l16]);
+            acc = mfma16x16x16(a, b, acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = kb * 16 + lq * 4 + i;
+            if (k0 + r < cnt) {
+              const int code = sRows[k0 + r];
+              float* dst;
+              if (is_v) {
+                dst = w.acc_v + ((size_t)code * p.Hkv + g) * DV;
+              } else if (code & kCmpFlag) {
+                dst = w.acc_cmp + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * DQK;
+              } else {
+                dst = w.acc_k + ((size_t)code * p.Hkv + g) * DQK;
+              }
+              unsafeAtomicAdd(dst + cb * 16 + l16, acc[i]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- dQ out (bf16) ---------------------------------------------------------
+#pragma unroll
+  for (int i = 0; i < NQB_W; ++i) {
+    const int cb = wv + 4 * i;
+    if (cb < NQB) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = lq * 4 + r;
+        if (h < Gc) w.dq[((size_t)t * p.Hq + h0 + h) * DQK + cb * 16 + l16] = (bf16)(accQ[i][r] * p.scale);
+      }
+    }
+  }
+}
+
+template <int DQK, int DV, bool SHARED>
+hipError_t launch_rows_t(const Params& p, const BwdBuffers& w, hipStream_t s) {
+  dim3 grid((unsigned)(p.T * p.Hkv), (unsigned)((p.G + kHC - 1) / kHC));
+  hipLaunchKernelGGL((bwd_rows_kernel<DQK, DV, SHARED>), grid, dim3(kThreads), 0, s, p, w);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_rows_supported(int dqk, int dv, int shared) {
+  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 576 && dv == 512);
+}
+
+hipError_t launch_bwd_rows(const Params& p, const BwdBuffers& w, hipStream_t s) {
+  if (p.dqk == 64 && p.dv == 64) return p.shared ? launch_rows_t<64, 64, true>(p, w, s) : launch_rows_t<64, 64, false>(p, w, s);
+  if (p.dqk == 128 && p.dv == 128) return p.shared ? launch_rows_t<128, 128, true>(p, w, s) : launch_rows_t<128, 128, false>(p, w, s);
+  if (p.dqk == 576 && p.dv == 512) return p.shared ? launch_rows_t<576, 512, true>(p, w, s) : launch_rows_t<576, 512, false>(p, w, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_preprocess(const Params& p, const BwdBuffers& w, hipStream_t s) {
+  const int rows = p.T * p.Hq;
+  const int cpr = p.dv / 8;   // 16-byte chunks per row
+  if (cpr >= 64) {
+    hipLaunchKernelGGL(preprocess_kernel<64>, dim3((rows + 3) / 4), dim3(kThreads), 0, s, p, w.D, w.sink_term);
+  } else if (cpr >= 16) {
+    hipLaunchKernelGGL(preprocess_kernel<16>, dim3((rows + 15) / 16), dim3(kThreads), 0, s, p, w.D, w.sink_term);
+  } else {
+    hipLaunchKernelGGL(preprocess_kernel<8>, dim3((rows + 31) / 32), dim3(kThreads), 0, s, p, w.D, w.sink_term);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* ptr, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t n4 = n / 4;
+  if (n4) {
+    const unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<float4*>(ptr), n4);
+  }
+  const size_t rest = n - n4 * 4;
+  if (rest) hipLaunchKernelGGL(fill_zero_tail_kernel, dim3(1), dim3(64), 0, s, ptr + n4 * 4, rest);
+  return hipGetLastError();
+}
+
+hipError_t launch_dsinks(const Params& p, const BwdBuffers& w, hipStream_t s) {
+  hipLaunchKernelGGL(dsinks_kernel, dim3(p.Hq), dim3(kThreads), 0, s, p, w.sink_term, w.dsinks);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(const float* src, bf16* dst, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 16384);
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace sa

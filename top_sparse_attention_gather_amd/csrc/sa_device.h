@@ -1,0 +1,164 @@
+// Device-side types and helpers shared by the gfx950 kernels of the
+// sparse-attention library.  Only included by the library's .hip files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace sa {
+
+constexpr int kSelToken = 0;
+constexpr int kSelBlock = 1;
+constexpr int kSelWindowCmp = 2;
+constexpr int kLayoutBSND = 0;
+constexpr int kLayoutTND = 1;
+
+// A selected row is encoded as its global row index; rows of cmp_kv carry
+// this flag; -1 marks an unused position.
+constexpr int kCmpFlag = 1 << 30;
+
+// Problem description handed to every kernel by value.  Element strides:
+// q/dq [T][Hq][dqk], o/dO [T][Hq][dv], k [rows][Hkv][dqk], v [rows][Hkv][dv],
+// cmp [cmp_rows][Hkv][dqk], lse/D [T][Hq], idx [T][Hkv][topk].
+struct Params {
+  int T, Hq, Hkv, G, dqk, dv, topk, bs, select, causal, win_left, win_right, cmp_ratio;
+  int has_sinks, shared, layout, B, Sq, Skv;
+  float scale;
+  const bf16* q;
+  const bf16* k;      // K rows, or the shared KV rows
+  const bf16* v;      // separate V rows (null when shared)
+  const bf16* cmp;    // cmp_kv rows (window+cmp)
+  const bf16* o;
+  const bf16* dO;
+  const float* lse;
+  const float* sinks;
+  const int* idx;
+  const int* cu_q;
+  const int* cu_kv;
+  const int* cu_cmp;
+};
+
+// Where a query token sits: its sequence, local position, and the first
+// row / row count of its sequence in the kv and cmp tables.
+struct SeqPos {
+  int b, tl, kv_base, kv_len, cmp_base, cmp_len;
+};
+
+__device__ __forceinline__ SeqPos seq_pos(const Params& p, int t) {
+  SeqPos s;
+  if (p.layout == kLayoutBSND) {
+    s.b = t / p.Sq;
+    s.tl = t - s.b * p.Sq;
+    s.kv_base = s.b * p.Skv;
+    s.kv_len = p.Skv;
+  } else {
+    int lo = 0, hi = p.B;           // largest b with cu_q[b] <= t
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (p.cu_q[mid] <= t) lo = mid; else hi = mid;
+    }
+    s.b = lo;
+    s.tl = t - p.cu_q[lo];
+    s.kv_base = p.cu_kv[lo];
+    s.kv_len = p.cu_kv[lo + 1] - p.cu_kv[lo];
+  }
+  if (p.select == kSelWindowCmp) {
+    s.cmp_base = p.cu_cmp[s.b];
+    s.cmp_len = p.cu_cmp[s.b + 1] - p.cu_cmp[s.b];
+  } else {
+    s.cmp_base = 0;
+    s.cmp_len = 0;
+  }
+  return s;
+}
+
+// Number of virtual positions of a (token, kv head) row before masking:
+// index slots (token), slots * block_size rows (block), or the window
+// followed by the cmp slots (window+cmp).
+__device__ __forceinline__ int n_positions(const Params& p) {
+  if (p.select == kSelToken) return p.topk;
+  if (p.select == kSelBlock) return p.topk * p.bs;
+  return p.win_left + 1 + p.win_right + p.topk;
+}
+
+// Decode virtual position `pos` of row (t, g): the encoded selected row, or
+// -1 when the slot is unused or masked.  `irow` points at idx[t][g][0].
+__device__ __forceinline__ int decode_position(const Params& p, const SeqPos& s,
+                                               const int* __restrict__ irow, int pos) {
+  if (p.select == kSelToken) {
+    int j = irow[pos];
+    if (j < 0 || j >= s.kv_len || (p.causal && j > s.tl)) return -1;
+    return s.kv_base + j;
+  }
+  if (p.select == kSelBlock) {
+    int slot = pos / p.bs;
+    int blk = irow[slot];
+    if (blk < 0) return -1;
+    long long j = (long long)blk * p.bs + (pos - slot * p.bs);
+    if (j >= s.kv_len || (p.causal && j > s.tl)) return -1;
+    return s.kv_base + (int)j;
+  }
+  const int nwin = p.win_left + 1 + p.win_right;
+  if (pos < nwin) {
+    int j = s.tl - p.win_left + pos;
+    if (j < 0 || j >= s.kv_len || (p.causal && j > s.tl)) return -1;
+    return s.kv_base + j;
+  }
+  int j = irow[pos - nwin];
+  if (j < 0 || j >= s.cmp_len) return -1;
+  if (p.causal && (long long)p.cmp_ratio * j + p.cmp_ratio - 1 > s.tl) return -1;
+  return (s.cmp_base + j) | kCmpFlag;
+}
+
+// Compact positions [pos0, pos0 + n) of a row into sRows, keeping position
+// order; returns the number of used positions (the same in every thread).
+// Block of 256 threads (4 waves); sWave holds 4 ints.  Ends with a barrier.
+__device__ __forceinline__ int compact_positions(const Params& p, const SeqPos& s,
+                                                 const int* __restrict__ irow, int pos0, int n,
+                                                 int* sRows, int* sWave) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int total = 0;
+  for (int base = 0; base < n; base += 256) {
+    const int pos = base + tid;
+    int code = -1;
+    if (pos < n) code = decode_position(p, s, irow, pos0 + pos);
+    const unsigned long long m = __ballot(code >= 0);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) sWave[w] = __popcll(m);
+    __syncthreads();
+    int off = total;
+    for (int i = 0; i < w; ++i) off += sWave[i];
+    if (code >= 0) sRows[off + before] = code;
+    total += sWave[0] + sWave[1] + sWave[2] + sWave[3];
+    __syncthreads();
+  }
+  return total;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x16(const i16x4& a, const i16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ short bf16_bits(bf16 x) { return __builtin_bit_cast(short, x); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace sa

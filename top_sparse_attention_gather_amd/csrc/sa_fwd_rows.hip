@@ -1,0 +1,201 @@
+// Selected-attention forward: O = softmax(scale q K_sel^T [, sink]) V_sel and
+// lse = log-sum-exp of the same logits (aclnnNsaSelectedAttentionInfer,
+// "Formula"; the lse output named in the SparseFlashMlaGrad parameter table).
+//
+// One workgroup of 4 waves owns one (token, kv head) row and up to 16 of its
+// query heads, compacts the row's selected rows into LDS and walks them in
+// tiles of 32 keys with an online softmax: S = Q K^T on bf16 MFMA, running
+// max / sum per head in LDS, O += P V on MFMA with the fp32 accumulator in
+// registers.  A sink logit enters as the initial running max with sum 1.
+#include "sa_launch.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kNT = 32;
+constexpr int kHC = 16;
+constexpr int kMaxPos = 2048;
+
+template <int DQK, int DV, bool SHARED>
+__global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __restrict__ out_o,
+                                                            float* __restrict__ out_lse) {
+  constexpr int QS = DQK + 8;
+  constexpr int VS = DV + 8;
+  constexpr int PS = kNT + 8;
+  constexpr int NVB = DV / 16;
+  constexpr int NVB_W = (NVB + 3) / 4;
+  static_assert(DQK % 32 == 0 && DV % 32 == 0 && DV <= DQK, "head dims");
+
+  __shared__ __attribute__((aligned(16))) bf16 sQ[kHC * QS];
+  __shared__ __attribute__((aligned(16))) bf16 sK[kNT * QS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[SHARED ? 8 : kNT * VS];
+  __shared__ float sS[kHC * kNT];
+  __shared__ __attribute__((aligned(16))) bf16 sP[kHC * PS];
+  __shared__ float sM[kHC], sL[kHC], sAlpha[kHC];
+  __shared__ int sRows[kMaxPos];
+  __shared__ int sWave[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int row = blockIdx.x;
+  const int t = row / p.Hkv, g = row - t * p.Hkv;
+  const int h0 = g * p.G + blockIdx.y * kHC;
+  const int Gc = min(kHC, p.G - blockIdx.y * kHC);
+  const SeqPos s = seq_pos(p, t);
+  const int* irow = p.idx + (size_t)row * p.topk;
+  const bf16* Vbase = SHARED ? p.k : p.v;
+
+  for (int c = tid; c < kHC * (DQK / 8); c += kThreads) {
+    const int h = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (h < Gc) v = *reinterpret_cast<const uint4*>(p.q + ((size_t)t * p.Hq + h0 + h) * DQK + col);
+    *reinterpret_cast<uint4*>(&sQ[h * QS + col]) = v;
+  }
+  if (tid < kHC) {
+    // running max and sum; a sink logit starts them at (sink, 1)
+    const bool sk = p.has_sinks && tid < Gc;
+    sM[tid] = sk ? p.sinks[h0 + tid] : -INFINITY;
+    sL[tid] = sk ? 1.f : 0.f;
+  }
+
+  f32x4 accO[NVB_W];
+#pragma unroll
+  for (int i = 0; i < NVB_W; ++i) accO[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int npos = n_positions(p);
+  for (int pos0 = 0; pos0 < npos; pos0 += kMaxPos) {
+    __syncthreads();
+    const int cnt = compact_positions(p, s, irow, pos0, min(kMaxPos, npos - pos0), sRows, sWave);
+    for (int k0 = 0; k0 < cnt; k0 += kNT) {
+      for (int c = tid; c < kNT * (DQK / 8); c += kThreads) {
+        const int r = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (k0 + r < cnt) {
+          const int code = sRows[k0 + r];
+          const bf16* src = (code & kCmpFlag) ? p.cmp + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * DQK
+                                              : p.k + ((size_t)code * p.Hkv + g) * DQK;
+          v = *reinterpret_cast<const uint4*>(src + col);
+        }
+        *reinterpret_cast<uint4*>(&sK[r * QS + col]) = v;
+      }
+      if (!SHARED) {
+        for (int c = tid; c < kNT * (DV / 8); c += kThreads) {
+          const int r = c / (DV / 8), col = (c % (DV / 8)) * 8;
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (k0 + r < cnt) {
+            const int code = sRows[k0 + r];
+            v = *reinterpret_cast<const uint4*>(Vbase + ((size_t)code * p.Hkv + g) * DV + col);
+          }
+          *reinterpret_cast<uint4*>(&sV[r * VS + col]) = v;
+        }
+      }
+      __syncthreads();
+
+      if (wv < 2) {
+        const int kb = wv;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int kk = 0; kk < DQK / 32; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[l16 * QS + kk * 32 + lq * 8]);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sK[(kb * 16 + l16) * QS + kk * 32 + lq * 8]);
+          acc = mfma16x16x32(a, b, acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sS[(lq * 4 + i) * kNT + kb * 16 + l16] = acc[i];
+      }
+      __syncthreads();
+
+      // online softmax: 16 threads per head, 2 keys each
+      {
+        const int h = tid >> 4, part = tid & 15;
+        const float m_old = sM[h];
+        float v0 = -INFINITY, v1 = -INFINITY;
+        if (k0 + part * 2 < cnt) v0 = sS[h * kNT + part * 2] * p.scale;
+        if (k0 + part * 2 + 1 < cnt) v1 = sS[h * kNT + part * 2 + 1] * p.scale;
+        float mx = fmaxf(v0, v1);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+        const float m_new = fmaxf(m_old, mx);
+        const float base = (m_new == -INFINITY) ? 0.f : m_new;
+        const float p0 = __expf(v0 - base), p1 = __expf(v1 - base);
+        float sum = p0 + p1;
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
+        sP[h * PS + part * 2] = (bf16)p0;
+        sP[h * PS + part * 2 + 1] = (bf16)p1;
+        __syncthreads();   // every thread has read sM[h] before it changes
+        if (part == 0) {
+          const float alpha = __expf(m_old - base);
+          sAlpha[h] = alpha;
+          sL[h] = sL[h] * alpha + sum;
+          sM[h] = m_new;
+        }
+      }
+      __syncthreads();
+
+      {
+        const bf16* vt = SHARED ? sK : sV;
+        constexpr int VT = SHARED ? QS : VS;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sP[l16 * PS + lq * 8]);
+        f32x4 al;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) al[r] = sAlpha[lq * 4 + r];
+#pragma unroll
+        for (int i = 0; i < NVB_W; ++i) {
+          const int cb = wv + 4 * i;
+          if (cb < NVB) {
+            bf16x8 b;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) b[jj] = vt[(lq * 8 + jj) * VT + cb * 16 + l16];
+            accO[i] = mfma16x16x32(a, b, accO[i] * al);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < NVB_W; ++i) {
+    const int cb = wv + 4 * i;
+    if (cb < NVB) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = lq * 4 + r;
+        if (h < Gc) {
+          const float l = sL[h];
+          const float o = l > 0.f ? accO[i][r] / l : 0.f;
+          out_o[((size_t)t * p.Hq + h0 + h) * DV + cb * 16 + l16] = (bf16)o;
+        }
+      }
+    }
+  }
+  if (tid < Gc) {
+    const float l = sL[tid];
+    out_lse[(size_t)t * p.Hq + h0 + tid] = l > 0.f ? sM[tid] + __logf(l) : -INFINITY;
+  }
+}
+
+template <int DQK, int DV, bool SHARED>
+hipError_t launch_t(const Params& p, bf16* o, float* lse, hipStream_t s) {
+  dim3 grid((unsigned)(p.T * p.Hkv), (unsigned)((p.G + kHC - 1) / kHC));
+  hipLaunchKernelGGL((fwd_rows_kernel<DQK, DV, SHARED>), grid, dim3(kThreads), 0, s, p, o, lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fwd_rows_supported(int dqk, int dv, int shared) {
+  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 576 && dv == 512);
+}
+
+hipError_t launch_fwd_rows(const Params& p, bf16* o, float* lse, hipStream_t s) {
+  if (p.dqk == 64 && p.dv == 64) return p.shared ? launch_t<64, 64, true>(p, o, lse, s) : launch_t<64, 64, false>(p, o, lse, s);
+  if (p.dqk == 128 && p.dv == 128) return p.shared ? launch_t<128, 128, true>(p, o, lse, s) : launch_t<128, 128, false>(p, o, lse, s);
+  if (p.dqk == 576 && p.dv == 512) return p.shared ? launch_t<576, 512, true>(p, o, lse, s) : launch_t<576, 512, false>(p, o, lse, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa
