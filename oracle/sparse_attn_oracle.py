@@ -92,14 +92,14 @@ class Problem:
         self.win_left, self.win_right = wl.win_left, wl.win_right
         self.cmp_ratio = wl.cmp_ratio
         self.causal = True
-        self.q = inputs["q"]
-        self.d_o = inputs["d_o"]
+        self.q = inputs.get("q")
+        self.d_o = inputs.get("d_o")
         if wl.kv_shared:
-            self.k = inputs["kv"]
+            self.k = inputs.get("kv")
             self.v = None
         else:
-            self.k = inputs["k"]
-            self.v = inputs["v"]
+            self.k = inputs.get("k")
+            self.v = inputs.get("v")
         self.cmp_kv = inputs.get("cmp_kv")
         self.sinks = inputs.get("sinks")
         self.idx = inputs["idx"].numpy()
@@ -326,10 +326,10 @@ def entry_keys(pb: Problem) -> np.ndarray:
 
 def n_keys(pb: Problem) -> int:
     if pb.select == SEL_TOKEN:
-        return pb.k.shape[0] * pb.Hkv
+        return int(pb.cu[-1]) * pb.Hkv
     if pb.select == SEL_BLOCK:
         return int(_block_base(pb)[-1]) * pb.Hkv
-    return pb.cmp_kv.shape[0] * pb.Hkv
+    return int(pb.cu_cmp[-1]) * pb.Hkv
 
 
 def csr_transpose(pb: Problem) -> Tuple[np.ndarray, np.ndarray]:

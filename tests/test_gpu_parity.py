@@ -48,12 +48,29 @@ SMALL = {
 }
 
 
+MODES = {"atomic": B.DKV_ATOMIC, "det": B.DKV_DETERMINISTIC}
+
+
+@pytest.mark.parametrize("mode", list(MODES))
 @pytest.mark.parametrize("name", list(SMALL))
-def test_bwd_parity_small(name):
-    U.run_full_case(SMALL[name])
+def test_bwd_parity_small(name, mode):
+    U.run_full_case(SMALL[name], dkv_mode=MODES[mode])
 
 
-def test_bwd_edge_shuffled_padding_duplicates_empty_rows():
+@pytest.mark.parametrize("name", ["token_gqa_d128_g20", "block_gqa_d128", "mla_wcmp_sinks_varlen"])
+def test_bwd_deterministic_mode_is_bitwise_repeatable(name):
+    wl = SMALL[name]
+    inp = W.make_inputs(wl)
+    pb, Ob, Lb = U.oracle_fwd_rounded(inp)
+    U.say(f"[det] {name}")
+    runs = [U.gpu_bwd(wl, inp, Ob, Lb, B.DKV_DETERMINISTIC) for _ in range(3)]
+    for k in runs[0]:
+        for r in runs[1:]:
+            assert np.array_equal(runs[0][k].view(np.uint32), r[k].view(np.uint32)), k
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_edge_shuffled_padding_duplicates_empty_rows(mode):
     """-1 in any slot, a duplicated index, an out-of-range index, and rows
     with no valid key (lse = -inf): finite outputs equal to the oracle."""
     wl = _wl(name="edge_token", seqlens=(96,), n_q_heads=4, n_kv_heads=1, topk=24)
@@ -67,7 +84,7 @@ def test_bwd_edge_shuffled_padding_duplicates_empty_rows():
     idx[40] = -1                                  # no valid key
     idx[41, 0, :] = -1
     inp["idx"] = torch.from_numpy(idx)
-    res, got, ref = U.run_full_case(wl, inputs=inp)
+    res, got, ref = U.run_full_case(wl, inputs=inp, dkv_mode=MODES[mode])
     assert np.all(got["dq"].reshape(ref["dq"].shape)[40] == 0)
 
 
@@ -116,10 +133,11 @@ def test_fwd_parity_small(name):
     np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
 
 
-def test_bwd_parity_nsa_block_full_size():
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_parity_nsa_block_full_size(mode):
     """The NSA-style block-sparse GQA workload at its full size (B=2,
     S=4096, 16:1 heads, d=128, 16 blocks of 64): every output element."""
-    U.run_full_case(W.WORKLOADS["nsa_block_gqa"])
+    U.run_full_case(W.WORKLOADS["nsa_block_gqa"], dkv_mode=MODES[mode])
 
 
 def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0):

@@ -244,7 +244,7 @@ def device_tensors(inputs: Dict[str, object], device="cuda") -> Dict[str, torch.
     """Move a generator dict to the device under the C ABI's argument names."""
     wl = inputs["workload"]
     out = {}
-    for k in ("q", "k", "v", "kv", "cmp_kv", "d_o", "sinks"):
+    for k in ("q", "k", "v", "kv", "cmp_kv", "d_o", "sinks", "o", "lse"):
         if k in inputs:
             out[k] = inputs[k].to(device).contiguous()
     out["topk_indices"] = inputs["idx"].to(device).contiguous()
@@ -254,3 +254,34 @@ def device_tensors(inputs: Dict[str, object], device="cuda") -> Dict[str, torch.
     if wl.select == W.SEL_WINDOW_CMP:
         out["cu_seqlens_cmp"] = inputs["cu_seqlens_cmp"].to(device)
     return out
+
+
+def sparse_attn_csr_size(desc: SaDesc, host_cu_seqlens_kv=None):
+    """(n_keys, workspace bytes) of the CSR transpose."""
+    nk = ctypes.c_int64(0)
+    nb = ctypes.c_size_t(0)
+    cu = None
+    if host_cu_seqlens_kv is not None:
+        arr = (ctypes.c_int32 * len(host_cu_seqlens_kv))(*[int(x) for x in host_cu_seqlens_kv])
+        cu = ctypes.cast(arr, _P)
+    _check("sparse_attn_csr_size", load().sparse_attn_csr_size(ctypes.byref(desc), cu, ctypes.byref(nk),
+                                                               ctypes.byref(nb)))
+    return nk.value, nb.value
+
+
+def sparse_attn_csr_transpose(desc: SaDesc, topk_indices: torch.Tensor, cu_seqlens_q=None, cu_seqlens_kv=None,
+                              host_cu_seqlens_kv=None, stream=None):
+    """CSR transpose of the index lists on the GPU: (row_ptr [n_keys+1],
+    entries [n_valid]) as int32 device tensors."""
+    lib = load()
+    n_keys, nbytes = sparse_attn_csr_size(desc, host_cu_seqlens_kv)
+    dev = topk_indices.device
+    row_ptr = torch.empty(n_keys + 1, dtype=torch.int32, device=dev)
+    entries = torch.empty(max(1, topk_indices.numel()), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _check("sparse_attn_csr_transpose",
+           lib.sparse_attn_csr_transpose(ctypes.byref(desc), _ptr(topk_indices), _ptr(cu_seqlens_q),
+                                         _ptr(cu_seqlens_kv), _ptr(row_ptr), _ptr(entries), _ptr(ws), ws.numel(),
+                                         _stream(stream)))
+    n_valid = int(row_ptr[-1].item())
+    return row_ptr, entries[:n_valid]

@@ -70,24 +70,75 @@ sa_status_t validate(const sa_desc_t* d) {
   return SA_OK;
 }
 
+// Partial-row buffer cap of the deterministic path; larger problems are
+// processed in token chunks whose partials fit under it.
+constexpr size_t kPartialCap = size_t(8) << 30;
+
+long long n_positions_host(const sa_desc_t* d) {
+  if (d->select == SA_SEL_TOKEN) return d->topk;
+  if (d->select == SA_SEL_BLOCK) return (long long)d->topk * d->block_size;
+  return (long long)d->win_left + 1 + d->win_right + d->topk;
+}
+
+// Keys of the internal CSR (an upper bound of the block count for TND).
+long long csr_keys_bound(const sa_desc_t* d) {
+  if (d->select == SA_SEL_TOKEN) return rows_kv(d) * d->n_kv_heads;
+  if (d->select == SA_SEL_BLOCK) {
+    if (d->layout == SA_LAYOUT_BSND)
+      return (long long)d->batch * ((d->seqlen_kv + d->block_size - 1) / d->block_size) * d->n_kv_heads;
+    return (rows_kv(d) / d->block_size + d->batch) * d->n_kv_heads;
+  }
+  return rows_cmp(d) * d->n_kv_heads;
+}
+
+Params make_params(const sa_desc_t* d);
+
 struct BwdLayout {
-  size_t D, sink_term, acc_k, acc_v, acc_cmp, total;
+  size_t D, sink_term, acc_k, acc_v, acc_cmp;                   // atomic mode
+  size_t blk_base, row_ptr, entries, csr_ws, partial, acc;      // deterministic mode
+  int Tc, n_hc, RW;
+  size_t total;
 };
 
-BwdLayout bwd_layout(const sa_desc_t* d) {
+BwdLayout bwd_layout(const sa_desc_t* d, const Params& p) {
   const size_t T = (size_t)total_q(d), Hq = (size_t)d->n_q_heads, Hkv = (size_t)d->n_kv_heads;
   BwdLayout L;
+  std::memset(&L, 0, sizeof(L));
   size_t off = 0;
   L.D = off;
   off += align_up(T * Hq * sizeof(float));
   L.sink_term = off;
   if (d->has_sinks) off += align_up(T * Hq * sizeof(float));
-  L.acc_k = off;
-  off += align_up((size_t)rows_kv(d) * Hkv * d->d_qk * sizeof(float));
-  L.acc_v = off;
-  if (!d->kv_shared) off += align_up((size_t)rows_kv(d) * Hkv * d->d_v * sizeof(float));
-  L.acc_cmp = off;
-  if (d->select == SA_SEL_WINDOW_CMP) off += align_up((size_t)rows_cmp(d) * Hkv * d->d_qk * sizeof(float));
+  if (d->dkv_mode == SA_DKV_ATOMIC) {
+    L.acc_k = off;
+    off += align_up((size_t)rows_kv(d) * Hkv * d->d_qk * sizeof(float));
+    L.acc_v = off;
+    if (!d->kv_shared) off += align_up((size_t)rows_kv(d) * Hkv * d->d_v * sizeof(float));
+    L.acc_cmp = off;
+    if (d->select == SA_SEL_WINDOW_CMP) off += align_up((size_t)rows_cmp(d) * Hkv * d->d_qk * sizeof(float));
+    L.Tc = (int)T;
+    L.total = off;
+    return L;
+  }
+  L.RW = d->kv_shared ? d->d_qk : d->d_qk + d->d_v;
+  L.n_hc = sa::bwd_rows_head_chunks(p);
+  const size_t npos = (size_t)n_positions_host(d);
+  const size_t per_token = (size_t)L.n_hc * Hkv * npos * L.RW * sizeof(float);
+  size_t Tc = per_token ? std::max<size_t>(1, kPartialCap / per_token) : T;
+  L.Tc = (int)std::min<size_t>(std::max<size_t>(T, 1), Tc);
+  const long long nk = csr_keys_bound(d);
+  L.blk_base = off;
+  off += align_up((size_t)(d->batch + 1) * 4);
+  L.row_ptr = off;
+  off += align_up((size_t)(nk + 1) * 4);
+  L.entries = off;
+  off += align_up((size_t)L.Tc * Hkv * d->topk * 4);
+  L.csr_ws = off;
+  off += align_up(sa::csr_workspace_bytes((long long)L.Tc * Hkv * d->topk, nk, d->batch));
+  L.partial = off;
+  off += align_up((size_t)L.Tc * per_token);
+  L.acc = off;
+  off += align_up((size_t)(rows_kv(d) + rows_cmp(d)) * Hkv * L.RW * sizeof(float));
   L.total = off;
   return L;
 }
@@ -149,9 +200,8 @@ sa_status_t sparse_attn_bwd_workspace_size(const sa_desc_t* desc, size_t* bytes)
   if (!bytes) return SA_ERR_NULL_PTR;
   sa_status_t st = validate(desc);
   if (st != SA_OK) return st;
-  if (desc->dkv_mode == SA_DKV_DETERMINISTIC) return SA_ERR_UNSUPPORTED;
   if (!sa::bwd_rows_supported(desc->d_qk, desc->d_v, desc->kv_shared)) return SA_ERR_UNSUPPORTED;
-  *bytes = bwd_layout(desc).total;
+  *bytes = bwd_layout(desc, make_params(desc)).total;
   return SA_OK;
 }
 
@@ -176,9 +226,9 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   if (!aligned16(a->o) || !aligned16(a->d_o)) return SA_ERR_MISALIGNED;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const BwdLayout L = bwd_layout(desc);
   char* ws = static_cast<char*>(workspace);
   Params p = make_params(desc);
+  const BwdLayout L = bwd_layout(desc, p);
   p.q = static_cast<const bf16*>(a->q);
   p.k = static_cast<const bf16*>(desc->kv_shared ? a->kv : a->k);
   p.v = desc->kv_shared ? nullptr : static_cast<const bf16*>(a->v);
@@ -193,30 +243,85 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   p.cu_cmp = a->cu_seqlens_cmp;
 
   BwdBuffers w;
+  std::memset(&w, 0, sizeof(w));
   w.D = reinterpret_cast<float*>(ws + L.D);
   w.sink_term = desc->has_sinks ? reinterpret_cast<float*>(ws + L.sink_term) : nullptr;
-  w.acc_k = reinterpret_cast<float*>(ws + L.acc_k);
-  w.acc_v = desc->kv_shared ? nullptr : reinterpret_cast<float*>(ws + L.acc_v);
-  w.acc_cmp = desc->select == SA_SEL_WINDOW_CMP ? reinterpret_cast<float*>(ws + L.acc_cmp) : nullptr;
   w.dq = static_cast<bf16*>(a->dq);
   w.dsinks = a->dsinks;
+  w.t0 = 0;
+  w.Tc = p.T;
 
   const size_t Hkv = (size_t)desc->n_kv_heads;
-  const size_t nk = (size_t)rows_kv(desc) * Hkv * desc->d_qk;
-  const size_t nv = desc->kv_shared ? 0 : (size_t)rows_kv(desc) * Hkv * desc->d_v;
-  const size_t nc = (size_t)rows_cmp(desc) * Hkv * desc->d_qk;
-
-  SA_TRY_HIP(sa::launch_fill_zero(w.acc_k, nk, s));
-  if (nv) SA_TRY_HIP(sa::launch_fill_zero(w.acc_v, nv, s));
-  if (nc) SA_TRY_HIP(sa::launch_fill_zero(w.acc_cmp, nc, s));
   SA_TRY_HIP(sa::launch_preprocess(p, w, s));
-  if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
-  SA_TRY_HIP(sa::launch_bwd_rows(p, w, s));
-  if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
   if (desc->has_sinks) SA_TRY_HIP(sa::launch_dsinks(p, w, s));
-  SA_TRY_HIP(sa::launch_cast_bf16(w.acc_k, static_cast<bf16*>(desc->kv_shared ? a->dkv : a->dk), nk, s));
-  if (nv) SA_TRY_HIP(sa::launch_cast_bf16(w.acc_v, static_cast<bf16*>(a->dv), nv, s));
-  if (nc) SA_TRY_HIP(sa::launch_cast_bf16(w.acc_cmp, static_cast<bf16*>(a->d_cmp_kv), nc, s));
+
+  if (desc->dkv_mode == SA_DKV_ATOMIC) {
+    w.acc_k = reinterpret_cast<float*>(ws + L.acc_k);
+    w.acc_v = desc->kv_shared ? nullptr : reinterpret_cast<float*>(ws + L.acc_v);
+    w.acc_cmp = desc->select == SA_SEL_WINDOW_CMP ? reinterpret_cast<float*>(ws + L.acc_cmp) : nullptr;
+    const size_t nk = (size_t)rows_kv(desc) * Hkv * desc->d_qk;
+    const size_t nv = desc->kv_shared ? 0 : (size_t)rows_kv(desc) * Hkv * desc->d_v;
+    const size_t nc = (size_t)rows_cmp(desc) * Hkv * desc->d_qk;
+    SA_TRY_HIP(sa::launch_fill_zero(w.acc_k, nk, s));
+    if (nv) SA_TRY_HIP(sa::launch_fill_zero(w.acc_v, nv, s));
+    if (nc) SA_TRY_HIP(sa::launch_fill_zero(w.acc_cmp, nc, s));
+    if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
+    SA_TRY_HIP(sa::launch_bwd_rows(p, w, s));
+    if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
+    SA_TRY_HIP(sa::launch_cast_bf16(w.acc_k, static_cast<bf16*>(desc->kv_shared ? a->dkv : a->dk), nk, s));
+    if (nv) SA_TRY_HIP(sa::launch_cast_bf16(w.acc_v, static_cast<bf16*>(a->dv), nv, s));
+    if (nc) SA_TRY_HIP(sa::launch_cast_bf16(w.acc_cmp, static_cast<bf16*>(a->d_cmp_kv), nc, s));
+    return SA_OK;
+  }
+
+  // deterministic: per token chunk, CSR of the chunk's slots, partial rows,
+  // key-major reduce into the fp32 accumulator; then one cast
+  int* blk_base = reinterpret_cast<int*>(ws + L.blk_base);
+  int* row_ptr = reinterpret_cast<int*>(ws + L.row_ptr);
+  int* entries = reinterpret_cast<int*>(ws + L.entries);
+  float* acc = reinterpret_cast<float*>(ws + L.acc);
+  const long long nk = csr_keys_bound(desc);
+  const bool has_slots = desc->topk > 0;
+  if (desc->select == SA_SEL_BLOCK) SA_TRY_HIP(sa::launch_block_base(p, blk_base, s));
+  w.det = 1;
+  w.partial = ws + L.partial;
+  w.npos = (int)n_positions_host(desc);
+  w.RW = L.RW;
+  sa::ReduceArgs r;
+  std::memset(&r, 0, sizeof(r));
+  r.partial = w.partial;
+  r.partial_bf16 = 0;
+  r.RW = L.RW;
+  r.npos = w.npos;
+  r.n_hc = L.n_hc;
+  r.row_ptr = row_ptr;
+  r.entries = entries;
+  r.blk_base = blk_base;
+  r.n_kv_out = rows_kv(desc) * (long long)Hkv;
+  r.n_out_rows = r.n_kv_out + rows_cmp(desc) * (long long)Hkv;
+  r.acc = acc;
+  bool first = true;
+  for (int t0 = 0; t0 < p.T; t0 += L.Tc) {
+    const int t1 = std::min(p.T, t0 + L.Tc);
+    w.t0 = t0;
+    w.Tc = t1 - t0;
+    if (has_slots)
+      SA_TRY_HIP(sa::launch_csr_transpose(p, t0, t1, nk, blk_base, row_ptr, entries, ws + L.csr_ws, s));
+    if (ev_main_start && first) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
+    SA_TRY_HIP(sa::launch_bwd_rows(p, w, s));
+    if (ev_main_stop && t1 == p.T) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
+    r.t0 = t0;
+    r.Tc = t1 - t0;
+    r.accumulate = first ? 0 : 1;
+    SA_TRY_HIP(sa::launch_reduce(p, r, s));
+    first = false;
+  }
+  bf16* out_a = static_cast<bf16*>(desc->kv_shared ? a->dkv : a->dk);
+  bf16* out_b = desc->kv_shared ? nullptr : static_cast<bf16*>(a->dv);
+  SA_TRY_HIP(sa::launch_split_cast(acc, r.n_kv_out, L.RW, desc->d_qk, out_a, out_b, s));
+  if (desc->select == SA_SEL_WINDOW_CMP)
+    SA_TRY_HIP(sa::launch_cast_bf16(acc + r.n_kv_out * L.RW, static_cast<bf16*>(a->d_cmp_kv),
+                                    (size_t)(r.n_out_rows - r.n_kv_out) * L.RW, s));
   return SA_OK;
 }
 
@@ -251,27 +356,58 @@ sa_status_t sparse_attn_fwd(const sa_desc_t* desc, const sa_fwd_args_t* a, void*
 
 sa_status_t sparse_attn_csr_size(const sa_desc_t* desc, const int32_t* host_cu_seqlens_kv, int64_t* n_keys,
                                  size_t* workspace_bytes) {
-  (void)desc;
-  (void)host_cu_seqlens_kv;
-  (void)n_keys;
-  (void)workspace_bytes;
-  return SA_ERR_UNSUPPORTED;
+  if (!n_keys || !workspace_bytes) return SA_ERR_NULL_PTR;
+  sa_status_t st = validate(desc);
+  if (st != SA_OK) return st;
+  long long nk;
+  if (desc->select == SA_SEL_BLOCK && desc->layout == SA_LAYOUT_TND) {
+    if (!host_cu_seqlens_kv) return SA_ERR_NULL_PTR;
+    long long blocks = 0;
+    for (int b = 0; b < desc->batch; ++b) {
+      const int len = host_cu_seqlens_kv[b + 1] - host_cu_seqlens_kv[b];
+      if (len < 0) return SA_ERR_BAD_SHAPE;
+      blocks += (len + desc->block_size - 1) / desc->block_size;
+    }
+    nk = blocks * desc->n_kv_heads;
+  } else {
+    nk = csr_keys_bound(desc);
+  }
+  if (nk >= (1LL << 31) - 1) return SA_ERR_BAD_SHAPE;
+  *n_keys = nk;
+  const long long n_slots = total_q(desc) * desc->n_kv_heads * desc->topk;
+  *workspace_bytes = align_up((size_t)(desc->batch + 1) * 4) + sa::csr_workspace_bytes(n_slots, nk, desc->batch);
+  return SA_OK;
 }
 
 sa_status_t sparse_attn_csr_transpose(const sa_desc_t* desc, const int32_t* topk_indices,
                                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
                                       int32_t* row_ptr, int32_t* entries, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  (void)desc;
-  (void)topk_indices;
-  (void)cu_seqlens_q;
-  (void)cu_seqlens_kv;
-  (void)row_ptr;
-  (void)entries;
-  (void)workspace;
-  (void)workspace_bytes;
-  (void)stream;
-  return SA_ERR_UNSUPPORTED;
+  sa_status_t st = validate(desc);
+  if (st != SA_OK) return st;
+  if (desc->topk < 1) return SA_ERR_BAD_SHAPE;
+  if (!topk_indices || !row_ptr || !entries || !workspace) return SA_ERR_NULL_PTR;
+  if (desc->layout == SA_LAYOUT_TND && (!cu_seqlens_q || !cu_seqlens_kv)) return SA_ERR_NULL_PTR;
+  if (desc->select == SA_SEL_WINDOW_CMP && !cu_seqlens_kv) return SA_ERR_NULL_PTR;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return SA_ERR_MISALIGNED;
+  // exact key count (BSND or TND token/window) comes from the descriptor;
+  // TND block mode uses the bound, whose extra keys stay empty
+  const long long nk = csr_keys_bound(desc);
+  const long long n_slots = total_q(desc) * desc->n_kv_heads * desc->topk;
+  const size_t need = align_up((size_t)(desc->batch + 1) * 4) + sa::csr_workspace_bytes(n_slots, nk, desc->batch);
+  if (workspace_bytes < need) return SA_ERR_WORKSPACE_TOO_SMALL;
+  if (total_q(desc) == 0) return SA_OK;
+  Params p = make_params(desc);
+  p.idx = topk_indices;
+  p.cu_q = cu_seqlens_q;
+  p.cu_kv = cu_seqlens_kv;
+  p.cu_cmp = cu_seqlens_kv;   // window+cmp: the key table is cmp_kv
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int* blk_base = static_cast<int*>(workspace);
+  void* ws = static_cast<char*>(workspace) + align_up((size_t)(desc->batch + 1) * 4);
+  if (desc->select == SA_SEL_BLOCK) SA_TRY_HIP(sa::launch_block_base(p, blk_base, s));
+  SA_TRY_HIP(sa::launch_csr_transpose(p, 0, p.T, nk, blk_base, row_ptr, entries, ws, s));
+  return SA_OK;
 }
 
 const char* sparse_attn_status_string(sa_status_t status) {

@@ -115,12 +115,13 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
   __shared__ __attribute__((aligned(16))) bf16 sPt[kNT * TS];
   __shared__ __attribute__((aligned(16))) bf16 sdSt[kNT * TS];
   __shared__ int sRows[kMaxPos];
+  __shared__ int sVpos[kMaxPos];
   __shared__ float sL[kHC], sD[kHC];
   __shared__ int sWave[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int row = blockIdx.x;                 // (token, kv head)
+  const int row = w.t0 * p.Hkv + blockIdx.x;  // (token, kv head)
   const int t = row / p.Hkv, g = row - t * p.Hkv;
   const int h0 = g * p.G + blockIdx.y * kHC;  // first query head of the chunk
   const int Gc = min(kHC, p.G - blockIdx.y * kHC);
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
   const int npos = n_positions(p);
   for (int pos0 = 0; pos0 < npos; pos0 += kMaxPos) {
     __syncthreads();
-    const int cnt = compact_positions(p, s, irow, pos0, min(kMaxPos, npos - pos0), sRows, sWave);
+    const int cnt = compact_positions(p, s, irow, pos0, min(kMaxPos, npos - pos0), sRows, sWave, sVpos);
     for (int k0 = 0; k0 < cnt; k0 += kNT) {
       // ---- gather the tile's K (and V) rows into LDS -----------------------
       for (int c = tid; c < kNT * (DQK / 8); c += kThreads) {
@@ -267,6 +268,18 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
             for (int jj = 0; jj < 4; ++jj) b[jj] = bf16_bits(sdO[(lq * 4 + jj) * VS + cb * 16 + l16]);
             acc = mfma16x16x16(a, b, acc);
           }
+          if (w.det) {
+            // one partial row per (head chunk, token row, position)
+            float* part = static_cast<float*>(w.partial) +
+                          (((size_t)blockIdx.y * w.Tc * p.Hkv + blockIdx.x) * w.npos) * w.RW +
+                          (is_v ? DQK : 0) + cb * 16 + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = kb * 16 + lq * 4 + i;
+              if (k0 + r < cnt) part[(size_t)sVpos[k0 + r] * w.RW] = acc[i];
+            }
+            continue;
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = kb * 16 + lq * 4 + i;
@@ -305,12 +318,14 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
 
 template <int DQK, int DV, bool SHARED>
 hipError_t launch_rows_t(const Params& p, const BwdBuffers& w, hipStream_t s) {
-  dim3 grid((unsigned)(p.T * p.Hkv), (unsigned)((p.G + kHC - 1) / kHC));
+  dim3 grid((unsigned)(w.Tc * p.Hkv), (unsigned)((p.G + kHC - 1) / kHC));
   hipLaunchKernelGGL((bwd_rows_kernel<DQK, DV, SHARED>), grid, dim3(kThreads), 0, s, p, w);
   return hipGetLastError();
 }
 
 }  // namespace
+
+int bwd_rows_head_chunks(const Params& p) { return (p.G + kHC - 1) / kHC; }
 
 bool bwd_rows_supported(int dqk, int dv, int shared) {
   return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 576 && dv == 512);

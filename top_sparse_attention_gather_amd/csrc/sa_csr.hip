@@ -1,0 +1,294 @@
+// CSR transpose of the top-k index lists on the GPU: for every key, the
+// flat slot ids p = (t * Hkv + g) * K + slot that name it, ascending.
+//
+// A slot's key follows the selection rules of the backward (token: the kv
+// row; block: the sequence's block; window+cmp: the cmp row) and unused or
+// fully masked slots get a sentinel key that sorts last.  The order is
+// produced by a stable LSD radix sort (8-bit digits) of (key, p) pairs in
+// p order: per pass a digit histogram per 4096-element tile, one
+// exclusive scan over the digit-major table, and a stable scatter that
+// ranks equal digits inside a tile with wave ballots.  Per-key counts come
+// from an integer histogram and the same scan, giving row_ptr.  Everything
+// is integer work, so the result is bit-exact and run-to-run identical.
+#include "sa_launch.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kItems = 16;
+constexpr int kTile = kThreads * kItems;   // elements per radix tile
+constexpr int kScanChunk = 1024;           // elements per scan block (4 per thread)
+
+// ---------------------------------------------------------------------------
+// Device-wide exclusive scan of int32 (values and totals must fit int32).
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+// Block-wide exclusive scan of one value per thread; returns the block total.
+__device__ int block_excl_scan(int v, int* excl, int* sWave) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) sWave[w] = inc;
+  __syncthreads();
+  int off = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    if (i < w) off += sWave[i];
+    total += sWave[i];
+  }
+  *excl = off + inc - v;
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kThreads) void scan_sums_kernel(const int* __restrict__ in, long long n,
+                                                             int* __restrict__ bsum) {
+  __shared__ int sWave[4];
+  const long long base = (long long)blockIdx.x * kScanChunk + threadIdx.x * 4;
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (base + i < n) s += in[base + i];
+  int excl;
+  const int total = block_excl_scan(s, &excl, sWave);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+// Single workgroup: exclusive scan of the block sums in place.
+__global__ __launch_bounds__(kThreads) void scan_bsums_kernel(int* __restrict__ bsum, int nb) {
+  __shared__ int sWave[4];
+  int carry = 0;
+  for (int base = 0; base < nb; base += kThreads) {
+    const int i = base + threadIdx.x;
+    const int v = i < nb ? bsum[i] : 0;
+    int excl;
+    const int total = block_excl_scan(v, &excl, sWave);
+    if (i < nb) bsum[i] = carry + excl;
+    carry += total;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void scan_apply_kernel(const int* __restrict__ in, long long n,
+                                                              const int* __restrict__ bsum,
+                                                              int* __restrict__ out, long long n_out) {
+  __shared__ int sWave[4];
+  const long long base = (long long)blockIdx.x * kScanChunk + threadIdx.x * 4;
+  int v[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = base + i < n ? in[base + i] : 0;
+    s += v[i];
+  }
+  int excl;
+  block_excl_scan(s, &excl, sWave);
+  int run = bsum[blockIdx.x] + excl;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (base + i < n_out) out[base + i] = run;
+    run += v[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Slot keys and per-key counts.
+
+__device__ __forceinline__ int slot_key(const Params& p, const SeqPos& s, int g, int j,
+                                        const int* __restrict__ blk_base, int sentinel) {
+  if (p.select == kSelToken) {
+    if (j < 0 || j >= s.kv_len || (p.causal && j > s.tl)) return sentinel;
+    return (s.kv_base + j) * p.Hkv + g;
+  }
+  if (p.select == kSelBlock) {
+    if (j < 0 || (long long)j * p.bs >= s.kv_len || (p.causal && (long long)j * p.bs > s.tl)) return sentinel;
+    return (blk_base[s.b] + j) * p.Hkv + g;
+  }
+  if (j < 0 || j >= s.cmp_len || (p.causal && (long long)p.cmp_ratio * j + p.cmp_ratio - 1 > s.tl))
+    return sentinel;
+  return (s.cmp_base + j) * p.Hkv + g;
+}
+
+// First block id of every sequence (block mode): blk_base[b] = sum over
+// c < b of ceil(len_kv(c) / bs); one thread, B is small.
+__global__ void block_base_kernel(Params p, int* __restrict__ blk_base) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int acc = 0;
+  for (int b = 0; b < p.B; ++b) {
+    blk_base[b] = acc;
+    const int len = p.layout == kLayoutBSND ? p.Skv : p.cu_kv[b + 1] - p.cu_kv[b];
+    acc += (len + p.bs - 1) / p.bs;
+  }
+  blk_base[p.B] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void slot_keys_kernel(Params p, long long slot0, long long n,
+                                                             const int* __restrict__ blk_base, int sentinel,
+                                                             int* __restrict__ keys, int* __restrict__ counts) {
+  const long long i = blockIdx.x * (long long)kThreads + threadIdx.x;
+  if (i >= n) return;
+  const long long slot = slot0 + i;
+  const int row = (int)(slot / p.topk);
+  const int t = row / p.Hkv, g = row - t * p.Hkv;
+  const SeqPos s = seq_pos(p, t);
+  const int key = slot_key(p, s, g, p.idx[slot], blk_base, sentinel);
+  keys[i] = key;
+  if (key != sentinel) atomicAdd(&counts[key], 1);
+}
+
+// ---------------------------------------------------------------------------
+// LSD radix sort passes.
+
+__global__ __launch_bounds__(kThreads) void radix_hist_kernel(const int* __restrict__ keys, long long n, int shift,
+                                                              int nb, int* __restrict__ hist) {
+  __shared__ int h[256];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  const long long base = (long long)blockIdx.x * kTile;
+  for (int r = 0; r < kItems; ++r) {
+    const long long i = base + r * kThreads + threadIdx.x;
+    if (i < n) atomicAdd(&h[(keys[i] >> shift) & 255], 1);
+  }
+  __syncthreads();
+  hist[(long long)threadIdx.x * nb + blockIdx.x] = h[threadIdx.x];
+}
+
+// Stable scatter: element e = base + r * 256 + tid is ranked after every
+// element of an earlier round or a lower thread with the same digit.
+__global__ __launch_bounds__(kThreads) void radix_scatter_kernel(const int* __restrict__ keys_in,
+                                                                 const int* __restrict__ vals_in,
+                                                                 long long val0, long long n, int shift, int nb,
+                                                                 const int* __restrict__ offs,
+                                                                 int* __restrict__ keys_out,
+                                                                 int* __restrict__ vals_out) {
+  __shared__ int cnt[256];
+  __shared__ int wcnt[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  cnt[tid] = offs[(long long)tid * nb + blockIdx.x];
+  for (int i = 0; i < 4; ++i) wcnt[i][tid] = 0;
+  __syncthreads();
+  const long long base = (long long)blockIdx.x * kTile;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int r = 0; r < kItems; ++r) {
+    const long long i = base + r * kThreads + tid;
+    const bool ok = i < n;
+    const int key = ok ? keys_in[i] : 0;
+    const int val = ok ? (vals_in ? vals_in[i] : (int)(val0 + i)) : 0;
+    const int d = (key >> shift) & 255;
+    // lanes of this wave holding the same digit
+    unsigned long long peers = __ballot(ok);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const unsigned long long m = __ballot((d >> b) & 1);
+      peers &= ((d >> b) & 1) ? m : ~m;
+    }
+    if (ok && (peers & lt) == 0) wcnt[w][d] = __popcll(peers);
+    __syncthreads();
+    if (ok) {
+      int rank = cnt[d] + __popcll(peers & lt);
+      for (int ww = 0; ww < w; ++ww) rank += wcnt[ww][d];
+      keys_out[rank] = key;
+      vals_out[rank] = val;
+    }
+    __syncthreads();
+    cnt[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+    wcnt[0][tid] = wcnt[1][tid] = wcnt[2][tid] = wcnt[3][tid] = 0;
+    __syncthreads();
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct CsrWs {
+  int *keys_a, *keys_b, *vals_a, *counts, *hist, *bsum;
+  long long nb_tiles, nb_scan;
+};
+
+CsrWs carve(void* ws, long long n, long long n_keys) {
+  CsrWs c;
+  char* p = static_cast<char*>(ws);
+  c.nb_tiles = (n + kTile - 1) / kTile;
+  const long long hist_n = 256 * c.nb_tiles;
+  const long long scan_n = std::max(hist_n, n_keys + 1);
+  c.nb_scan = (scan_n + kScanChunk - 1) / kScanChunk;
+  c.keys_a = reinterpret_cast<int*>(p); p += align256(n * 4);
+  c.keys_b = reinterpret_cast<int*>(p); p += align256(n * 4);
+  c.vals_a = reinterpret_cast<int*>(p); p += align256(n * 4);
+  c.counts = reinterpret_cast<int*>(p); p += align256((n_keys + 1) * 4);
+  c.hist = reinterpret_cast<int*>(p); p += align256(hist_n * 4);
+  c.bsum = reinterpret_cast<int*>(p); p += align256(c.nb_scan * 4);
+  return c;
+}
+
+hipError_t scan_excl(const int* in, long long n, int* out, long long n_out, int* bsum, hipStream_t s) {
+  const long long nb = (std::max(n, n_out) + kScanChunk - 1) / kScanChunk;
+  hipLaunchKernelGGL(scan_sums_kernel, dim3((unsigned)nb), dim3(kThreads), 0, s, in, n, bsum);
+  hipLaunchKernelGGL(scan_bsums_kernel, dim3(1), dim3(kThreads), 0, s, bsum, (int)nb);
+  hipLaunchKernelGGL(scan_apply_kernel, dim3((unsigned)nb), dim3(kThreads), 0, s, in, n, bsum, out, n_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t csr_workspace_bytes(long long n, long long n_keys, int batch) {
+  const long long nb_tiles = (n + kTile - 1) / kTile;
+  const long long hist_n = 256 * nb_tiles;
+  const long long scan_n = std::max(hist_n, n_keys + 1);
+  const long long nb_scan = (scan_n + kScanChunk - 1) / kScanChunk;
+  return align256(n * 4) * 3 + align256((n_keys + 1) * 4) + align256(hist_n * 4) + align256(nb_scan * 4) +
+         align256((size_t)(batch + 1) * 4);
+}
+
+hipError_t launch_block_base(const Params& p, int* blk_base, hipStream_t s) {
+  hipLaunchKernelGGL(block_base_kernel, dim3(1), dim3(64), 0, s, p, blk_base);
+  return hipGetLastError();
+}
+
+int csr_sentinel_bits(long long n_keys) {
+  int bits = 1;
+  while ((1LL << bits) <= n_keys) ++bits;
+  return bits;
+}
+
+hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_keys, const int* blk_base,
+                                int* row_ptr, int* entries, void* ws, hipStream_t s) {
+  const long long slot0 = (long long)t0 * p.Hkv * p.topk;
+  const long long n = (long long)(t1 - t0) * p.Hkv * p.topk;
+  CsrWs c = carve(ws, n, n_keys);
+  const int sentinel = (int)n_keys;
+  hipError_t e;
+  if ((e = launch_fill_zero(reinterpret_cast<float*>(c.counts), (size_t)(n_keys + 1), s)) != hipSuccess) return e;
+  if (n > 0) {
+    hipLaunchKernelGGL(slot_keys_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, p,
+                       slot0, n, blk_base, sentinel, c.keys_a, c.counts);
+  }
+  if ((e = scan_excl(c.counts, n_keys, row_ptr, n_keys + 1, c.bsum, s)) != hipSuccess) return e;
+  if (n == 0) return hipGetLastError();
+  const int bits = csr_sentinel_bits(n_keys);
+  const int passes = (bits + 7) / 8;
+  const int nb = (int)c.nb_tiles;
+  int* kin = c.keys_a;
+  int* kout = c.keys_b;
+  int* vin = nullptr;            // first pass: values are the slot ids
+  for (int pass = 0; pass < passes; ++pass) {
+    // value buffers alternate so that the last pass lands in `entries`
+    int* vout = ((passes - 1 - pass) % 2 == 0) ? entries : c.vals_a;
+    hipLaunchKernelGGL(radix_hist_kernel, dim3(nb), dim3(kThreads), 0, s, kin, n, pass * 8, nb, c.hist);
+    if ((e = scan_excl(c.hist, 256LL * nb, c.hist, 256LL * nb, c.bsum, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(radix_scatter_kernel, dim3(nb), dim3(kThreads), 0, s, kin, vin, slot0, n, pass * 8, nb,
+                       c.hist, kout, vout);
+    std::swap(kin, kout);
+    vin = vout;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

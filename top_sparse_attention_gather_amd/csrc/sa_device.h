@@ -118,10 +118,11 @@ __device__ __forceinline__ int decode_position(const Params& p, const SeqPos& s,
 
 // Compact positions [pos0, pos0 + n) of a row into sRows, keeping position
 // order; returns the number of used positions (the same in every thread).
-// Block of 256 threads (4 waves); sWave holds 4 ints.  Ends with a barrier.
+// Block of 256 threads (4 waves); sWave holds 4 ints.  With sVpos, also
+// stores each used position's index.  Ends with a barrier.
 __device__ __forceinline__ int compact_positions(const Params& p, const SeqPos& s,
                                                  const int* __restrict__ irow, int pos0, int n,
-                                                 int* sRows, int* sWave) {
+                                                 int* sRows, int* sWave, int* sVpos = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int total = 0;
   for (int base = 0; base < n; base += 256) {
@@ -134,7 +135,10 @@ __device__ __forceinline__ int compact_positions(const Params& p, const SeqPos& 
     __syncthreads();
     int off = total;
     for (int i = 0; i < w; ++i) off += sWave[i];
-    if (code >= 0) sRows[off + before] = code;
+    if (code >= 0) {
+      sRows[off + before] = code;
+      if (sVpos) sVpos[off + before] = pos0 + pos;
+    }
     total += sWave[0] + sWave[1] + sWave[2] + sWave[3];
     __syncthreads();
   }

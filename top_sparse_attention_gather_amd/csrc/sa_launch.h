@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "sa_device.h"
 
 namespace sa {
@@ -14,11 +16,31 @@ namespace sa {
 struct BwdBuffers {
   float* D;          // [T][Hq] softmax-grad term
   float* sink_term;  // [T][Hq] per-row dSinks terms (sinks only)
-  float* acc_k;      // fp32 dK (or shared dKV) accumulator, rows x Hkv x dqk
-  float* acc_v;      // fp32 dV accumulator (separate V only)
-  float* acc_cmp;    // fp32 dCmpKV accumulator (window+cmp only)
+  float* acc_k;      // fp32 dK (or shared dKV) accumulator, rows x Hkv x dqk (atomic mode)
+  float* acc_v;      // fp32 dV accumulator (separate V, atomic mode)
+  float* acc_cmp;    // fp32 dCmpKV accumulator (window+cmp, atomic mode)
   bf16* dq;
   float* dsinks;
+  // deterministic mode: one partial row per (head chunk, token, kv head,
+  // selected position) of tokens [t0, t0 + Tc), RW columns each
+  // (shared KV: dKV [dqk]; separate: dK [dqk] then dV [dv])
+  void* partial;
+  int det;
+  int t0, Tc, npos, RW;
+};
+
+// Arguments of the key-major reduction of partial rows.
+struct ReduceArgs {
+  const void* partial;
+  int partial_bf16;
+  int RW, npos, n_hc, t0, Tc;
+  const int* row_ptr;    // CSR over keys of the chunk's slots
+  const int* entries;
+  const int* blk_base;   // block mode: first block id of every sequence
+  long long n_out_rows;  // kv rows * Hkv (+ cmp rows * Hkv)
+  long long n_kv_out;    // kv rows * Hkv
+  float* acc;            // [n_out_rows][RW]
+  int accumulate;        // 0: overwrite, 1: add
 };
 
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
@@ -27,13 +49,19 @@ hipError_t launch_bwd_rows(const Params& p, const BwdBuffers& w, hipStream_t s);
 hipError_t launch_dsinks(const Params& p, const BwdBuffers& w, hipStream_t s);
 hipError_t launch_cast_bf16(const float* src, bf16* dst, size_t n, hipStream_t s);
 bool bwd_rows_supported(int dqk, int dv, int shared);
+int bwd_rows_head_chunks(const Params& p);
 
 hipError_t launch_fwd_rows(const Params& p, bf16* o, float* lse, hipStream_t s);
 bool fwd_rows_supported(int dqk, int dv, int shared);
 
-// CSR transpose of the index lists.
-size_t csr_workspace_bytes(long long n_entries, long long n_keys);
-hipError_t launch_csr_transpose(const Params& p, long long n_keys, const int* key_base_of_seq,
+// CSR transpose of the index lists of tokens [t0, t1): row_ptr[n_keys + 1]
+// and entries (flat slot ids, ascending per key).
+size_t csr_workspace_bytes(long long n_slots, long long n_keys, int batch);
+hipError_t launch_block_base(const Params& p, int* blk_base, hipStream_t s);
+hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_keys, const int* blk_base,
                                 int* row_ptr, int* entries, void* ws, hipStream_t s);
+
+hipError_t launch_reduce(const Params& p, const ReduceArgs& r, hipStream_t s);
+hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk, bf16* a, bf16* b, hipStream_t s);
 
 }  // namespace sa

@@ -1,0 +1,183 @@
+// Deterministic key-major reduction of the per-pair dK/dV (dKV) partial rows.
+//
+// The row kernels write one partial row per (head chunk, token, kv head,
+// selected position) into a token-major buffer; this kernel sums, for
+// every output row, the partials that name it in a fixed order -- by the
+// CSR transpose of the index lists (ascending slot id), or for window
+// keys by ascending query token -- and adds the sum into an fp32
+// accumulator.  The order never depends on scheduling, so results are
+// bitwise repeatable.  (aclnnSparseFlashAttentionGrad, "Formula": dK[u] and
+// dV[u] collect the contributions of every query that gathered row u.)
+#include "sa_launch.h"
+
+namespace sa {
+
+namespace {
+
+template <typename PT>
+struct Vec8;
+
+template <>
+struct Vec8<float> {
+  // 4 floats per thread-step
+  static constexpr int kPer = 4;
+  __device__ static void add(const float* p, float* acc) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    acc[0] += v.x;
+    acc[1] += v.y;
+    acc[2] += v.z;
+    acc[3] += v.w;
+  }
+};
+
+template <>
+struct Vec8<bf16> {
+  static constexpr int kPer = 8;
+  __device__ static void add(const bf16* p, float* acc) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += (float)v[i];
+  }
+};
+
+// One group of TPR threads per output row; each thread owns kPer columns.
+template <typename PT>
+__global__ void reduce_kernel(Params p, ReduceArgs r) {
+  constexpr int kPer = Vec8<PT>::kPer;
+  const int tpr = r.RW / kPer;
+  const int sub = threadIdx.x % tpr;
+  const long long orow = (long long)blockIdx.x * (blockDim.x / tpr) + threadIdx.x / tpr;
+  if (orow >= r.n_out_rows || threadIdx.x / tpr >= blockDim.x / tpr) return;
+  const int col = sub * kPer;
+  const PT* part = static_cast<const PT*>(r.partial);
+  float acc[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
+  const long long rows_chunk = (long long)r.Tc * p.Hkv;          // partial rows per head chunk
+  const long long row0 = (long long)r.t0 * p.Hkv;
+  const int npos = r.npos;
+
+  auto add_entry = [&](long long prow, int pos) {
+    for (int hc = 0; hc < r.n_hc; ++hc) {
+      const PT* src = part + (((long long)hc * rows_chunk + prow - row0) * npos + pos) * r.RW + col;
+      Vec8<PT>::add(src, acc);
+    }
+  };
+
+  const bool is_cmp = orow >= r.n_kv_out;   // cmp rows follow the kv rows
+  if (!is_cmp && p.select == kSelWindowCmp) {
+    // window keys: query tokens t with t - win_left <= j <= t + win_right
+    const long long jg = orow / p.Hkv;                 // global kv row
+    const int g = (int)(orow - jg * p.Hkv);
+    // sequence of this kv row
+    int b = 0;
+    if (p.layout == kLayoutBSND) {
+      b = (int)(jg / p.Skv);
+    } else {
+      int lo = 0, hi = p.B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.cu_kv[mid] <= jg) lo = mid; else hi = mid;
+      }
+      b = lo;
+    }
+    const int kv_base = p.layout == kLayoutBSND ? b * p.Skv : p.cu_kv[b];
+    const int q_base = p.layout == kLayoutBSND ? b * p.Sq : p.cu_q[b];
+    const int q_len = p.layout == kLayoutBSND ? p.Sq : p.cu_q[b + 1] - p.cu_q[b];
+    const int jl = (int)(jg - kv_base);
+    int tl_lo = max(0, jl - p.win_right);
+    int tl_hi = min(q_len - 1, jl + p.win_left);
+    if (p.causal) tl_lo = max(tl_lo, jl);
+    for (int tl = tl_lo; tl <= tl_hi; ++tl) {
+      const int t = q_base + tl;
+      if (t < r.t0 || t >= r.t0 + r.Tc) continue;
+      add_entry((long long)t * p.Hkv + g, jl - (tl - p.win_left));
+    }
+  } else {
+    const long long key = is_cmp ? orow - r.n_kv_out : orow;
+    const long long kcsr = key;   // CSR key id (kv row * Hkv + g, block key, or cmp row * Hkv + g)
+    const int nwin = p.select == kSelWindowCmp ? p.win_left + 1 + p.win_right : 0;
+    if (p.select == kSelBlock) {
+      // orow is (global kv row, g); its block key comes from the sequence
+      const long long jg = orow / p.Hkv;
+      const int g = (int)(orow - jg * p.Hkv);
+      int b = 0;
+      if (p.layout == kLayoutBSND) {
+        b = (int)(jg / p.Skv);
+      } else {
+        int lo = 0, hi = p.B;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (p.cu_kv[mid] <= jg) lo = mid; else hi = mid;
+        }
+        b = lo;
+      }
+      const int kv_base = p.layout == kLayoutBSND ? b * p.Skv : p.cu_kv[b];
+      const int jl = (int)(jg - kv_base);
+      const long long bkey = (long long)(r.blk_base[b] + jl / p.bs) * p.Hkv + g;
+      const int off = jl % p.bs;
+      for (int e = r.row_ptr[bkey]; e < r.row_ptr[bkey + 1]; ++e) {
+        const long long slot = r.entries[e];
+        const long long prow = slot / p.topk;
+        const int s = (int)(slot - prow * p.topk);
+        if (p.causal) {
+          const SeqPos sp = seq_pos(p, (int)(prow / p.Hkv));
+          if (jl > sp.tl) continue;   // row masked inside the selected block
+        }
+        add_entry(prow, s * p.bs + off);
+      }
+    } else {
+      for (int e = r.row_ptr[kcsr]; e < r.row_ptr[kcsr + 1]; ++e) {
+        const long long slot = r.entries[e];
+        const long long prow = slot / p.topk;
+        add_entry(prow, nwin + (int)(slot - prow * p.topk));
+      }
+    }
+  }
+  float* dst = r.acc + orow * (long long)r.RW + col;
+  if (r.accumulate) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) dst[i] += acc[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) dst[i] = acc[i];
+  }
+}
+
+// fp32 accumulator rows [n][RW] -> bf16 outputs: first dqk columns to
+// `a`, the next dv columns (separate K/V) to `b`.
+__global__ void split_cast_kernel(const float* __restrict__ acc, long long n, int RW, int dqk, bf16* __restrict__ a,
+                                  bf16* __restrict__ b) {
+  const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  if (i >= n * RW) return;
+  const long long row = i / RW;
+  const int c = (int)(i - row * RW);
+  if (c < dqk) a[row * dqk + c] = (bf16)acc[i];
+  else b[row * (RW - dqk) + (c - dqk)] = (bf16)acc[i];
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const Params& p, const ReduceArgs& r, hipStream_t s) {
+  if (r.n_out_rows == 0) return hipSuccess;
+  const int kPer = r.partial_bf16 ? 8 : 4;
+  const int tpr = r.RW / kPer;
+  const int rpw = std::max(1, 512 / tpr);
+  const int threads = tpr * rpw;
+  const unsigned blocks = (unsigned)((r.n_out_rows + rpw - 1) / rpw);
+  if (r.partial_bf16)
+    hipLaunchKernelGGL(reduce_kernel<bf16>, dim3(blocks), dim3(threads), 0, s, p, r);
+  else
+    hipLaunchKernelGGL(reduce_kernel<float>, dim3(blocks), dim3(threads), 0, s, p, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk, bf16* a, bf16* b, hipStream_t s) {
+  const long long n = n_rows * RW;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_cast_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, acc, n_rows, RW, dqk, a,
+                     b);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -265,6 +265,12 @@ def make_indices(wl: Workload, rng: Optional[np.random.Generator] = None) -> np.
     return out
 
 
+def make_index_inputs(wl: Workload) -> Dict[str, object]:
+    """Only the index lists and sequence offsets of `wl` (no tensors)."""
+    return {"workload": wl, "idx": torch.from_numpy(make_indices(wl)),
+            "cu_seqlens": torch.from_numpy(wl.cu_seqlens()), "cu_seqlens_cmp": torch.from_numpy(wl.cu_seqlens_cmp())}
+
+
 def make_inputs(wl: Workload, with_indices: bool = True, threads: int = 8) -> Dict[str, object]:
     """Seeded bf16 inputs for `wl` on the CPU (torch tensors), plus metadata.
 
