@@ -90,7 +90,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mla_token_8k", choices=W.WORKLOAD_ORDER)
-    ap.add_argument("--dkv-mode", default="atomic", choices=["atomic", "deterministic"])
+    ap.add_argument("--dkv-mode", default="deterministic", choices=["atomic", "deterministic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
@@ -174,7 +174,8 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "bwd_rows_kernel",
+            "kernel": "mla_bwd_kernel" if (wl.kv_shared and wl.d_qk == 576 and args.dkv_mode == "deterministic")
+                      else "bwd_rows_kernel",
             "bound": "mfma",
             "achieved": round(kern_tflops, 3),
             "peak": PEAK_BF16_TFLOPS,

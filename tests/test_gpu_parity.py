@@ -140,7 +140,7 @@ def test_bwd_parity_nsa_block_full_size(mode):
     U.run_full_case(W.WORKLOADS["nsa_block_gqa"], dkv_mode=MODES[mode])
 
 
-def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0):
+def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINISTIC):
     """Full-size run where only the compared rows need the oracle: GPU
     forward supplies O/lse for all tokens, the oracle's own O/lse replace
     them for the last n_tail tokens (and a few early ones); compared are dq
@@ -150,7 +150,7 @@ def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0):
     inp = W.make_inputs(wl)
     T = wl.total_q
     dev = B.device_tensors(inp)
-    desc = B.make_desc(wl)
+    desc = B.make_desc(wl, dkv_mode)
     U.say(f"[full] {wl.name}: GPU forward")
     o, lse = B.sparse_attn_fwd(desc, dev)
     rng = np.random.default_rng(seed)
@@ -183,8 +183,9 @@ def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0):
     return U.compare_all(got, ref, rows=rows, tag=wl.name)
 
 
-def test_bwd_parity_mla_8k_full_size_sampled():
-    _tail_splice_case(W.WORKLOADS["mla_token_8k"])
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_parity_mla_8k_full_size_sampled(mode):
+    _tail_splice_case(W.WORKLOADS["mla_token_8k"], dkv_mode=MODES[mode])
 
 
 def test_bwd_parity_mla_32k_full_size_sampled():

@@ -72,7 +72,7 @@ sa_status_t validate(const sa_desc_t* d) {
 
 // Partial-row buffer cap of the deterministic path; larger problems are
 // processed in token chunks whose partials fit under it.
-constexpr size_t kPartialCap = size_t(8) << 30;
+constexpr size_t kPartialCap = size_t(24) << 30;
 
 long long n_positions_host(const sa_desc_t* d) {
   if (d->select == SA_SEL_TOKEN) return d->topk;
@@ -96,7 +96,7 @@ Params make_params(const sa_desc_t* d);
 struct BwdLayout {
   size_t D, sink_term, acc_k, acc_v, acc_cmp;                   // atomic mode
   size_t blk_base, row_ptr, entries, csr_ws, partial, acc;      // deterministic mode
-  int Tc, n_hc, RW;
+  int Tc, n_hc, RW, fast;
   size_t total;
 };
 
@@ -121,9 +121,11 @@ BwdLayout bwd_layout(const sa_desc_t* d, const Params& p) {
     return L;
   }
   L.RW = d->kv_shared ? d->d_qk : d->d_qk + d->d_v;
-  L.n_hc = sa::bwd_rows_head_chunks(p);
+  L.fast = sa::mla_bwd_supported(p) ? 1 : 0;
+  L.n_hc = L.fast ? sa::mla_bwd_head_groups(p) : sa::bwd_rows_head_chunks(p);
   const size_t npos = (size_t)n_positions_host(d);
-  const size_t per_token = (size_t)L.n_hc * Hkv * npos * L.RW * sizeof(float);
+  const size_t elem = L.fast ? 2 : 4;   // bf16 partials from the MLA kernel, fp32 otherwise
+  const size_t per_token = (size_t)L.n_hc * Hkv * npos * L.RW * elem;
   size_t Tc = per_token ? std::max<size_t>(1, kPartialCap / per_token) : T;
   L.Tc = (int)std::min<size_t>(std::max<size_t>(T, 1), Tc);
   const long long nk = csr_keys_bound(d);
@@ -290,7 +292,7 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   sa::ReduceArgs r;
   std::memset(&r, 0, sizeof(r));
   r.partial = w.partial;
-  r.partial_bf16 = 0;
+  r.partial_bf16 = L.fast;
   r.RW = L.RW;
   r.npos = w.npos;
   r.n_hc = L.n_hc;
@@ -308,7 +310,7 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     if (has_slots)
       SA_TRY_HIP(sa::launch_csr_transpose(p, t0, t1, nk, blk_base, row_ptr, entries, ws + L.csr_ws, s));
     if (ev_main_start && first) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
-    SA_TRY_HIP(sa::launch_bwd_rows(p, w, s));
+    SA_TRY_HIP(L.fast ? sa::launch_bwd_mla(p, w, s) : sa::launch_bwd_rows(p, w, s));
     if (ev_main_stop && t1 == p.T) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
     r.t0 = t0;
     r.Tc = t1 - t0;

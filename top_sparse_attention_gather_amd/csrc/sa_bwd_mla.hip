@@ -1,0 +1,291 @@
+// Shared-KV (MLA) sparse-attention backward, d_qk = 576, d_v = 512, 64
+// query heads of one (token, kv head) row per workgroup.
+//
+// Formulas: SparseFlashMlaGrad README, "Computation formula", Stage 2
+// (P = SimpleSoftmax(scale Q KV^T, lse), dP = dO KV^T, dS = P (dP - D)) and
+// Stage 3 (dQ = scale dS KV, dKV = scale dS^T Q + P^T dO); gathers as in
+// aclnnSparseFlashAttentionGrad, "Formula".
+//
+// Work split (4 waves, one per SIMD, 1 workgroup per CU):
+//   phase A, wave w owns heads 16w..16w+15 for every key of a 32-key tile:
+//     S^T = KV Q^T and dP^T = V dO^T (16x16x32 MFMA, KV fragments read once
+//     from LDS for both, Q/dO of the wave's heads resident in registers),
+//     P and dS in registers, dQ^T += KV^T dS^T (KV^T read from the same LDS
+//     tile with the transposing ds_read_b64_tr_b16; dS^T taken straight from
+//     the MFMA result layout, no LDS round trip).
+//   phase B, wave w owns dKV columns 128w..128w+127 and 512+16w..+15 for
+//     every key of the tile: dKV^T = Q^T (scale dS) + dO^T P over all 64
+//     heads (dS, P exchanged through LDS; Q^T/dO^T column slices resident in
+//     registers), written as bf16 into an LDS staging tile.
+//   The staging tile is stored (coalesced 16-byte stores of whole partial
+//   rows) at the start of the next tile, and the next KV tile is gathered
+//   with direct global->LDS loads while the current one computes, so
+//   neither the gather nor the store latency sits on the MFMA path.
+// Partial rows go to the token-major buffer consumed by the key-major
+// reduce (deterministic sum in CSR order).
+#include "sa_launch.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kNT = 32;            // keys per tile
+constexpr int kDQK = 576;
+constexpr int kDV = 512;
+constexpr int kHeads = 64;         // heads per workgroup
+constexpr int kKS = kDQK + 8;      // LDS row stride (elements) of KV / Q / dO tiles: 1168 B
+constexpr int kSS = kDQK + 8;      // staging row stride: 1168 B (16-byte rows, conflict-free 8-byte writes)
+constexpr int kXS = kHeads + 8;    // exchange row stride: 144 B
+constexpr int kMaxPos = 2048;
+constexpr int kUnitsPerRow = kKS * 2 / 16;           // 73 16-byte units per padded row
+constexpr int kTileUnits = kNT * kUnitsPerRow;       // 2336
+constexpr int kTileLoads = (kTileUnits + 63) / 64;   // 37 wave-wide 16-byte loads per tile
+
+struct __attribute__((aligned(16))) MlaSmem {
+  bf16 kv[2][kNT * kKS];           // KV tiles (double buffer); Q / dO staging at token start
+  bf16 stage[kNT * kSS];           // dKV partial tile (bf16)
+  bf16 xds[kNT * kXS];             // scale * dS  [key][head]
+  bf16 xp[kNT * kXS];              // P           [key][head]
+  int rows[kMaxPos];
+  int vpos[kMaxPos];
+  int wave[4];
+};
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+__device__ __forceinline__ i16x4 tr_read(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join(i16x4 a, i16x4 b) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ const bf16* row_ptr(const Params& p, int code, int g) {
+  return (code & kCmpFlag) ? p.cmp + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * kDQK
+                           : p.k + ((size_t)code * p.Hkv + g) * kDQK;
+}
+
+// Gather the tile's rows (positions k0 .. k0+31 of the compacted list) into
+// `dst` with direct global->LDS loads; wave w issues loads w, w+4, ...
+__device__ __forceinline__ void gather_tile(const Params& p, const MlaSmem& sm, bf16* dst, int k0, int cnt,
+                                            int g, int wv, int lane) {
+  for (int j = wv; j < kTileLoads; j += 4) {
+    const int v = j * 64 + lane;
+    if (v < kTileUnits) {
+      const int r = v / kUnitsPerRow;
+      const int c = v - r * kUnitsPerRow;
+      const int code = sm.rows[(k0 + r < cnt) ? k0 + r : 0];
+      const bf16* src = row_ptr(p, code, g) + (c < kUnitsPerRow - 1 ? c * 8 : 0);
+      __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)(dst + j * 512), 16, 0, 0);
+    }
+  }
+}
+
+// Store the staged partial rows of a finished tile (nvalid rows).
+__device__ __forceinline__ void store_stage(const MlaSmem& sm, bf16* part_row0, int k0, int nvalid, int tid) {
+  for (int c = tid; c < nvalid * 72; c += kThreads) {
+    const int r = c / 72, ch = c - r * 72;
+    const uint4 v = *reinterpret_cast<const uint4*>(&sm.stage[r * kSS + ch * 8]);
+    *reinterpret_cast<uint4*>(part_row0 + (size_t)sm.vpos[k0 + r] * kDQK + ch * 8) = v;
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffers w) {
+  __shared__ MlaSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int row = w.t0 * p.Hkv + blockIdx.x;   // (token, kv head)
+  const int t = row / p.Hkv, g = row - t * p.Hkv;
+  const int h0 = g * p.G + blockIdx.y * kHeads;
+  const SeqPos s = seq_pos(p, t);
+  const int* irow = p.idx + (size_t)row * p.topk;
+  bf16* part_row0 = static_cast<bf16*>(w.partial) +
+                    (((size_t)blockIdx.y * w.Tc * p.Hkv + blockIdx.x) * w.npos) * kDQK;
+
+  // ---- compacted selection (positions and their row codes) --------------
+  const int cnt = compact_positions(p, s, irow, 0, n_positions(p), sm.rows, sm.wave, sm.vpos);
+
+  // ---- lse / D of the wave's heads (phase-A layout: head = 16 wv + l16) ---
+  const int hA = h0 + wv * 16 + l16;
+  const float lse = p.lse[(size_t)t * p.Hq + hA];
+  const float Dv = w.D[(size_t)t * p.Hq + hA];
+  const float kLog2e = 1.4426950408889634f;
+  const float lse2 = lse * kLog2e;
+  const float sl2 = p.scale * kLog2e;
+  const bool row_live = lse > -INFINITY;
+
+  // ---- Q and dO into registers, via LDS, in both operand layouts ---------
+  bf16x8 QA[18], dOA[16];          // phase A: [head 16wv + l16][32kk + 8lq .. +8]
+  bf16x8 QT[9][2], dOT[8][2];      // phase B: [col][heads 32ks + 8lq .. +8]
+  {
+    bf16* st = sm.kv[0];
+    const bf16* qsrc = p.q + ((size_t)t * p.Hq + h0) * kDQK;
+    for (int c = tid; c < kHeads * 72; c += kThreads) {
+      const int h = c / 72, ch = c - h * 72;
+      *reinterpret_cast<uint4*>(&st[h * kKS + ch * 8]) =
+          *reinterpret_cast<const uint4*>(qsrc + (size_t)h * kDQK + ch * 8);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk)
+      QA[kk] = *reinterpret_cast<const bf16x8*>(&st[(wv * 16 + l16) * kKS + kk * 32 + lq * 8]);
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      const int col0 = c < 8 ? wv * 128 + c * 16 : 512 + wv * 16;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16* b0 = &st[(ks * 32 + lq * 8 + (l16 >> 2)) * kKS + col0 + (l16 & 3) * 4];
+        QT[c][ks] = join(tr_read(b0), tr_read(b0 + 4 * kKS));
+      }
+    }
+    __syncthreads();
+    const bf16* dsrc = p.dO + ((size_t)t * p.Hq + h0) * kDV;
+    for (int c = tid; c < kHeads * 64; c += kThreads) {
+      const int h = c >> 6, ch = c & 63;
+      *reinterpret_cast<uint4*>(&st[h * kKS + ch * 8]) =
+          *reinterpret_cast<const uint4*>(dsrc + (size_t)h * kDV + ch * 8);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      dOA[kk] = *reinterpret_cast<const bf16x8*>(&st[(wv * 16 + l16) * kKS + kk * 32 + lq * 8]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int col0 = wv * 128 + c * 16;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16* b0 = &st[(ks * 32 + lq * 8 + (l16 >> 2)) * kKS + col0 + (l16 & 3) * 4];
+        dOT[c][ks] = join(tr_read(b0), tr_read(b0 + 4 * kKS));
+      }
+    }
+    __syncthreads();
+  }
+
+  f32x4 dQ[36];
+#pragma unroll
+  for (int m = 0; m < 36; ++m) dQ[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ntiles = (cnt + kNT - 1) / kNT;
+  if (ntiles > 0) gather_tile(p, sm, sm.kv[0], 0, cnt, g, wv, lane);
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = it * kNT;
+    const int nvalid = min(kNT, cnt - k0);
+    const bf16* kvb = sm.kv[it & 1];
+    // every wave's loads of this tile (and stores of older tiles) are done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 1 < ntiles) gather_tile(p, sm, sm.kv[(it + 1) & 1], k0 + kNT, cnt, g, wv, lane);
+    if (it > 0) store_stage(sm, part_row0, k0 - kNT, kNT, tid);
+
+    // ---- phase A: S^T and dP^T for the wave's 16 heads -------------------
+    f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = S0, P0 = S0, P1 = S0;
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&kvb[l16 * kKS + kk * 32 + lq * 8]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&kvb[(16 + l16) * kKS + kk * 32 + lq * 8]);
+      S0 = mfma16x16x32(a0, QA[kk], S0);
+      S1 = mfma16x16x32(a1, QA[kk], S1);
+      if (kk < 16) {
+        P0 = mfma16x16x32(a0, dOA[kk], P0);
+        P1 = mfma16x16x32(a1, dOA[kk], P1);
+      }
+    }
+    // P = exp(scale S - lse), dS = P (dP - D); lane: keys 16b + 4lq + r, head l16
+    bf16x8 Bds;
+    {
+      float pr[2][4], dsr[2][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kA = lq * 4 + r;
+        const bool vA = row_live && kA < nvalid;
+        const bool vB = row_live && 16 + kA < nvalid;
+        pr[0][r] = vA ? __builtin_amdgcn_exp2f(S0[r] * sl2 - lse2) : 0.f;
+        pr[1][r] = vB ? __builtin_amdgcn_exp2f(S1[r] * sl2 - lse2) : 0.f;
+        dsr[0][r] = pr[0][r] * (P0[r] - Dv);
+        dsr[1][r] = pr[1][r] * (P1[r] - Dv);
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = b * 16 + lq * 4 + r;
+          sm.xds[key * kXS + wv * 16 + l16] = (bf16)(dsr[b][r] * p.scale);
+          sm.xp[key * kXS + wv * 16 + l16] = (bf16)pr[b][r];
+          Bds[b * 4 + r] = (bf16)dsr[b][r];
+        }
+      }
+    }
+    // dQ^T[d][h] += KV^T[d][keys] dS^T[keys][h]; keys of k-group lq:
+    // 4lq..4lq+3 and 16+4lq..16+4lq+3, matching Bds
+#pragma unroll
+    for (int m = 0; m < 36; ++m) {
+      const bf16* b0 = &kvb[(lq * 4 + (l16 >> 2)) * kKS + m * 16 + (l16 & 3) * 4];
+      const bf16x8 a = join(tr_read(b0), tr_read(b0 + 16 * kKS));
+      dQ[m] = mfma16x16x32(a, Bds, dQ[m]);
+    }
+    __syncthreads();   // exchange written; staging free (its stores were issued)
+
+    // ---- phase B: dKV^T columns of this wave over all 64 heads -----------
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int krow = kb * 16 + l16;
+      const bf16x8 d0 = *reinterpret_cast<const bf16x8*>(&sm.xds[krow * kXS + lq * 8]);
+      const bf16x8 d1 = *reinterpret_cast<const bf16x8*>(&sm.xds[krow * kXS + 32 + lq * 8]);
+      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(&sm.xp[krow * kXS + lq * 8]);
+      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(&sm.xp[krow * kXS + 32 + lq * 8]);
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16x16x32(QT[c][0], d0, acc);
+        acc = mfma16x16x32(QT[c][1], d1, acc);
+        if (c < 8) {
+          acc = mfma16x16x32(dOT[c][0], p0, acc);
+          acc = mfma16x16x32(dOT[c][1], p1, acc);
+        }
+        const int col0 = (c < 8 ? wv * 128 + c * 16 : 512 + wv * 16) + lq * 4;
+        typedef short i16x4v __attribute__((ext_vector_type(4)));
+        i16x4v o = {bf16_bits((bf16)acc[0]), bf16_bits((bf16)acc[1]), bf16_bits((bf16)acc[2]),
+                    bf16_bits((bf16)acc[3])};
+        *reinterpret_cast<i16x4v*>(&sm.stage[krow * kSS + col0]) = o;
+      }
+    }
+  }
+
+  // ---- last tile's partial rows, then dQ ----------------------------------
+  if (ntiles > 0) {
+    __syncthreads();
+    store_stage(sm, part_row0, (ntiles - 1) * kNT, cnt - (ntiles - 1) * kNT, tid);
+  }
+  bf16* dq = w.dq + ((size_t)t * p.Hq + h0 + wv * 16 + l16) * kDQK;
+#pragma unroll
+  for (int m = 0; m < 36; ++m) {
+    typedef short i16x4v __attribute__((ext_vector_type(4)));
+    i16x4v o = {bf16_bits((bf16)(dQ[m][0] * p.scale)), bf16_bits((bf16)(dQ[m][1] * p.scale)),
+                bf16_bits((bf16)(dQ[m][2] * p.scale)), bf16_bits((bf16)(dQ[m][3] * p.scale))};
+    *reinterpret_cast<i16x4v*>(dq + m * 16 + lq * 4) = o;
+  }
+}
+
+}  // namespace
+
+bool mla_bwd_supported(const Params& p) {
+  return p.shared && p.dqk == kDQK && p.dv == kDV && p.G % kHeads == 0 && p.select != kSelBlock &&
+         (p.select == kSelToken ? p.topk : p.win_left + 1 + p.win_right + p.topk) <= kMaxPos;
+}
+
+int mla_bwd_head_groups(const Params& p) { return p.G / kHeads; }
+
+hipError_t launch_bwd_mla(const Params& p, const BwdBuffers& w, hipStream_t s) {
+  dim3 grid((unsigned)(w.Tc * p.Hkv), (unsigned)(p.G / kHeads));
+  hipLaunchKernelGGL(mla_bwd_kernel, grid, dim3(kThreads), 0, s, p, w);
+  return hipGetLastError();
+}
+
+}  // namespace sa

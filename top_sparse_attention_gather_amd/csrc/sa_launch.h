@@ -65,3 +65,10 @@ hipError_t launch_reduce(const Params& p, const ReduceArgs& r, hipStream_t s);
 hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk, bf16* a, bf16* b, hipStream_t s);
 
 }  // namespace sa
+
+namespace sa {
+// Shared-KV 576/512 backward with 64 heads per workgroup (bf16 partials).
+bool mla_bwd_supported(const Params& p);
+int mla_bwd_head_groups(const Params& p);
+hipError_t launch_bwd_mla(const Params& p, const BwdBuffers& w, hipStream_t s);
+}  // namespace sa
