@@ -38,12 +38,24 @@ constexpr int kKS = kDQK + 8;      // LDS row stride (elements) of KV / Q / dO t
 constexpr int kSS = kDQK + 8;      // staging row stride: 1168 B (16-byte rows, conflict-free 8-byte writes)
 constexpr int kXS = kHeads + 8;    // exchange row stride: 144 B
 constexpr int kMaxPos = 2048;
-constexpr int kUnitsPerRow = kKS * 2 / 16;           // 73 16-byte units per padded row
-constexpr int kTileUnits = kNT * kUnitsPerRow;       // 2336
-constexpr int kTileLoads = (kTileUnits + 63) / 64;   // 37 wave-wide 16-byte loads per tile
+// KV tile layout in LDS: 16-byte chunks (8 columns) grouped in pairs; pair
+// j holds chunks 2j (parity 0) and 2j+1 (parity 1), each as 32 row slots,
+// and row r of parity q sits in slot (r + 8q) mod 32.  One direct
+// global->LDS load (64 lanes x 16 B) fills one pair, with every lane on the
+// same row for the whole tile; the MFMA reads (16-byte rows of one chunk,
+// and the transposing 8-byte reads that span both parities) touch each
+// bank once per pass.
+constexpr int kTileElems = kDQK * kNT;               // 18432 (36 KiB)
+constexpr int kTilePairs = kDQK / 16;                // 36 pairs = 36 wave-wide loads
+constexpr int kStageElems = kHeads * kKS;            // Q / dO staging at token start (row-major)
+
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  const int par = chunk & 1;
+  return (chunk >> 1) * 512 + par * 256 + ((row + 8 * par) & 31) * 8;
+}
 
 struct __attribute__((aligned(16))) MlaSmem {
-  bf16 kv[2][kNT * kKS];           // KV tiles (double buffer); Q / dO staging at token start
+  bf16 kv[kStageElems];            // KV tiles at 0 and kTileElems; Q / dO staging at token start
   bf16 stage[kNT * kSS];           // dKV partial tile (bf16)
   bf16 xds[kNT * kXS];             // scale * dS  [key][head]
   bf16 xp[kNT * kXS];              // P           [key][head]
@@ -75,30 +87,35 @@ __device__ __forceinline__ const bf16* row_ptr(const Params& p, int code, int g)
 // `dst` with direct global->LDS loads; wave w issues loads w, w+4, ...
 __device__ __forceinline__ void gather_tile(const Params& p, const MlaSmem& sm, bf16* dst, int k0, int cnt,
                                             int g, int wv, int lane) {
-  for (int j = wv; j < kTileLoads; j += 4) {
-    const int v = j * 64 + lane;
-    if (v < kTileUnits) {
-      const int r = v / kUnitsPerRow;
-      const int c = v - r * kUnitsPerRow;
-      const int code = sm.rows[(k0 + r < cnt) ? k0 + r : 0];
-      const bf16* src = row_ptr(p, code, g) + (c < kUnitsPerRow - 1 ? c * 8 : 0);
-      __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)(dst + j * 512), 16, 0, 0);
-    }
+  const int par = lane >> 5;
+  const int r = ((lane & 31) - 8 * par) & 31;          // the row this lane fills in every pair
+  const int code = sm.rows[(k0 + r < cnt) ? k0 + r : k0];
+  const bf16* src = row_ptr(p, code, g) + par * 8;
+#pragma unroll
+  for (int i = 0; i < kTilePairs / 4; ++i) {
+    const int j = wv + 4 * i;
+    __builtin_amdgcn_global_load_lds((gbl_void*)(src + j * 16), (lds_void*)(dst + j * 512), 16, 0, 0);
   }
 }
 
-// Store the staged partial rows of a finished tile (nvalid rows).
+// Store the staged partial rows of a finished tile (nvalid rows): thread
+// t owns row t / 8 and chunks t % 8 + 8i, so each lane looks up one row.
 __device__ __forceinline__ void store_stage(const MlaSmem& sm, bf16* part_row0, int k0, int nvalid, int tid) {
-  for (int c = tid; c < nvalid * 72; c += kThreads) {
-    const int r = c / 72, ch = c - r * 72;
-    const uint4 v = *reinterpret_cast<const uint4*>(&sm.stage[r * kSS + ch * 8]);
-    *reinterpret_cast<uint4*>(part_row0 + (size_t)sm.vpos[k0 + r] * kDQK + ch * 8) = v;
-  }
+  const int r = tid >> 3, c0 = tid & 7;
+  if (r >= nvalid) return;
+  bf16* dst = part_row0 + (size_t)sm.vpos[k0 + r] * kDQK;
+  const bf16* src = &sm.stage[r * kSS];
+#pragma unroll
+  for (int i = 0; i < 9; ++i)
+    *reinterpret_cast<uint4*>(dst + (c0 + 8 * i) * 8) = *reinterpret_cast<const uint4*>(src + (c0 + 8 * i) * 8);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffers w) {
   __shared__ MlaSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform: keep it (and everything derived from it,
+  // e.g. the LDS destinations of the direct loads) in scalar registers
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lq = lane >> 4;
   const int row = w.t0 * p.Hkv + blockIdx.x;   // (token, kv head)
   const int t = row / p.Hkv, g = row - t * p.Hkv;
@@ -124,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   bf16x8 QA[18], dOA[16];          // phase A: [head 16wv + l16][32kk + 8lq .. +8]
   bf16x8 QT[9][2], dOT[8][2];      // phase B: [col][heads 32ks + 8lq .. +8]
   {
-    bf16* st = sm.kv[0];
+    bf16* st = sm.kv;
     const bf16* qsrc = p.q + ((size_t)t * p.Hq + h0) * kDQK;
     for (int c = tid; c < kHeads * 72; c += kThreads) {
       const int h = c / 72, ch = c - h * 72;
@@ -172,24 +189,33 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   for (int m = 0; m < 36; ++m) dQ[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ntiles = (cnt + kNT - 1) / kNT;
-  if (ntiles > 0) gather_tile(p, sm, sm.kv[0], 0, cnt, g, wv, lane);
+  if (ntiles > 0) gather_tile(p, sm, sm.kv, 0, cnt, g, wv, lane);
+
+  // per-lane LDS offsets inside a tile: phase-A fragments (row l16 or
+  // 16 + l16, chunk 4kk + lq) and the transposing reads of phase A4 (rows
+  // 4lq + l16/4 and 16 + 4lq + l16/4, columns 16m + 4(l16 % 4))
+  const int offA0 = tile_off(l16, lq);
+  const int offA1 = tile_off(16 + l16, lq);
+  const int trq = l16 & 3;
+  const int offT0 = tile_off(lq * 4 + (l16 >> 2), trq >> 1) + (trq & 1) * 4;
+  const int offT1 = tile_off(16 + lq * 4 + (l16 >> 2), trq >> 1) + (trq & 1) * 4;
 
   for (int it = 0; it < ntiles; ++it) {
     const int k0 = it * kNT;
     const int nvalid = min(kNT, cnt - k0);
-    const bf16* kvb = sm.kv[it & 1];
+    const bf16* kvb = sm.kv + (it & 1) * kTileElems;
     // every wave's loads of this tile (and stores of older tiles) are done
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (it + 1 < ntiles) gather_tile(p, sm, sm.kv[(it + 1) & 1], k0 + kNT, cnt, g, wv, lane);
+    if (it + 1 < ntiles) gather_tile(p, sm, sm.kv + ((it + 1) & 1) * kTileElems, k0 + kNT, cnt, g, wv, lane);
     if (it > 0) store_stage(sm, part_row0, k0 - kNT, kNT, tid);
 
     // ---- phase A: S^T and dP^T for the wave's 16 heads -------------------
     f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = S0, P0 = S0, P1 = S0;
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&kvb[l16 * kKS + kk * 32 + lq * 8]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&kvb[(16 + l16) * kKS + kk * 32 + lq * 8]);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&kvb[offA0 + kk * 1024]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&kvb[offA1 + kk * 1024]);
       S0 = mfma16x16x32(a0, QA[kk], S0);
       S1 = mfma16x16x32(a1, QA[kk], S1);
       if (kk < 16) {
@@ -226,8 +252,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     // 4lq..4lq+3 and 16+4lq..16+4lq+3, matching Bds
 #pragma unroll
     for (int m = 0; m < 36; ++m) {
-      const bf16* b0 = &kvb[(lq * 4 + (l16 >> 2)) * kKS + m * 16 + (l16 & 3) * 4];
-      const bf16x8 a = join(tr_read(b0), tr_read(b0 + 16 * kKS));
+      const bf16x8 a = join(tr_read(&kvb[offT0 + m * 512]), tr_read(&kvb[offT1 + m * 512]));
       dQ[m] = mfma16x16x32(a, Bds, dQ[m]);
     }
     __syncthreads();   // exchange written; staging free (its stores were issued)

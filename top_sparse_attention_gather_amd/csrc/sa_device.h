@@ -145,6 +145,40 @@ __device__ __forceinline__ int compact_positions(const Params& p, const SeqPos& 
   return total;
 }
 
+// Same result as compact_positions for n <= 256 * ROUNDS, with every
+// position decoded (and its index loaded) before the first ballot, so the
+// index loads overlap instead of costing one round trip per round.
+template <int ROUNDS>
+__device__ __forceinline__ int compact_positions_batched(const Params& p, const SeqPos& s,
+                                                         const int* __restrict__ irow, int n, int* sRows,
+                                                         int* sWave, int* sVpos) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int code[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int pos = r * 256 + tid;
+    code[r] = pos < n ? decode_position(p, s, irow, pos) : -1;
+  }
+  int total = 0;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    if (r * 256 >= n) break;
+    const unsigned long long m = __ballot(code[r] >= 0);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) sWave[w] = __popcll(m);
+    __syncthreads();
+    int off = total;
+    for (int i = 0; i < w; ++i) off += sWave[i];
+    if (code[r] >= 0) {
+      sRows[off + before] = code[r];
+      sVpos[off + before] = r * 256 + tid;
+    }
+    total += sWave[0] + sWave[1] + sWave[2] + sWave[3];
+    __syncthreads();
+  }
+  return total;
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -19,10 +19,10 @@ struct Vec8;
 
 template <>
 struct Vec8<float> {
-  // 4 floats per thread-step
-  static constexpr int kPer = 4;
-  __device__ static void add(const float* p, float* acc) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
+  static constexpr int kPer = 4;   // columns per thread-step
+  typedef float4 T;
+  __device__ static T load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static void add(const T& v, float* acc) {
     acc[0] += v.x;
     acc[1] += v.y;
     acc[2] += v.z;
@@ -33,12 +33,15 @@ struct Vec8<float> {
 template <>
 struct Vec8<bf16> {
   static constexpr int kPer = 8;
-  __device__ static void add(const bf16* p, float* acc) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+  typedef bf16x8 T;
+  __device__ static T load(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  __device__ static void add(const T& v, float* acc) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += (float)v[i];
   }
 };
+
+constexpr int kBatch = 8;   // partial rows whose loads are in flight together
 
 // One group of TPR threads per output row; each thread owns kPer columns.
 template <typename PT>
@@ -57,11 +60,21 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
   const long long row0 = (long long)r.t0 * p.Hkv;
   const int npos = r.npos;
 
-  auto add_entry = [&](long long prow, int pos) {
+  const long long hc_stride = rows_chunk * npos * (long long)r.RW;
+  // Adds up to kBatch partial rows (element offsets off[], for every head
+  // chunk) in the listed order; all loads are issued before the first add.
+  auto add_batch = [&](const long long* off, const bool* ok) {
     for (int hc = 0; hc < r.n_hc; ++hc) {
-      const PT* src = part + (((long long)hc * rows_chunk + prow - row0) * npos + pos) * r.RW + col;
-      Vec8<PT>::add(src, acc);
+      typename Vec8<PT>::T v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = Vec8<PT>::load(part + hc * hc_stride + off[u]);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (ok[u]) Vec8<PT>::add(v[u], acc);
     }
+  };
+  auto offset_of = [&](long long prow, int pos) -> long long {
+    return ((prow - row0) * npos + pos) * r.RW + col;
   };
 
   const bool is_cmp = orow >= r.n_kv_out;   // cmp rows follow the kv rows
@@ -88,10 +101,19 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
     int tl_lo = max(0, jl - p.win_right);
     int tl_hi = min(q_len - 1, jl + p.win_left);
     if (p.causal) tl_lo = max(tl_lo, jl);
-    for (int tl = tl_lo; tl <= tl_hi; ++tl) {
-      const int t = q_base + tl;
-      if (t < r.t0 || t >= r.t0 + r.Tc) continue;
-      add_entry((long long)t * p.Hkv + g, jl - (tl - p.win_left));
+    // only query tokens of this chunk contribute
+    tl_lo = max(tl_lo, r.t0 - q_base);
+    tl_hi = min(tl_hi, r.t0 + r.Tc - 1 - q_base);
+    for (int tb = tl_lo; tb <= tl_hi; tb += kBatch) {
+      long long off[kBatch];
+      bool ok[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        ok[u] = tb + u <= tl_hi;
+        const int tl = ok[u] ? tb + u : tl_lo;
+        off[u] = offset_of((long long)(q_base + tl) * p.Hkv + g, jl - (tl - p.win_left));
+      }
+      add_batch(off, ok);
     }
   } else {
     const long long key = is_cmp ? orow - r.n_kv_out : orow;
@@ -116,21 +138,37 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
       const int jl = (int)(jg - kv_base);
       const long long bkey = (long long)(r.blk_base[b] + jl / p.bs) * p.Hkv + g;
       const int off = jl % p.bs;
-      for (int e = r.row_ptr[bkey]; e < r.row_ptr[bkey + 1]; ++e) {
-        const long long slot = r.entries[e];
-        const long long prow = slot / p.topk;
-        const int s = (int)(slot - prow * p.topk);
-        if (p.causal) {
-          const SeqPos sp = seq_pos(p, (int)(prow / p.Hkv));
-          if (jl > sp.tl) continue;   // row masked inside the selected block
+      const int eb = r.row_ptr[bkey], ee = r.row_ptr[bkey + 1];
+      for (int e = eb; e < ee; e += kBatch) {
+        long long offs[kBatch];
+        bool ok[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          ok[u] = e + u < ee;
+          const long long slot = r.entries[ok[u] ? e + u : eb];
+          const long long prow = slot / p.topk;
+          const int s = (int)(slot - prow * p.topk);
+          if (ok[u] && p.causal) {
+            const SeqPos sp = seq_pos(p, (int)(prow / p.Hkv));
+            ok[u] = jl <= sp.tl;     // row masked inside the selected block
+          }
+          offs[u] = offset_of(prow, s * p.bs + off);
         }
-        add_entry(prow, s * p.bs + off);
+        add_batch(offs, ok);
       }
     } else {
-      for (int e = r.row_ptr[kcsr]; e < r.row_ptr[kcsr + 1]; ++e) {
-        const long long slot = r.entries[e];
-        const long long prow = slot / p.topk;
-        add_entry(prow, nwin + (int)(slot - prow * p.topk));
+      const int eb = r.row_ptr[kcsr], ee = r.row_ptr[kcsr + 1];
+      for (int e = eb; e < ee; e += kBatch) {
+        long long offs[kBatch];
+        bool ok[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          ok[u] = e + u < ee;
+          const long long slot = r.entries[ok[u] ? e + u : eb];
+          const long long prow = slot / p.topk;
+          offs[u] = offset_of(prow, nwin + (int)(slot - prow * p.topk));
+        }
+        add_batch(offs, ok);
       }
     }
   }
