@@ -23,6 +23,8 @@
 //   neither the gather nor the store latency sits on the MFMA path.
 // Partial rows go to the token-major buffer consumed by the key-major
 // reduce (deterministic sum in CSR order).
+#include <type_traits>
+
 #include "sa_launch.h"
 
 namespace sa {
@@ -54,11 +56,16 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
   return (chunk >> 1) * 512 + par * 256 + ((row + 8 * par) & 31) * 8;
 }
 
+// dO^T operand blocks of phase B kept in LDS instead of registers (the
+// registers go to prefetching the MFMA operands).
+constexpr int kDotLds = 3;
+
 struct __attribute__((aligned(16))) MlaSmem {
   bf16 kv[kStageElems];            // KV tiles at 0 and kTileElems; Q / dO staging at token start
   bf16 stage[kNT * kSS];           // dKV partial tile (bf16)
   bf16 xds[kNT * kXS];             // scale * dS  [key][head]
   bf16 xp[kNT * kXS];              // P           [key][head]
+  bf16x8 dot[4][kDotLds][2][64];   // phase-B dO^T operand blocks 0..kDotLds-1, register layout per lane
   int rows[kMaxPos];
   int vpos[kMaxPos];
   int wave[4];
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
                     (((size_t)blockIdx.y * w.Tc * p.Hkv + blockIdx.x) * w.npos) * kDQK;
 
   // ---- compacted selection (positions and their row codes) --------------
-  const int cnt = compact_positions(p, s, irow, 0, n_positions(p), sm.rows, sm.wave, sm.vpos);
+  const int cnt = compact_positions_batched<kMaxPos / 256>(p, s, irow, n_positions(p), sm.rows, sm.wave, sm.vpos);
 
   // ---- lse / D of the wave's heads (phase-A layout: head = 16 wv + l16) ---
   const int hA = h0 + wv * 16 + l16;
@@ -141,44 +148,65 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   bf16x8 QA[18], dOA[16];          // phase A: [head 16wv + l16][32kk + 8lq .. +8]
   bf16x8 QT[9][2], dOT[8][2];      // phase B: [col][heads 32ks + 8lq .. +8]
   {
-    bf16* st = sm.kv;
-    const bf16* qsrc = p.q + ((size_t)t * p.Hq + h0) * kDQK;
-    for (int c = tid; c < kHeads * 72; c += kThreads) {
-      const int h = c / 72, ch = c - h * 72;
-      *reinterpret_cast<uint4*>(&st[h * kKS + ch * 8]) =
-          *reinterpret_cast<const uint4*>(qsrc + (size_t)h * kDQK + ch * 8);
+    // 32 heads per buffer, in the tile layout; every lane owns one head row
+    const int par = lane >> 5;
+    const int hr = ((lane & 31) - 8 * par) & 31;
+    // QA: head 16wv + l16 = buffer wv / 2, local row 16 (wv % 2) + l16
+    const bf16* qa = sm.kv + (wv >> 1) * kTileElems;
+    const int qrow = (wv & 1) * 16 + l16;
+    {
+      const bf16* src = p.q + ((size_t)t * p.Hq + h0 + hr) * kDQK + par * 8;
+#pragma unroll
+      for (int i = 0; i < 18; ++i) {
+        const int j = wv + 4 * i;          // 72 loads: pair j % 36 of buffer j / 36
+        const int hb = j >= 36 ? 1 : 0;
+        const int pj = j - 36 * hb;
+        __builtin_amdgcn_global_load_lds((gbl_void*)(src + (size_t)hb * 32 * kDQK + pj * 16),
+                                         (lds_void*)(sm.kv + hb * kTileElems + pj * 512), 16, 0, 0);
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk)
-      QA[kk] = *reinterpret_cast<const bf16x8*>(&st[(wv * 16 + l16) * kKS + kk * 32 + lq * 8]);
+    for (int kk = 0; kk < 18; ++kk) QA[kk] = *reinterpret_cast<const bf16x8*>(&qa[tile_off(qrow, 4 * kk + lq)]);
 #pragma unroll
     for (int c = 0; c < 9; ++c) {
       const int col0 = c < 8 ? wv * 128 + c * 16 : 512 + wv * 16;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16* b0 = &st[(ks * 32 + lq * 8 + (l16 >> 2)) * kKS + col0 + (l16 & 3) * 4];
-        QT[c][ks] = join(tr_read(b0), tr_read(b0 + 4 * kKS));
+        const bf16* b = sm.kv + ks * kTileElems;
+        const int r0 = lq * 8 + (l16 >> 2);
+        const int ch = (col0 >> 3) + ((l16 & 3) >> 1);
+        const int sub = (l16 & 1) * 4;
+        QT[c][ks] = join(tr_read(&b[tile_off(r0, ch) + sub]), tr_read(&b[tile_off(r0 + 4, ch) + sub]));
       }
     }
     __syncthreads();
-    const bf16* dsrc = p.dO + ((size_t)t * p.Hq + h0) * kDV;
-    for (int c = tid; c < kHeads * 64; c += kThreads) {
-      const int h = c >> 6, ch = c & 63;
-      *reinterpret_cast<uint4*>(&st[h * kKS + ch * 8]) =
-          *reinterpret_cast<const uint4*>(dsrc + (size_t)h * kDV + ch * 8);
+    {
+      const bf16* src = p.dO + ((size_t)t * p.Hq + h0 + hr) * kDV + par * 8;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = wv + 4 * i;          // 64 loads: pair j % 32 of buffer j / 32
+        const int hb = j >= 32 ? 1 : 0;
+        const int pj = j - 32 * hb;
+        __builtin_amdgcn_global_load_lds((gbl_void*)(src + (size_t)hb * 32 * kDV + pj * 16),
+                                         (lds_void*)(sm.kv + hb * kTileElems + pj * 512), 16, 0, 0);
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-      dOA[kk] = *reinterpret_cast<const bf16x8*>(&st[(wv * 16 + l16) * kKS + kk * 32 + lq * 8]);
+    for (int kk = 0; kk < 16; ++kk) dOA[kk] = *reinterpret_cast<const bf16x8*>(&qa[tile_off(qrow, 4 * kk + lq)]);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int col0 = wv * 128 + c * 16;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16* b0 = &st[(ks * 32 + lq * 8 + (l16 >> 2)) * kKS + col0 + (l16 & 3) * 4];
-        dOT[c][ks] = join(tr_read(b0), tr_read(b0 + 4 * kKS));
+        const bf16* b = sm.kv + ks * kTileElems;
+        const int r0 = lq * 8 + (l16 >> 2);
+        const int ch = (col0 >> 3) + ((l16 & 3) >> 1);
+        const int sub = (l16 & 1) * 4;
+        const bf16x8 v = join(tr_read(&b[tile_off(r0, ch) + sub]), tr_read(&b[tile_off(r0 + 4, ch) + sub]));
+        if (c < kDotLds) sm.dot[wv][c][ks][lane] = v;
+        else dOT[c][ks] = v;
       }
     }
     __syncthreads();
@@ -200,27 +228,62 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   const int offT0 = tile_off(lq * 4 + (l16 >> 2), trq >> 1) + (trq & 1) * 4;
   const int offT1 = tile_off(16 + lq * 4 + (l16 >> 2), trq >> 1) + (trq & 1) * 4;
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One tile.  kvb (read) and kvn (filled by direct loads for the next
+  // tile) are restrict-qualified: they never overlap, and the alias scopes
+  // this gives every LDS access let the compiler skip waiting for the
+  // in-flight loads before each LDS read.
+  const int gpar = lane >> 5;
+  const int grow = ((lane & 31) - 8 * gpar) & 31;   // the row this lane gathers in every pair
+  const int srow = tid >> 3, scol = tid & 7;        // the staged row / chunks this thread stores
+
+  // STORE: whether the previous tile's staged partial rows are stored here.
+  // The next tile's direct loads and these stores are spread over the
+  // phase-A MFMAs (one or two per step) instead of being issued in a burst.
+  auto step = [&](const bf16* __restrict__ kvb, bf16* __restrict__ kvn, int it, auto store_tag) {
+    constexpr bool STORE = decltype(store_tag)::value;
     const int k0 = it * kNT;
     const int nvalid = min(kNT, cnt - k0);
-    const bf16* kvb = sm.kv + (it & 1) * kTileElems;
     // every wave's loads of this tile (and stores of older tiles) are done
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (it + 1 < ntiles) gather_tile(p, sm, sm.kv + ((it + 1) & 1) * kTileElems, k0 + kNT, cnt, g, wv, lane);
-    if (it > 0) store_stage(sm, part_row0, k0 - kNT, kNT, tid);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int kn = k0 + kNT;   // next tile (for the last tile a harmless reload into the free buffer)
+    const bf16* gsrc = row_ptr(p, sm.rows[(kn + grow < cnt) ? kn + grow : k0], g) + gpar * 8;
+    bf16* sdst = part_row0 + (size_t)sm.vpos[(STORE ? k0 - kNT : k0) + srow] * kDQK + scol * 8;
+    const bf16* ssrc = &sm.stage[srow * kSS + scol * 8];
+    auto vmem_step = [&](int kk) {
+      if (kk < 9) {
+        const int j = wv + 4 * kk;
+        __builtin_amdgcn_global_load_lds((gbl_void*)(gsrc + j * 16), (lds_void*)(kvn + j * 512), 16, 0, 0);
+      }
+      if (STORE && kk >= 2 && kk < 11) {
+        const int i = kk - 2;
+        *reinterpret_cast<uint4*>(sdst + i * 64) = *reinterpret_cast<const uint4*>(ssrc + i * 64);
+      }
+    };
 
     // ---- phase A: S^T and dP^T for the wave's 16 heads -------------------
     f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = S0, P0 = S0, P1 = S0;
+    {
+      constexpr int kPF = 2;   // KV fragments in flight ahead of their MFMAs
+      bf16x8 f0[kPF + 1], f1[kPF + 1];
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&kvb[offA0 + kk * 1024]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&kvb[offA1 + kk * 1024]);
-      S0 = mfma16x16x32(a0, QA[kk], S0);
-      S1 = mfma16x16x32(a1, QA[kk], S1);
-      if (kk < 16) {
-        P0 = mfma16x16x32(a0, dOA[kk], P0);
-        P1 = mfma16x16x32(a1, dOA[kk], P1);
+      for (int kk = 0; kk < kPF; ++kk) {
+        f0[kk] = *reinterpret_cast<const bf16x8*>(&kvb[offA0 + kk * 1024]);
+        f1[kk] = *reinterpret_cast<const bf16x8*>(&kvb[offA1 + kk * 1024]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) {
+        if (kk + kPF < 18) {
+          f0[(kk + kPF) % (kPF + 1)] = *reinterpret_cast<const bf16x8*>(&kvb[offA0 + (kk + kPF) * 1024]);
+          f1[(kk + kPF) % (kPF + 1)] = *reinterpret_cast<const bf16x8*>(&kvb[offA1 + (kk + kPF) * 1024]);
+        }
+        const bf16x8 a0 = f0[kk % (kPF + 1)], a1 = f1[kk % (kPF + 1)];
+        vmem_step(kk);
+        S0 = mfma16x16x32(a0, QA[kk], S0);
+        S1 = mfma16x16x32(a1, QA[kk], S1);
+        if (kk < 16) {
+          P0 = mfma16x16x32(a0, dOA[kk], P0);
+          P1 = mfma16x16x32(a1, dOA[kk], P1);
+        }
       }
     }
     // P = exp(scale S - lse), dS = P (dP - D); lane: keys 16b + 4lq + r, head l16
@@ -250,12 +313,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     }
     // dQ^T[d][h] += KV^T[d][keys] dS^T[keys][h]; keys of k-group lq:
     // 4lq..4lq+3 and 16+4lq..16+4lq+3, matching Bds
+    {
+      constexpr int kPF = 3;   // transposed KV operands in flight
+      bf16x8 fa[kPF + 1];
 #pragma unroll
-    for (int m = 0; m < 36; ++m) {
-      const bf16x8 a = join(tr_read(&kvb[offT0 + m * 512]), tr_read(&kvb[offT1 + m * 512]));
-      dQ[m] = mfma16x16x32(a, Bds, dQ[m]);
+      for (int m = 0; m < kPF; ++m) fa[m] = join(tr_read(&kvb[offT0 + m * 512]), tr_read(&kvb[offT1 + m * 512]));
+#pragma unroll
+      for (int m = 0; m < 36; ++m) {
+        if (m + kPF < 36)
+          fa[(m + kPF) % (kPF + 1)] = join(tr_read(&kvb[offT0 + (m + kPF) * 512]), tr_read(&kvb[offT1 + (m + kPF) * 512]));
+        dQ[m] = mfma16x16x32(fa[m % (kPF + 1)], Bds, dQ[m]);
+      }
     }
-    __syncthreads();   // exchange written; staging free (its stores were issued)
+    // exchange written, staging free (its stores were issued): an LDS-only
+    // barrier, so the next tile's gather stays in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // ---- phase B: dKV^T columns of this wave over all 64 heads -----------
 #pragma unroll
@@ -265,22 +337,51 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
       const bf16x8 d1 = *reinterpret_cast<const bf16x8*>(&sm.xds[krow * kXS + 32 + lq * 8]);
       const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(&sm.xp[krow * kXS + lq * 8]);
       const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(&sm.xp[krow * kXS + 32 + lq * 8]);
+      // two column blocks at a time so their MFMA chains interleave
 #pragma unroll
-      for (int c = 0; c < 9; ++c) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma16x16x32(QT[c][0], d0, acc);
-        acc = mfma16x16x32(QT[c][1], d1, acc);
-        if (c < 8) {
-          acc = mfma16x16x32(dOT[c][0], p0, acc);
-          acc = mfma16x16x32(dOT[c][1], p1, acc);
+      for (int c = 0; c < 9; c += 2) {
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (c + u < 9) acc[u] = mfma16x16x32(QT[c + u][0], d0, acc[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (c + u < 9) acc[u] = mfma16x16x32(QT[c + u][1], d1, acc[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int cc = c + u;
+          if (cc < 8) {
+            const bf16x8 o0 = cc < kDotLds ? sm.dot[wv][cc < kDotLds ? cc : 0][0][lane] : dOT[cc][0];
+            acc[u] = mfma16x16x32(o0, p0, acc[u]);
+          }
         }
-        const int col0 = (c < 8 ? wv * 128 + c * 16 : 512 + wv * 16) + lq * 4;
-        typedef short i16x4v __attribute__((ext_vector_type(4)));
-        i16x4v o = {bf16_bits((bf16)acc[0]), bf16_bits((bf16)acc[1]), bf16_bits((bf16)acc[2]),
-                    bf16_bits((bf16)acc[3])};
-        *reinterpret_cast<i16x4v*>(&sm.stage[krow * kSS + col0]) = o;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int cc = c + u;
+          if (cc < 8) {
+            const bf16x8 o1 = cc < kDotLds ? sm.dot[wv][cc < kDotLds ? cc : 0][1][lane] : dOT[cc][1];
+            acc[u] = mfma16x16x32(o1, p1, acc[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int cc = c + u;
+          if (cc < 9) {
+            const int col0 = (cc < 8 ? wv * 128 + cc * 16 : 512 + wv * 16) + lq * 4;
+            typedef short i16x4v __attribute__((ext_vector_type(4)));
+            i16x4v o = {bf16_bits((bf16)acc[u][0]), bf16_bits((bf16)acc[u][1]), bf16_bits((bf16)acc[u][2]),
+                        bf16_bits((bf16)acc[u][3])};
+            *reinterpret_cast<i16x4v*>(&sm.stage[krow * kSS + col0]) = o;
+          }
+        }
       }
     }
+  };
+  if (ntiles > 0) step(sm.kv, sm.kv + kTileElems, 0, std::integral_constant<bool, false>());
+  for (int it = 1; it < ntiles; ++it) {
+    bf16* b0 = sm.kv + (it & 1) * kTileElems;
+    bf16* b1 = sm.kv + ((it + 1) & 1) * kTileElems;
+    step(b0, b1, it, std::integral_constant<bool, true>());
   }
 
   // ---- last tile's partial rows, then dQ ----------------------------------
