@@ -133,13 +133,6 @@ def test_fwd_parity_small(name):
     np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
 
 
-@pytest.mark.parametrize("mode", list(MODES))
-def test_bwd_parity_nsa_block_full_size(mode):
-    """The NSA-style block-sparse GQA workload at its full size (B=2,
-    S=4096, 16:1 heads, d=128, 16 blocks of 64): every output element."""
-    U.run_full_case(W.WORKLOADS["nsa_block_gqa"], dkv_mode=MODES[mode])
-
-
 def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINISTIC):
     """Full-size run where only the compared rows need the oracle: GPU
     forward supplies O/lse for all tokens, the oracle's own O/lse replace
@@ -179,8 +172,27 @@ def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINI
     rows = {"dq": toks, key: np.arange(T - n_tail, T)}
     if not wl.kv_shared:
         rows["dv"] = np.arange(T - n_tail, T)
+    if wl.select == W.SEL_WINDOW_CMP:
+        # cmp row c of the last sequence is visible only to tokens whose
+        # local position is >= cmp_ratio * c + cmp_ratio - 1
+        n_c = n_tail // wl.cmp_ratio
+        rows["d_cmp_kv"] = np.arange(wl.total_cmp - n_c, wl.total_cmp)
     got = {k: v for k, v in got.items() if k in rows}
     return U.compare_all(got, ref, rows=rows, tag=wl.name)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_parity_nsa_block_full_size_sampled(mode):
+    """The NSA-style block-sparse GQA workload at its full size (B=2,
+    S=4096, 16:1 heads, d=128, 16 blocks of 64), sampled rows."""
+    _tail_splice_case(W.WORKLOADS["nsa_block_gqa"], dkv_mode=MODES[mode])
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_parity_mla_cmp_sinks_varlen_full_size_sampled(mode):
+    """Window + cmp with sinks, varlen {1024, 3000, 6000, 16000}, at full
+    size: sampled dq rows, the last dKV rows and the last cmp rows."""
+    _tail_splice_case(W.WORKLOADS["mla_cmp_sinks_varlen"], dkv_mode=MODES[mode])
 
 
 @pytest.mark.parametrize("mode", list(MODES))

@@ -95,7 +95,7 @@ Params make_params(const sa_desc_t* d);
 
 struct BwdLayout {
   size_t D, sink_term, acc_k, acc_v, acc_cmp;                   // atomic mode
-  size_t blk_base, row_ptr, entries, csr_ws, partial, acc;      // deterministic mode
+  size_t blk_base, row_ptr, entries, csr_ws, partial, dump, acc;   // deterministic mode
   int Tc, n_hc, RW, fast;
   size_t total;
 };
@@ -139,6 +139,8 @@ BwdLayout bwd_layout(const sa_desc_t* d, const Params& p) {
   off += align_up(sa::csr_workspace_bytes((long long)L.Tc * Hkv * d->topk, nk, d->batch));
   L.partial = off;
   off += align_up((size_t)L.Tc * per_token);
+  L.dump = off;
+  off += align_up((size_t)L.RW * sizeof(float));
   L.acc = off;
   off += align_up((size_t)(rows_kv(d) + rows_cmp(d)) * Hkv * L.RW * sizeof(float));
   L.total = off;
@@ -287,6 +289,7 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   if (desc->select == SA_SEL_BLOCK) SA_TRY_HIP(sa::launch_block_base(p, blk_base, s));
   w.det = 1;
   w.partial = ws + L.partial;
+  w.dump = ws + L.dump;
   w.npos = (int)n_positions_host(desc);
   w.RW = L.RW;
   sa::ReduceArgs r;

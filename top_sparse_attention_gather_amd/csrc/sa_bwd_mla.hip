@@ -6,21 +6,22 @@
 // Stage 3 (dQ = scale dS KV, dKV = scale dS^T Q + P^T dO); gathers as in
 // aclnnSparseFlashAttentionGrad, "Formula".
 //
-// Work split (4 waves, one per SIMD, 1 workgroup per CU):
-//   phase A, wave w owns heads 16w..16w+15 for every key of a 32-key tile:
+// Work split (4 waves, one per SIMD, 1 workgroup per CU), per 32-key tile:
+//   phase A, wave w owns heads 16w..16w+15 for every key of the tile:
 //     S^T = KV Q^T and dP^T = V dO^T (16x16x32 MFMA, KV fragments read once
 //     from LDS for both, Q/dO of the wave's heads resident in registers),
-//     P and dS in registers, dQ^T += KV^T dS^T (KV^T read from the same LDS
-//     tile with the transposing ds_read_b64_tr_b16; dS^T taken straight from
-//     the MFMA result layout, no LDS round trip).
-//   phase B, wave w owns dKV columns 128w..128w+127 and 512+16w..+15 for
-//     every key of the tile: dKV^T = Q^T (scale dS) + dO^T P over all 64
-//     heads (dS, P exchanged through LDS; Q^T/dO^T column slices resident in
-//     registers), written as bf16 into an LDS staging tile.
-//   The staging tile is stored (coalesced 16-byte stores of whole partial
-//   rows) at the start of the next tile, and the next KV tile is gathered
-//   with direct global->LDS loads while the current one computes, so
-//   neither the gather nor the store latency sits on the MFMA path.
+//     keys 0..15 then 16..31, so that P and dS of the first half are
+//     computed while the MFMAs of the second half run; scale dS and P go
+//     to an LDS exchange ([key][head]).
+//   phase B, wave w owns dKV / dQ columns 128w..128w+127 and 512+16w..+15:
+//     dKV^T = Q^T (scale dS) + dO^T P over all 64 heads (Q^T/dO^T column
+//     slices resident in registers), stored as bf16 partial rows straight
+//     from the MFMA results; then dQ^T += KV^T (scale dS)^T for all 64
+//     heads, with KV^T of the wave's columns only (transposing
+//     ds_read_b64_tr_b16 reads) -- every wave reads a quarter of the tile
+//     instead of all of it.
+//   The next KV tile is gathered with direct global->LDS loads during
+//   phase A, so the gather latency is off the MFMA path.
 // Partial rows go to the token-major buffer consumed by the key-major
 // reduce (deterministic sum in CSR order).
 #include <type_traits>
@@ -37,7 +38,6 @@ constexpr int kDQK = 576;
 constexpr int kDV = 512;
 constexpr int kHeads = 64;         // heads per workgroup
 constexpr int kKS = kDQK + 8;      // LDS row stride (elements) of KV / Q / dO tiles: 1168 B
-constexpr int kSS = kDQK + 8;      // staging row stride: 1168 B (16-byte rows, conflict-free 8-byte writes)
 constexpr int kXS = kHeads + 8;    // exchange row stride: 144 B
 constexpr int kMaxPos = 2048;
 // KV tile layout in LDS: 16-byte chunks (8 columns) grouped in pairs; pair
@@ -58,13 +58,12 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
 
 // dO^T operand blocks of phase B kept in LDS instead of registers (the
 // registers go to prefetching the MFMA operands).
-constexpr int kDotLds = 3;
+constexpr int kDotLds = 5;
 
 struct __attribute__((aligned(16))) MlaSmem {
   bf16 kv[kStageElems];            // KV tiles at 0 and kTileElems; Q / dO staging at token start
-  bf16 stage[kNT * kSS];           // dKV partial tile (bf16)
-  bf16 xds[kNT * kXS];             // scale * dS  [key][head]
-  bf16 xp[kNT * kXS];              // P           [key][head]
+  bf16 xds[2][kNT * kXS];          // scale * dS  [key][head], tiles alternate
+  bf16 xp[2][kNT * kXS];           // P           [key][head]
   bf16x8 dot[4][kDotLds][2][64];   // phase-B dO^T operand blocks 0..kDotLds-1, register layout per lane
   int rows[kMaxPos];
   int vpos[kMaxPos];
@@ -103,18 +102,6 @@ __device__ __forceinline__ void gather_tile(const Params& p, const MlaSmem& sm, 
     const int j = wv + 4 * i;
     __builtin_amdgcn_global_load_lds((gbl_void*)(src + j * 16), (lds_void*)(dst + j * 512), 16, 0, 0);
   }
-}
-
-// Store the staged partial rows of a finished tile (nvalid rows): thread
-// t owns row t / 8 and chunks t % 8 + 8i, so each lane looks up one row.
-__device__ __forceinline__ void store_stage(const MlaSmem& sm, bf16* part_row0, int k0, int nvalid, int tid) {
-  const int r = tid >> 3, c0 = tid & 7;
-  if (r >= nvalid) return;
-  bf16* dst = part_row0 + (size_t)sm.vpos[k0 + r] * kDQK;
-  const bf16* src = &sm.stage[r * kSS];
-#pragma unroll
-  for (int i = 0; i < 9; ++i)
-    *reinterpret_cast<uint4*>(dst + (c0 + 8 * i) * 8) = *reinterpret_cast<const uint4*>(src + (c0 + 8 * i) * 8);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffers w) {
@@ -220,182 +207,212 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   if (ntiles > 0) gather_tile(p, sm, sm.kv, 0, cnt, g, wv, lane);
 
   // per-lane LDS offsets inside a tile: phase-A fragments (row l16 or
-  // 16 + l16, chunk 4kk + lq) and the transposing reads of phase A4 (rows
-  // 4lq + l16/4 and 16 + 4lq + l16/4, columns 16m + 4(l16 % 4))
+  // 16 + l16, chunk 4kk + lq) and the transposing reads of the dQ product
+  // (rows 4lq + l16/4 and 16 + 4lq + l16/4, columns 4(l16 % 4) of a
+  // 16-column block)
   const int offA0 = tile_off(l16, lq);
   const int offA1 = tile_off(16 + l16, lq);
   const int trq = l16 & 3;
   const int offT0 = tile_off(lq * 4 + (l16 >> 2), trq >> 1) + (trq & 1) * 4;
   const int offT1 = tile_off(16 + lq * 4 + (l16 >> 2), trq >> 1) + (trq & 1) * 4;
+  // the same key rows of the exchange ([key][head], heads 4(l16 % 4)..+3)
+  const int offX0 = (lq * 4 + (l16 >> 2)) * kXS + trq * 4;
+  const int offX1 = (16 + lq * 4 + (l16 >> 2)) * kXS + trq * 4;
+  bf16* dump = static_cast<bf16*>(w.dump);
+  const int gpar = lane >> 5;
+  const int grow = ((lane & 31) - 8 * gpar) & 31;   // the row this lane gathers in every pair
+  // phase-B / dQ column block c of this wave (16 columns)
+  auto col_block = [&](int c) { return c < 8 ? wv * 128 + c * 16 : 512 + wv * 16; };
+
+  // ---- phase B: dKV^T columns of this wave over all 64 heads for one key
+  // half (kb) of tile `itb`, stored as partial rows.  The 9 column-block
+  // MFMA chains of a half are spread over the phase-A steps of the next
+  // tile, so that the partial-row stores (the HBM write stream) go out
+  // evenly instead of in one burst that stalls the wave.
+  struct BHalf {
+    bf16x8 d0, d1, p0, p1;   // scale dS and P, B operands (key krow, heads 8lq..)
+    bf16* row;               // partial row of key krow (or the dump row)
+  };
+  auto b_setup = [&](int itb, int kb, bool live) {
+    BHalf h;
+    const bf16* xd = sm.xds[itb & 1];
+    const bf16* xpp = sm.xp[itb & 1];
+    const int krow = kb * 16 + l16;
+    h.d0 = *reinterpret_cast<const bf16x8*>(&xd[krow * kXS + lq * 8]);
+    h.d1 = *reinterpret_cast<const bf16x8*>(&xd[krow * kXS + 32 + lq * 8]);
+    h.p0 = *reinterpret_cast<const bf16x8*>(&xpp[krow * kXS + lq * 8]);
+    h.p1 = *reinterpret_cast<const bf16x8*>(&xpp[krow * kXS + 32 + lq * 8]);
+    // rows past the end of the list go to the dump row, so the stores need
+    // no branch
+    const int k0 = itb * kNT;
+    const bool kvalid = live && krow < cnt - k0;
+    h.row = kvalid ? part_row0 + (size_t)sm.vpos[kvalid ? k0 + krow : 0] * kDQK : dump;
+    return h;
+  };
+  auto b_chain = [&](const BHalf& h, int cc) {
+    f32x4 acc = mfma16x16x32(QT[cc][0], h.d0, f32x4{0.f, 0.f, 0.f, 0.f});
+    acc = mfma16x16x32(QT[cc][1], h.d1, acc);
+    if (cc < 8) {
+      const bf16x8 o0 = cc < kDotLds ? sm.dot[wv][cc < kDotLds ? cc : 0][0][lane] : dOT[cc][0];
+      const bf16x8 o1 = cc < kDotLds ? sm.dot[wv][cc < kDotLds ? cc : 0][1][lane] : dOT[cc][1];
+      acc = mfma16x16x32(o0, h.p0, acc);
+      acc = mfma16x16x32(o1, h.p1, acc);
+    }
+    return acc;
+  };
+  // Stores of the MFMA results (lane: columns 4lq..4lq+3 of a 16-column
+  // block, key l16).  Blocks c and c + 1 (c even, < 8) go out together:
+  // after swapping halves with the neighbouring 16-lane row, lane lq holds
+  // 8 contiguous columns (lq even: block c from 4lq, lq odd: block c + 1
+  // from 4(lq - 1)), so one 16-byte store per lane writes 64 contiguous
+  // bytes of every row -- half as many L1 write requests as 8-byte stores.
+  auto pk2 = [](float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, bf16x2{(bf16)a, (bf16)b});
+  };
+  auto b_put_pair = [&](const BHalf& h, int c, const f32x4& a, const f32x4& b) {
+    const auto s0 = __builtin_amdgcn_permlane16_swap(pk2(a[0], a[1]), pk2(b[0], b[1]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(pk2(a[2], a[3]), pk2(b[2], b[3]), false, false);
+    const uint4 v = {s0[0], s1[0], s0[1], s1[1]};
+    *reinterpret_cast<uint4*>(h.row + col_block(c) + (lq & 1) * 16 + (lq >> 1) * 8) = v;
+  };
+  auto b_put_single = [&](const BHalf& h, int c, const f32x4& a) {
+    const uint2 v = {pk2(a[0], a[1]), pk2(a[2], a[3])};
+    *reinterpret_cast<uint2*>(h.row + col_block(c) + lq * 4) = v;
+  };
 
   // One tile.  kvb (read) and kvn (filled by direct loads for the next
   // tile) are restrict-qualified: they never overlap, and the alias scopes
   // this gives every LDS access let the compiler skip waiting for the
   // in-flight loads before each LDS read.
-  const int gpar = lane >> 5;
-  const int grow = ((lane & 31) - 8 * gpar) & 31;   // the row this lane gathers in every pair
-  const int srow = tid >> 3, scol = tid & 7;        // the staged row / chunks this thread stores
-
-  // STORE: whether the previous tile's staged partial rows are stored here.
-  // The next tile's direct loads and these stores are spread over the
-  // phase-A MFMAs (one or two per step) instead of being issued in a burst.
-  auto step = [&](const bf16* __restrict__ kvb, bf16* __restrict__ kvn, int it, auto store_tag) {
-    constexpr bool STORE = decltype(store_tag)::value;
+  auto step = [&](const bf16* __restrict__ kvb, bf16* __restrict__ kvn, int it) {
     const int k0 = it * kNT;
     const int nvalid = min(kNT, cnt - k0);
-    // every wave's loads of this tile (and stores of older tiles) are done
+    // every wave's loads of this tile are done and the previous tile's
+    // exchange / KV buffer reads are finished
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int kn = k0 + kNT;   // next tile (for the last tile a harmless reload into the free buffer)
+    bf16* xw = sm.xds[it & 1];
+    bf16* pw = sm.xp[it & 1];
+    const int kn = k0 + kNT;   // next tile
     const bf16* gsrc = row_ptr(p, sm.rows[(kn + grow < cnt) ? kn + grow : k0], g) + gpar * 8;
-    bf16* sdst = part_row0 + (size_t)sm.vpos[(STORE ? k0 - kNT : k0) + srow] * kDQK + scol * 8;
-    const bf16* ssrc = &sm.stage[srow * kSS + scol * 8];
-    auto vmem_step = [&](int kk) {
-      if (kk < 9) {
-        const int j = wv + 4 * kk;
-        __builtin_amdgcn_global_load_lds((gbl_void*)(gsrc + j * 16), (lds_void*)(kvn + j * 512), 16, 0, 0);
-      }
-      if (STORE && kk >= 2 && kk < 11) {
-        const int i = kk - 2;
-        *reinterpret_cast<uint4*>(sdst + i * 64) = *reinterpret_cast<const uint4*>(ssrc + i * 64);
-      }
-    };
 
-    // ---- phase A: S^T and dP^T for the wave's 16 heads -------------------
-    f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = S0, P0 = S0, P1 = S0;
-    {
-      constexpr int kPF = 2;   // KV fragments in flight ahead of their MFMAs
-      bf16x8 f0[kPF + 1], f1[kPF + 1];
-#pragma unroll
-      for (int kk = 0; kk < kPF; ++kk) {
-        f0[kk] = *reinterpret_cast<const bf16x8*>(&kvb[offA0 + kk * 1024]);
-        f1[kk] = *reinterpret_cast<const bf16x8*>(&kvb[offA1 + kk * 1024]);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
-        if (kk + kPF < 18) {
-          f0[(kk + kPF) % (kPF + 1)] = *reinterpret_cast<const bf16x8*>(&kvb[offA0 + (kk + kPF) * 1024]);
-          f1[(kk + kPF) % (kPF + 1)] = *reinterpret_cast<const bf16x8*>(&kvb[offA1 + (kk + kPF) * 1024]);
-        }
-        const bf16x8 a0 = f0[kk % (kPF + 1)], a1 = f1[kk % (kPF + 1)];
-        vmem_step(kk);
-        S0 = mfma16x16x32(a0, QA[kk], S0);
-        S1 = mfma16x16x32(a1, QA[kk], S1);
-        if (kk < 16) {
-          P0 = mfma16x16x32(a0, dOA[kk], P0);
-          P1 = mfma16x16x32(a1, dOA[kk], P1);
-        }
-      }
-    }
-    // P = exp(scale S - lse), dS = P (dP - D); lane: keys 16b + 4lq + r, head l16
-    bf16x8 Bds;
-    {
-      float pr[2][4], dsr[2][4];
+    // ---- phase A: S^T and dP^T for the wave's 16 heads, two key halves ---
+    // P = exp(scale S - lse), dS = P (dP - D) for keys 16b + 4lq + r, head
+    // l16; scale dS and P into the exchange
+    auto softmax_grad = [&](int b, const f32x4& S, const f32x4& dP) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int kA = lq * 4 + r;
-        const bool vA = row_live && kA < nvalid;
-        const bool vB = row_live && 16 + kA < nvalid;
-        pr[0][r] = vA ? __builtin_amdgcn_exp2f(S0[r] * sl2 - lse2) : 0.f;
-        pr[1][r] = vB ? __builtin_amdgcn_exp2f(S1[r] * sl2 - lse2) : 0.f;
-        dsr[0][r] = pr[0][r] * (P0[r] - Dv);
-        dsr[1][r] = pr[1][r] * (P1[r] - Dv);
+        const int key = b * 16 + lq * 4 + r;
+        const bool v = row_live && key < nvalid;
+        const float pr = v ? __builtin_amdgcn_exp2f(S[r] * sl2 - lse2) : 0.f;
+        const float ds = pr * (dP[r] - Dv);
+        xw[key * kXS + wv * 16 + l16] = (bf16)(ds * p.scale);
+        pw[key * kXS + wv * 16 + l16] = (bf16)pr;
       }
+    };
+    f32x4 Sh0, Ph0;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 2; ++b) {
+      const int off = b ? offA1 : offA0;
+      constexpr int kPF = 2;   // KV fragments in flight ahead of their MFMAs
+      bf16x8 f[kPF + 1];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = b * 16 + lq * 4 + r;
-          sm.xds[key * kXS + wv * 16 + l16] = (bf16)(dsr[b][r] * p.scale);
-          sm.xp[key * kXS + wv * 16 + l16] = (bf16)pr[b][r];
-          Bds[b * 4 + r] = (bf16)dsr[b][r];
+      for (int kk = 0; kk < kPF; ++kk) f[kk] = *reinterpret_cast<const bf16x8*>(&kvb[off + kk * 1024]);
+      f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = S;
+      // phase B of the previous tile, key half b (for the first tile the
+      // products run on stale exchange data and go to the dump row)
+      const BHalf hb = b_setup(it - 1, b, it > 0);
+      f32x4 br[9];
+#pragma unroll
+      for (int kk = 0; kk < 18; ++kk) {
+        if ((kk & 1) == 0) {
+          const int cc = kk >> 1;
+          br[cc] = b_chain(hb, cc);
+          if (cc >= 2 && (cc & 1) == 0) b_put_pair(hb, cc - 2, br[cc - 2], br[cc - 1]);
         }
+        if (kk + kPF < 18) f[(kk + kPF) % (kPF + 1)] = *reinterpret_cast<const bf16x8*>(&kvb[off + (kk + kPF) * 1024]);
+        if (b == 0 && (kk & 1) == 0) {
+          // next tile's rows: one direct load every other step (for the
+          // last tile a harmless reload into the free buffer)
+          const int j = wv + 4 * (kk >> 1);
+          __builtin_amdgcn_global_load_lds((gbl_void*)(gsrc + j * 16), (lds_void*)(kvn + j * 512), 16, 0, 0);
+        }
+        const bf16x8 a = f[kk % (kPF + 1)];
+        S = mfma16x16x32(a, QA[kk], S);
+        if (kk < 16) dP = mfma16x16x32(a, dOA[kk], dP);
+        if (b == 1 && kk == 2) softmax_grad(0, Sh0, Ph0);
+      }
+      b_put_single(hb, 8, br[8]);
+      if (b == 0) {
+        Sh0 = S;
+        Ph0 = dP;
+      } else {
+        softmax_grad(1, S, dP);
       }
     }
-    // dQ^T[d][h] += KV^T[d][keys] dS^T[keys][h]; keys of k-group lq:
-    // 4lq..4lq+3 and 16+4lq..16+4lq+3, matching Bds
-    {
-      constexpr int kPF = 3;   // transposed KV operands in flight
-      bf16x8 fa[kPF + 1];
-#pragma unroll
-      for (int m = 0; m < kPF; ++m) fa[m] = join(tr_read(&kvb[offT0 + m * 512]), tr_read(&kvb[offT1 + m * 512]));
-#pragma unroll
-      for (int m = 0; m < 36; ++m) {
-        if (m + kPF < 36)
-          fa[(m + kPF) % (kPF + 1)] = join(tr_read(&kvb[offT0 + (m + kPF) * 512]), tr_read(&kvb[offT1 + (m + kPF) * 512]));
-        dQ[m] = mfma16x16x32(fa[m % (kPF + 1)], Bds, dQ[m]);
-      }
-    }
-    // exchange written, staging free (its stores were issued): an LDS-only
-    // barrier, so the next tile's gather stays in flight
+    // exchange written: an LDS-only barrier, so the gather stays in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // ---- phase B: dKV^T columns of this wave over all 64 heads -----------
+    // ---- dQ^T[cols][h] += KV^T[cols][keys] (scale dS^T)[keys][h] ---------
+    // keys of k-group lq: 4lq..4lq+3 and 16+4lq..16+4lq+3 on both operands
+    {
+      bf16x8 bt[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int krow = kb * 16 + l16;
-      const bf16x8 d0 = *reinterpret_cast<const bf16x8*>(&sm.xds[krow * kXS + lq * 8]);
-      const bf16x8 d1 = *reinterpret_cast<const bf16x8*>(&sm.xds[krow * kXS + 32 + lq * 8]);
-      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(&sm.xp[krow * kXS + lq * 8]);
-      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(&sm.xp[krow * kXS + 32 + lq * 8]);
-      // two column blocks at a time so their MFMA chains interleave
+      for (int hb = 0; hb < 4; ++hb)
+        bt[hb] = join(tr_read(&xw[offX0 + hb * 16]), tr_read(&xw[offX1 + hb * 16]));
+      constexpr int kPF = 2;   // transposed KV operands in flight
+      bf16x8 fa[kPF + 1];
 #pragma unroll
-      for (int c = 0; c < 9; c += 2) {
-        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      for (int c = 0; c < kPF; ++c) {
+        const int m = col_block(c) >> 4;
+        fa[c] = join(tr_read(&kvb[offT0 + m * 512]), tr_read(&kvb[offT1 + m * 512]));
+      }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          if (c + u < 9) acc[u] = mfma16x16x32(QT[c + u][0], d0, acc[u]);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          if (c + u < 9) acc[u] = mfma16x16x32(QT[c + u][1], d1, acc[u]);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int cc = c + u;
-          if (cc < 8) {
-            const bf16x8 o0 = cc < kDotLds ? sm.dot[wv][cc < kDotLds ? cc : 0][0][lane] : dOT[cc][0];
-            acc[u] = mfma16x16x32(o0, p0, acc[u]);
-          }
+      for (int c = 0; c < 9; ++c) {
+        if (c + kPF < 9) {
+          const int m = col_block(c + kPF) >> 4;
+          fa[(c + kPF) % (kPF + 1)] = join(tr_read(&kvb[offT0 + m * 512]), tr_read(&kvb[offT1 + m * 512]));
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int cc = c + u;
-          if (cc < 8) {
-            const bf16x8 o1 = cc < kDotLds ? sm.dot[wv][cc < kDotLds ? cc : 0][1][lane] : dOT[cc][1];
-            acc[u] = mfma16x16x32(o1, p1, acc[u]);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int cc = c + u;
-          if (cc < 9) {
-            const int col0 = (cc < 8 ? wv * 128 + cc * 16 : 512 + wv * 16) + lq * 4;
-            typedef short i16x4v __attribute__((ext_vector_type(4)));
-            i16x4v o = {bf16_bits((bf16)acc[u][0]), bf16_bits((bf16)acc[u][1]), bf16_bits((bf16)acc[u][2]),
-                        bf16_bits((bf16)acc[u][3])};
-            *reinterpret_cast<i16x4v*>(&sm.stage[krow * kSS + col0]) = o;
-          }
-        }
+        for (int hb = 0; hb < 4; ++hb) dQ[c * 4 + hb] = mfma16x16x32(fa[c % (kPF + 1)], bt[hb], dQ[c * 4 + hb]);
       }
     }
   };
-  if (ntiles > 0) step(sm.kv, sm.kv + kTileElems, 0, std::integral_constant<bool, false>());
-  for (int it = 1; it < ntiles; ++it) {
-    bf16* b0 = sm.kv + (it & 1) * kTileElems;
+  for (int it = 0; it < ntiles; ++it) {
+    const bf16* b0 = sm.kv + (it & 1) * kTileElems;
     bf16* b1 = sm.kv + ((it + 1) & 1) * kTileElems;
-    step(b0, b1, it, std::integral_constant<bool, true>());
+    step(b0, b1, it);
   }
 
-  // ---- last tile's partial rows, then dQ ----------------------------------
+  // phase B of the last tile
   if (ntiles > 0) {
-    __syncthreads();
-    store_stage(sm, part_row0, (ntiles - 1) * kNT, cnt - (ntiles - 1) * kNT, tid);
-  }
-  bf16* dq = w.dq + ((size_t)t * p.Hq + h0 + wv * 16 + l16) * kDQK;
 #pragma unroll
-  for (int m = 0; m < 36; ++m) {
-    typedef short i16x4v __attribute__((ext_vector_type(4)));
-    i16x4v o = {bf16_bits((bf16)(dQ[m][0] * p.scale)), bf16_bits((bf16)(dQ[m][1] * p.scale)),
-                bf16_bits((bf16)(dQ[m][2] * p.scale)), bf16_bits((bf16)(dQ[m][3] * p.scale))};
-    *reinterpret_cast<i16x4v*>(dq + m * 16 + lq * 4) = o;
+    for (int kb = 0; kb < 2; ++kb) {
+      const BHalf h = b_setup(ntiles - 1, kb, true);
+      f32x4 br[9];
+#pragma unroll
+      for (int cc = 0; cc < 9; ++cc) {
+        br[cc] = b_chain(h, cc);
+        if (cc >= 2 && (cc & 1) == 0) b_put_pair(h, cc - 2, br[cc - 2], br[cc - 1]);
+      }
+      b_put_single(h, 8, br[8]);
+    }
+  }
+  // no direct load may still be writing this workgroup's LDS when it ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- dQ (already scaled: the exchange holds scale dS) -------------------
+  // lane: columns col_block(c) + 4lq .. +3 of head 16hb + l16
+#pragma unroll
+  for (int c = 0; c < 9; ++c) {
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      bf16* dq = w.dq + ((size_t)t * p.Hq + h0 + hb * 16 + l16) * kDQK + col_block(c) + lq * 4;
+      const f32x4 v = dQ[c * 4 + hb];
+      typedef short i16x4v __attribute__((ext_vector_type(4)));
+      i16x4v o = {bf16_bits((bf16)v[0]), bf16_bits((bf16)v[1]), bf16_bits((bf16)v[2]), bf16_bits((bf16)v[3])};
+      *reinterpret_cast<i16x4v*>(dq) = o;
+    }
   }
 }
 

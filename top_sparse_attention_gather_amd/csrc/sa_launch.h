@@ -25,6 +25,7 @@ struct BwdBuffers {
   // selected position) of tokens [t0, t0 + Tc), RW columns each
   // (shared KV: dKV [dqk]; separate: dK [dqk] then dV [dv])
   void* partial;
+  void* dump;        // one never-read row: target of the stores of unused tile rows
   int det;
   int t0, Tc, npos, RW;
 };
