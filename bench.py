@@ -17,6 +17,7 @@ bounded sample on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +35,28 @@ from top_sparse_attention_gather_amd import workloads as W  # noqa: E402
 METRIC = "sparse-attn bwd TFLOP/s (selected-KV FLOPs) and % of bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
+
+# HBM bytes per launch of the dominant kernel on the MLA 8K workload, from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by the same counters on a
+# plain 1 GiB copy (`--copy-calibration`); valid only for the kernel source
+# they were taken on (its SHA-256), else reported as null.
+MEASURED_TRAFFIC = {
+    ("mla_token_8k", "deterministic"): {
+        "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
+        "sha256": "a83bca329a5de0ebee012405569ce6f4841c55620c61fbd93721c8d6475233bf",
+        "fetch_bytes": 8074726270, "write_bytes": 17518854048,
+    },
+}
+
+
+def measured_traffic(wl_name: str, mode: str):
+    t = MEASURED_TRAFFIC.get((wl_name, mode))
+    if t is None:
+        return None
+    with open(os.path.join(ROOT, t["kernel_source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
+            return None
+    return t["fetch_bytes"] + t["write_bytes"]
 
 
 def log(*a):
@@ -93,12 +116,25 @@ def main():
     ap.add_argument("--dkv-mode", default="deterministic", choices=["atomic", "deterministic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB): the known-size kernel "
+                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (see the design notes on "
               "sharding); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
+        return
 
     wl = W.WORKLOADS[args.workload]
     mode = B.DKV_ATOMIC if args.dkv_mode == "atomic" else B.DKV_DETERMINISTIC
@@ -181,7 +217,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name, args.dkv_mode),
+            "traffic_unit": "bytes per launch (HBM fetch + write, copy-calibrated rocprofv3 counters)",
             "kernel_ms": round(kern_ms, 4),
         },
         "cpu_baseline": cpu,
