@@ -88,6 +88,28 @@ def test_bwd_edge_shuffled_padding_duplicates_empty_rows(mode):
     assert np.all(got["dq"].reshape(ref["dq"].shape)[40] == 0)
 
 
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_block_edge_varlen_ragged_heads_duplicates(mode):
+    """Block selection, varlen TND with ragged last blocks (lengths 200 and
+    75, block 32), 20 query heads over 2 kv heads (a 16-head and a 4-head
+    chunk on the key-major path), shuffled -1 padding, a duplicated block,
+    an out-of-range block, and tokens with no block at all."""
+    wl = _wl(name="edge_block", select=W.SEL_BLOCK, layout=W.LAYOUT_TND, seqlens=(200, 75), n_q_heads=40,
+             n_kv_heads=2, d_qk=64, d_v=64, topk=4, block_size=32, index_policy="own_block_plus_uniform")
+    inp = W.make_inputs(wl)
+    idx = inp["idx"].numpy().copy()
+    rng = np.random.default_rng(5)
+    for t in range(idx.shape[0]):
+        for g in range(idx.shape[1]):
+            rng.shuffle(idx[t, g])
+    idx[150, 0, 0] = idx[150, 0, 1] = 2           # duplicate block
+    idx[151, 1, 2] = 999                          # out of range -> unused
+    idx[30] = -1                                  # no block for either kv head
+    inp["idx"] = torch.from_numpy(idx)
+    res, got, ref = U.run_full_case(wl, inputs=inp, dkv_mode=MODES[mode])
+    assert np.all(got["dq"].reshape(ref["dq"].shape)[30] == 0)
+
+
 def test_bwd_empty_query_is_noop():
     wl = _wl(name="empty", seqlens=(0,))
     desc = B.make_desc(wl)

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libsparse_attn.so")
 
-SOURCES = ["sa_api.hip", "sa_bwd_rows.hip", "sa_bwd_mla.hip", "sa_fwd_rows.hip", "sa_csr.hip", "sa_reduce.hip"]
+SOURCES = ["sa_api.hip", "sa_bwd_rows.hip", "sa_bwd_mla.hip", "sa_bwd_blk.hip", "sa_fwd_rows.hip", "sa_csr.hip",
+           "sa_reduce.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

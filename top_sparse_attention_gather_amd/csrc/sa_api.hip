@@ -96,7 +96,8 @@ Params make_params(const sa_desc_t* d);
 struct BwdLayout {
   size_t D, sink_term, acc_k, acc_v, acc_cmp;                   // atomic mode
   size_t blk_base, row_ptr, entries, csr_ws, partial, dump, acc;   // deterministic mode
-  int Tc, n_hc, RW, fast;
+  size_t bpart;                                                 // block key-major slices
+  int Tc, n_hc, RW, fast, blk_km, n_split, n_hc_blk;
   size_t total;
 };
 
@@ -125,10 +126,17 @@ BwdLayout bwd_layout(const sa_desc_t* d, const Params& p) {
   L.n_hc = L.fast ? sa::mla_bwd_head_groups(p) : sa::bwd_rows_head_chunks(p);
   const size_t npos = (size_t)n_positions_host(d);
   const size_t elem = L.fast ? 2 : 4;   // bf16 partials from the MLA kernel, fp32 otherwise
-  const size_t per_token = (size_t)L.n_hc * Hkv * npos * L.RW * elem;
+  // block selection with separate K/V: dK/dV from the key-major block
+  // kernel, no partial rows, one pass over all tokens
+  L.blk_km = (!L.fast && sa::blk_dkv_supported(p)) ? 1 : 0;
+  const size_t per_token = L.blk_km ? 0 : (size_t)L.n_hc * Hkv * npos * L.RW * elem;
   size_t Tc = per_token ? std::max<size_t>(1, kPartialCap / per_token) : T;
   L.Tc = (int)std::min<size_t>(std::max<size_t>(T, 1), Tc);
   const long long nk = csr_keys_bound(d);
+  if (L.blk_km) {
+    L.n_hc_blk = sa::blk_dkv_head_chunks(p);
+    L.n_split = sa::blk_dkv_splits(nk, L.n_hc_blk);
+  }
   L.blk_base = off;
   off += align_up((size_t)(d->batch + 1) * 4);
   L.row_ptr = off;
@@ -142,7 +150,10 @@ BwdLayout bwd_layout(const sa_desc_t* d, const Params& p) {
   L.dump = off;
   off += align_up((size_t)L.RW * sizeof(float));
   L.acc = off;
-  off += align_up((size_t)(rows_kv(d) + rows_cmp(d)) * Hkv * L.RW * sizeof(float));
+  if (!L.blk_km) off += align_up((size_t)(rows_kv(d) + rows_cmp(d)) * Hkv * L.RW * sizeof(float));
+  L.bpart = off;
+  if (L.blk_km)
+    off += align_up((size_t)L.n_hc_blk * L.n_split * rows_kv(d) * Hkv * (size_t)(2 * d->d_qk) * sizeof(float));
   L.total = off;
   return L;
 }
@@ -287,6 +298,35 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   const long long nk = csr_keys_bound(desc);
   const bool has_slots = desc->topk > 0;
   if (desc->select == SA_SEL_BLOCK) SA_TRY_HIP(sa::launch_block_base(p, blk_base, s));
+  if (L.blk_km) {
+    // dQ from the row kernel; dK/dV key-major over the CSR of block keys
+    if (has_slots) SA_TRY_HIP(sa::launch_csr_transpose(p, 0, p.T, nk, blk_base, row_ptr, entries, ws + L.csr_ws, s));
+    w.det = 1;
+    w.dq_only = 1;
+    if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
+    SA_TRY_HIP(sa::launch_bwd_rows(p, w, s));
+    if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
+    sa::BlkArgs ba;
+    std::memset(&ba, 0, sizeof(ba));
+    ba.row_ptr = row_ptr;
+    ba.entries = entries;
+    ba.blk_base = blk_base;
+    ba.D = w.D;
+    ba.part = reinterpret_cast<float*>(ws + L.bpart);
+    ba.rows_kv = rows_kv(desc);
+    ba.n_split = L.n_split;
+    ba.n_hc = L.n_hc_blk;
+    ba.n_keys = has_slots ? nk : 0;
+    const long long nrows = rows_kv(desc) * (long long)Hkv;
+    if (ba.n_keys) {
+      SA_TRY_HIP(sa::launch_blk_dkv(p, ba, s));
+    } else {
+      SA_TRY_HIP(sa::launch_fill_zero(ba.part, (size_t)nrows * 2 * desc->d_qk * L.n_split * L.n_hc_blk, s));
+    }
+    SA_TRY_HIP(sa::launch_blk_sum_cast(ba.part, L.n_split * L.n_hc_blk, nrows, desc->d_qk,
+                                       static_cast<bf16*>(a->dk), static_cast<bf16*>(a->dv), s));
+    return SA_OK;
+  }
   w.det = 1;
   w.partial = ws + L.partial;
   w.dump = ws + L.dump;

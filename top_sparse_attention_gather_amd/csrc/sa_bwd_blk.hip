@@ -1,0 +1,287 @@
+// Key-major dK/dV for block selection (NSA-style block-sparse GQA).
+//
+// Formulas: aclnnSparseFlashAttentionGrad, "Formula": Phase 1 dV[u] = P^T dO,
+// Phase 2 dS = P * (dP - softmax-grad(dO, O)), Phase 3 dK[u] = dS^T Q scale,
+// with u the rows of the blocks a query's index list names; P is recomputed
+// as exp(scale Q K^T - lse) (SparseFlashMlaGrad README, "Computation
+// formula", Stage 2).
+//
+// A selected block holds block_size rows and is named by many queries, so
+// instead of one partial row per (query, row) -- 1 KB of fp32 traffic per
+// pair at d = 128 -- one workgroup takes a block and walks the queries that
+// selected it (the CSR transpose of the index lists, in ascending slot
+// order), recomputing P and dS for the block's rows and accumulating dK and
+// dV in registers.  A key's list is cut into `n_split` slices (and the
+// query heads into chunks of 16) so that enough workgroups exist; each
+// writes its fp32 dK|dV rows to its own slice of the output buffer, and the
+// slices are summed in a fixed order afterwards, so the result is bitwise
+// repeatable.
+//
+// Workgroup: 4 waves; wave w owns block rows 16w..16w+15 (their K and V
+// fragments stay in registers for the whole list).  Per query: its 16
+// heads' Q and dO rows (and lse, D) are double-buffered through LDS;
+// S = Q K^T and dP = dO V^T on 16x16x32 MFMA; P and dS in registers, taken
+// straight from the MFMA result layout as the A operand of the 16x16x16
+// MFMAs dV += P^T dO and dK += dS^T Q, whose B operands are transposing LDS
+// reads of dO and Q.
+#include <type_traits>
+
+#include "sa_launch.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kHeads = 16;   // query heads per workgroup
+constexpr int kPD = 4;       // queries fetched ahead (the query loop below is unrolled by 4)
+constexpr int kIds = 512;    // query token ids staged in LDS at a time
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i16x4 tr_read4(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) {
+  constexpr int QS = D + 8;        // LDS row stride: 16-byte rows land 4 banks apart
+  constexpr int NK = D / 32;       // 16x16x32 steps over d
+  constexpr int NC = D / 16;       // 16-column blocks of dK / dV
+  constexpr int CPR = D / 8;       // 16-byte chunks per head row
+  __shared__ __attribute__((aligned(16))) bf16 sQ[2][kHeads * QS];
+  __shared__ __attribute__((aligned(16))) bf16 sdO[2][kHeads * QS];
+  __shared__ float sL[2][kHeads], sD[2][kHeads];
+  __shared__ int sTok[kIds];   // tokens of the current part of the list
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const long long bkey = blockIdx.x;
+  const int hc = blockIdx.y / a.n_split, split = blockIdx.y - hc * a.n_split;
+  const int bn = (int)(bkey / p.Hkv), g = (int)(bkey - (long long)bn * p.Hkv);
+  if (bn >= a.blk_base[p.B]) return;                 // past the last block (uniform)
+  int b = 0;
+  {
+    int lo = 0, hi = p.B;                            // largest b with blk_base[b] <= bn
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.blk_base[mid] <= bn) lo = mid; else hi = mid;
+    }
+    b = lo;
+  }
+  const int jb = bn - a.blk_base[b];                 // block index within the sequence
+  const int kv_base = p.layout == kLayoutBSND ? b * p.Skv : p.cu_kv[b];
+  const int kv_len = p.layout == kLayoutBSND ? p.Skv : p.cu_kv[b + 1] - p.cu_kv[b];
+  const int q_base = p.layout == kLayoutBSND ? b * p.Sq : p.cu_q[b];
+  const int h0 = g * p.G + hc * kHeads;
+  const int Gc = min(kHeads, p.G - hc * kHeads);
+  const int eb0 = a.row_ptr[bkey], n_all = a.row_ptr[bkey + 1] - eb0;
+  const int eb = eb0 + (int)((long long)n_all * split / a.n_split);
+  const int ee = eb0 + (int)((long long)n_all * (split + 1) / a.n_split);
+
+  // the wave's 16 block rows; this lane's row (B operand n index)
+  const int r0 = wv * 16;
+  const int jl = jb * p.bs + r0 + l16;               // sequence-local key row
+  const bool krow_ok = r0 + l16 < p.bs && jl < kv_len;
+  bf16x8 Kf[NK], Vf[NK];
+  {
+    const size_t off = ((size_t)(kv_base + (krow_ok ? jl : 0)) * p.Hkv + g) * D + lq * 8;
+    const bf16x8 z = {};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(p.k + off + kk * 32);
+      const bf16x8 vv = *reinterpret_cast<const bf16x8*>(p.v + off + kk * 32);
+      Kf[kk] = krow_ok ? kv : z;
+      Vf[kk] = krow_ok ? vv : z;
+    }
+  }
+  f32x4 dK[NC], dV[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) dK[c] = dV[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // staging of one query's rows: token t, heads h0..h0+Gc-1 (rows past Gc
+  // are zero, with lse = +inf so that their P is 0)
+  // queries are fetched kPD ahead into a register ring (slot = position in
+  // the list mod kPD) so the load latency spans several queries' work
+  constexpr int kR = (kHeads * CPR + kThreads - 1) / kThreads;
+  u32x4 qn[kPD][kR], dn[kPD][kR];
+  float ln[kPD], dln[kPD];
+  auto fetch = [&](int i, int u) {                    // i: position in the staged part
+    const int t = sTok[i];
+#pragma unroll
+    for (int i = 0; i < (kHeads * CPR + kThreads - 1) / kThreads; ++i) {
+      const int c = tid + i * kThreads;
+      const int h = c / CPR, col = (c - h * CPR) * 8;
+      // unconditional loads from a valid row (no branch, so the compiler
+      // can count the ring's loads in flight); zeroed past the head chunk
+      // when written to LDS
+      const bool ok = c < kHeads * CPR && h < Gc;
+      const size_t src = ((size_t)t * p.Hq + h0 + min(h, Gc - 1)) * D + (ok ? col : 0);
+      qn[u][i] = *reinterpret_cast<const u32x4*>(p.q + src);
+      dn[u][i] = *reinterpret_cast<const u32x4*>(p.dO + src);
+    }
+    const size_t hr = (size_t)t * p.Hq + h0 + min(tid, Gc - 1);   // always a valid head
+    ln[u] = p.lse[hr];
+    dln[u] = a.D[hr];
+  };
+  auto put = [&](int buf, int u) {
+#pragma unroll
+    for (int i = 0; i < (kHeads * CPR + kThreads - 1) / kThreads; ++i) {
+      const int c = tid + i * kThreads;
+      const int h = c / CPR, col = (c - h * CPR) * 8;
+      if (c < kHeads * CPR) {
+        // rows past the head chunk are zero (the select is made here, not at
+        // the load, so that the load's latency is not waited for early)
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&sQ[buf][h * QS + col]) = h < Gc ? qn[u][i] : z;
+        *reinterpret_cast<u32x4*>(&sdO[buf][h * QS + col]) = h < Gc ? dn[u][i] : z;
+      }
+    }
+    if (tid < kHeads) {
+      sL[buf][tid] = tid < Gc ? ln[u] : INFINITY;
+      sD[buf][tid] = tid < Gc ? dln[u] : 0.f;
+    }
+  };
+
+  const float kLog2e = 1.4426950408889634f;
+  const float sl2 = p.scale * kLog2e;
+  // transposing-read offsets: heads 4lq + l16/4, columns 4 (l16 % 4)
+  const int trow = lq * 4 + (l16 >> 2), tcol = (l16 & 3) * 4;
+  for (int c0 = eb; c0 < ee; c0 += kIds) {
+    const int n = min(kIds, ee - c0);
+    __syncthreads();   // the previous part's tokens are no longer read
+    for (int i = tid; i < n; i += kThreads) sTok[i] = (a.entries[c0 + i] / p.topk) / p.Hkv;
+    __syncthreads();
+    // the part is walked in groups of kPD queries; positions past the end
+    // reload the last query and contribute nothing, so the sequence of
+    // loads has no branches and the compiler can count them in flight
+    fetch(0, 0);
+    fetch(min(1, n - 1), 1);
+    fetch(min(2, n - 1), 2);
+    fetch(min(3, n - 1), 3);
+    put(0, 0);
+    __syncthreads();
+    // one query of the list; U: its ring slot (compile time, so the ring
+    // stays in registers)
+    auto query = [&](int i, auto U) {
+      constexpr int u = decltype(U)::value;
+      const int buf = i & 1;
+      // entry i's registers went to LDS at the end of the previous step
+      fetch(min(i + kPD, n - 1), u);
+      const int tl = sTok[min(i, n - 1)] - q_base;
+      if (r0 < p.bs) {
+        // S[h][key], dP[h][key]: lane holds heads 4lq + i of key l16
+        f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = S;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sQ[buf][l16 * QS + kk * 32 + lq * 8]);
+          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&sdO[buf][l16 * QS + kk * 32 + lq * 8]);
+          S = mfma16x16x32(aq, Kf[kk], S);
+          dP = mfma16x16x32(ad, Vf[kk], dP);
+        }
+        const bool key_ok = i < n && krow_ok && (!p.causal || jl <= tl);
+        i16x4 Pa, dSa;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = lq * 4 + r;
+          const float l = sL[buf][h];
+          const bool v = key_ok && l > -INFINITY && l < INFINITY;
+          const float pr = v ? __builtin_amdgcn_exp2f(S[r] * sl2 - l * kLog2e) : 0.f;
+          const float ds = pr * (dP[r] - sD[buf][h]);
+          Pa[r] = bf16_bits((bf16)pr);
+          dSa[r] = bf16_bits((bf16)ds);
+        }
+        // dV[key][d] += P^T dO, dK[key][d] += dS^T Q (head sum inside the MFMA)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const i16x4 bo = tr_read4(&sdO[buf][trow * QS + c * 16 + tcol]);
+          const i16x4 bq = tr_read4(&sQ[buf][trow * QS + c * 16 + tcol]);
+          dV[c] = mfma16x16x16(Pa, bo, dV[c]);
+          dK[c] = mfma16x16x16(dSa, bq, dK[c]);
+        }
+      }
+      // all waves are done with the other buffer (read two queries ago)
+      put(buf ^ 1, (u + 1) % kPD);
+      __syncthreads();
+    };
+    for (int i0 = 0; i0 < n; i0 += kPD) {
+      query(i0, std::integral_constant<int, 0>());
+      query(i0 + 1, std::integral_constant<int, 1>());
+      query(i0 + 2, std::integral_constant<int, 2>());
+      query(i0 + 3, std::integral_constant<int, 3>());
+    }
+  }
+
+  // this slice's dK|dV rows of the block: lane holds rows r0 + 4lq + i,
+  // columns 16c + l16
+  if (r0 < p.bs) {
+    const size_t slice = (size_t)hc * a.n_split + split;
+    const long long rows_total = a.rows_kv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = r0 + lq * 4 + i;
+      const int jr = jb * p.bs + rr;
+      if (rr < p.bs && jr < kv_len) {
+        float* dst = a.part + ((slice * rows_total + kv_base + jr) * p.Hkv + g) * (2 * D);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          dst[c * 16 + l16] = dK[c][i] * p.scale;
+          dst[D + c * 16 + l16] = dV[c][i];
+        }
+      }
+    }
+  }
+}
+
+// dK / dV = sum over the slices in slice order, rounded to bf16.
+__global__ void blk_sum_cast_kernel(const float* __restrict__ part, int n_slices, long long n_rows, int d,
+                                    bf16* __restrict__ dk, bf16* __restrict__ dv) {
+  const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  const long long per = n_rows * 2 * d;
+  if (i >= per) return;
+  float acc = 0.f;
+  for (int s = 0; s < n_slices; ++s) acc += part[(size_t)s * per + i];
+  const long long row = i / (2 * d);
+  const int c = (int)(i - row * 2 * d);
+  if (c < d) dk[row * d + c] = (bf16)acc;
+  else dv[row * d + (c - d)] = (bf16)acc;
+}
+
+}  // namespace
+
+bool blk_dkv_supported(const Params& p) {
+  return p.select == kSelBlock && !p.shared && p.dqk == p.dv && (p.dqk == 64 || p.dqk == 128) && p.bs >= 1 &&
+         p.bs <= 64;
+}
+
+int blk_dkv_head_chunks(const Params& p) { return (p.G + kHeads - 1) / kHeads; }
+
+int blk_dkv_splits(long long n_keys, int n_hc) {
+  // about 1024 workgroups in all, at most 16 slices per key
+  const long long per = std::max<long long>(1, n_keys * n_hc);
+  return (int)std::min<long long>(16, std::max<long long>(1, (1024 + per - 1) / per));
+}
+
+hipError_t launch_blk_dkv(const Params& p, const BlkArgs& a, hipStream_t s) {
+  if (a.n_keys == 0) return hipSuccess;
+  dim3 grid((unsigned)a.n_keys, (unsigned)(a.n_hc * a.n_split));
+  if (p.dqk == 128)
+    hipLaunchKernelGGL(blk_dkv_kernel<128>, grid, dim3(kThreads), 0, s, p, a);
+  else if (p.dqk == 64)
+    hipLaunchKernelGGL(blk_dkv_kernel<64>, grid, dim3(kThreads), 0, s, p, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_blk_sum_cast(const float* part, int n_slices, long long n_rows, int d, bf16* dk, bf16* dv,
+                               hipStream_t s) {
+  const long long n = n_rows * 2 * d;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(blk_sum_cast_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, n_slices, n_rows,
+                     d, dk, dv);
+  return hipGetLastError();
+}
+
+}  // namespace sa

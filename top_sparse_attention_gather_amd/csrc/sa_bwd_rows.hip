@@ -224,8 +224,10 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
         const bf16 pb = (bf16)pv, db = (bf16)ds;
         sP[h * PS + j] = pb;
         sdS[h * PS + j] = db;
-        sPt[j * TS + h] = pb;
-        sdSt[j * TS + h] = db;
+        if (!w.dq_only) {
+          sPt[j * TS + h] = pb;
+          sdSt[j * TS + h] = db;
+        }
       }
       __syncthreads();
 
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
       }
 
       // ---- dK / dV (dKV) tile contributions -> fp32 atomics -----------------
-      {
+      if (!w.dq_only) {
         constexpr int NOB = SHARED ? 2 * NQB : 2 * (NQB + NVB);
         for (int ob = wv; ob < NOB; ob += 4) {
           const int kb = ob & 1;

@@ -27,6 +27,7 @@ struct BwdBuffers {
   void* partial;
   void* dump;        // one never-read row: target of the stores of unused tile rows
   int det;
+  int dq_only;       // row kernel: dQ only (dK/dV come from the key-major block kernel)
   int t0, Tc, npos, RW;
 };
 
@@ -68,6 +69,28 @@ hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk
 }  // namespace sa
 
 namespace sa {
+// Key-major dK/dV of block selection (separate K/V, d_qk = d_v): one
+// workgroup per (block key, head chunk, slice of the key's CSR list), each
+// writing fp32 dK|dV rows of its block into its own slice of `part`
+// ([n_slices][kv rows][Hkv][2 d]); the slices are then summed in order.
+struct BlkArgs {
+  const int* row_ptr;
+  const int* entries;
+  const int* blk_base;
+  const float* D;   // [T][Hq] softmax-grad term
+  float* part;
+  long long rows_kv;  // kv rows of all sequences
+  int n_split;      // slices of every key's list
+  int n_hc;         // head chunks of 16
+  long long n_keys; // CSR keys (bound)
+};
+bool blk_dkv_supported(const Params& p);
+int blk_dkv_head_chunks(const Params& p);
+int blk_dkv_splits(long long n_keys, int n_hc);
+hipError_t launch_blk_dkv(const Params& p, const BlkArgs& a, hipStream_t s);
+hipError_t launch_blk_sum_cast(const float* part, int n_slices, long long n_rows, int d, bf16* dk, bf16* dv,
+                               hipStream_t s);
+
 // Shared-KV 576/512 backward with 64 heads per workgroup (bf16 partials).
 bool mla_bwd_supported(const Params& p);
 int mla_bwd_head_groups(const Params& p);

@@ -41,7 +41,7 @@ struct Vec8<bf16> {
   }
 };
 
-constexpr int kBatch = 8;   // partial rows whose loads are in flight together
+constexpr int kBatch = 16;  // partial rows whose loads are in flight together
 
 // One group of TPR threads per output row; each thread owns kPer columns.
 template <typename PT>
