@@ -40,25 +40,41 @@ constexpr int kHeads = 64;         // heads per workgroup
 constexpr int kKS = kDQK + 8;      // LDS row stride (elements) of KV / Q / dO tiles: 1168 B
 constexpr int kXS = kHeads + 8;    // exchange row stride: 144 B
 constexpr int kMaxPos = 2048;
-// KV tile layout in LDS: 16-byte chunks (8 columns) grouped in pairs; pair
-// j holds chunks 2j (parity 0) and 2j+1 (parity 1), each as 32 row slots,
-// and row r of parity q sits in slot (r + 8q) mod 32.  One direct
-// global->LDS load (64 lanes x 16 B) fills one pair, with every lane on the
-// same row for the whole tile; the MFMA reads (16-byte rows of one chunk,
-// and the transposing 8-byte reads that span both parities) touch each
-// bank once per pass.
-constexpr int kTileElems = kDQK * kNT;               // 18432 (36 KiB)
-constexpr int kTilePairs = kDQK / 16;                // 36 pairs = 36 wave-wide loads
-constexpr int kStageElems = kHeads * kKS;            // Q / dO staging at token start (row-major)
+// KV tile layout in LDS (32 rows x 72 chunks of 16 bytes): the rows form 4
+// groups of 8; group rg starts at rg * (9 KiB + 64 B) and holds 9
+// segments of 1 KiB, segment s = columns 64s..64s+63 of its 8 rows (row rr
+// at rr * 128 B), with chunk c at position (c & 4) | ((c & 3) ^ (rr >> 1)).
+//  - One direct global->LDS load (64 lanes x 16 B) fills one segment of one
+//    group: 8 whole 128-byte lines, half the address-unit work per byte of
+//    loads that touch a line per lane pair.  Wave w loads group w.
+//  - A 16-byte MFMA fragment read (16 rows, one chunk) hits 16 distinct
+//    4-bank groups (row parity, the 64-byte group skew and the XOR split
+//    them), and chunk c + 4 sits at a fixed offset from chunk c.
+constexpr int kSegElems = 512;                       // one 1 KiB segment
+constexpr int kGroupElems = 9 * kSegElems;           // 8 rows x 576 columns
+constexpr int kGroupStride = kGroupElems + 32;       // groups 64 B apart in bank phase
+constexpr int kTileElems = 4 * kGroupStride;         // 18560 (36.25 KiB)
+constexpr int kStageElems = kHeads * kKS;            // LDS of the KV tiles and of the Q / dO staging
+static_assert(2 * kTileElems <= kStageElems, "two tiles fit the staging region");
+
+__device__ __forceinline__ int group_base(int rg) { return rg * kGroupStride; }
 
 __device__ __forceinline__ int tile_off(int row, int chunk) {
-  const int par = chunk & 1;
-  return (chunk >> 1) * 512 + par * 256 + ((row + 8 * par) & 31) * 8;
+  const int rr = row & 7;
+  return group_base(row >> 3) + (chunk >> 3) * kSegElems + rr * 64 + ((chunk & 4) | ((chunk & 3) ^ (rr >> 1))) * 8;
+}
+
+// The chunk (within its segment) that lane `lane` of a wave-wide segment
+// load fetches: position lane & 7 of row lane >> 3 (the XOR is its own
+// inverse).
+__device__ __forceinline__ int seg_chunk(int lane) {
+  const int pos = lane & 7, rr = lane >> 3;
+  return (pos & 4) | ((pos & 3) ^ (rr >> 1));
 }
 
 // dO^T operand blocks of phase B kept in LDS instead of registers (the
 // registers go to prefetching the MFMA operands).
-constexpr int kDotLds = 5;
+constexpr int kDotLds = 6;
 
 struct __attribute__((aligned(16))) MlaSmem {
   bf16 kv[kStageElems];            // KV tiles at 0 and kTileElems; Q / dO staging at token start
@@ -90,18 +106,17 @@ __device__ __forceinline__ const bf16* row_ptr(const Params& p, int code, int g)
 }
 
 // Gather the tile's rows (positions k0 .. k0+31 of the compacted list) into
-// `dst` with direct global->LDS loads; wave w issues loads w, w+4, ...
+// `dst` with direct global->LDS loads; wave w loads row group w, one
+// segment per load.
 __device__ __forceinline__ void gather_tile(const Params& p, const MlaSmem& sm, bf16* dst, int k0, int cnt,
                                             int g, int wv, int lane) {
-  const int par = lane >> 5;
-  const int r = ((lane & 31) - 8 * par) & 31;          // the row this lane fills in every pair
+  const int r = wv * 8 + (lane >> 3);                   // the row this lane fills
   const int code = sm.rows[(k0 + r < cnt) ? k0 + r : k0];
-  const bf16* src = row_ptr(p, code, g) + par * 8;
+  const bf16* src = row_ptr(p, code, g) + seg_chunk(lane) * 8;
+  bf16* d = dst + group_base(wv);
 #pragma unroll
-  for (int i = 0; i < kTilePairs / 4; ++i) {
-    const int j = wv + 4 * i;
-    __builtin_amdgcn_global_load_lds((gbl_void*)(src + j * 16), (lds_void*)(dst + j * 512), 16, 0, 0);
-  }
+  for (int sg = 0; sg < 9; ++sg)
+    __builtin_amdgcn_global_load_lds((gbl_void*)(src + sg * 64), (lds_void*)(d + sg * kSegElems), 16, 0, 0);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffers w) {
@@ -135,22 +150,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   bf16x8 QA[18], dOA[16];          // phase A: [head 16wv + l16][32kk + 8lq .. +8]
   bf16x8 QT[9][2], dOT[8][2];      // phase B: [col][heads 32ks + 8lq .. +8]
   {
-    // 32 heads per buffer, in the tile layout; every lane owns one head row
-    const int par = lane >> 5;
-    const int hr = ((lane & 31) - 8 * par) & 31;
+    // 32 heads per buffer, in the tile layout; wave w loads row group w of
+    // both buffers (heads 32hb + 8w + lane / 8)
+    const int hr = wv * 8 + (lane >> 3);
+    const int sc = seg_chunk(lane) * 8;
     // QA: head 16wv + l16 = buffer wv / 2, local row 16 (wv % 2) + l16
     const bf16* qa = sm.kv + (wv >> 1) * kTileElems;
     const int qrow = (wv & 1) * 16 + l16;
     {
-      const bf16* src = p.q + ((size_t)t * p.Hq + h0 + hr) * kDQK + par * 8;
+      const bf16* src = p.q + ((size_t)t * p.Hq + h0 + hr) * kDQK + sc;
 #pragma unroll
-      for (int i = 0; i < 18; ++i) {
-        const int j = wv + 4 * i;          // 72 loads: pair j % 36 of buffer j / 36
-        const int hb = j >= 36 ? 1 : 0;
-        const int pj = j - 36 * hb;
-        __builtin_amdgcn_global_load_lds((gbl_void*)(src + (size_t)hb * 32 * kDQK + pj * 16),
-                                         (lds_void*)(sm.kv + hb * kTileElems + pj * 512), 16, 0, 0);
-      }
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int sg = 0; sg < 9; ++sg)
+          __builtin_amdgcn_global_load_lds((gbl_void*)(src + (size_t)hb * 32 * kDQK + sg * 64),
+                                           (lds_void*)(sm.kv + hb * kTileElems + group_base(wv) + sg * kSegElems),
+                                           16, 0, 0);
     }
     __syncthreads();
 #pragma unroll
@@ -169,15 +184,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     }
     __syncthreads();
     {
-      const bf16* src = p.dO + ((size_t)t * p.Hq + h0 + hr) * kDV + par * 8;
+      const bf16* src = p.dO + ((size_t)t * p.Hq + h0 + hr) * kDV + sc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = wv + 4 * i;          // 64 loads: pair j % 32 of buffer j / 32
-        const int hb = j >= 32 ? 1 : 0;
-        const int pj = j - 32 * hb;
-        __builtin_amdgcn_global_load_lds((gbl_void*)(src + (size_t)hb * 32 * kDV + pj * 16),
-                                         (lds_void*)(sm.kv + hb * kTileElems + pj * 512), 16, 0, 0);
-      }
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int sg = 0; sg < 8; ++sg)
+          __builtin_amdgcn_global_load_lds((gbl_void*)(src + (size_t)hb * 32 * kDV + sg * 64),
+                                           (lds_void*)(sm.kv + hb * kTileElems + group_base(wv) + sg * kSegElems),
+                                           16, 0, 0);
     }
     __syncthreads();
 #pragma unroll
@@ -210,17 +224,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   // 16 + l16, chunk 4kk + lq) and the transposing reads of the dQ product
   // (rows 4lq + l16/4 and 16 + 4lq + l16/4, columns 4(l16 % 4) of a
   // 16-column block)
+  // chunk 4kk + lq of a row sits at tile_off(row, lq) + (kk / 2) 512 +
+  // (kk % 2) 32; the transposing read of column block m (chunks 2m, 2m+1)
+  // at tile_off(row, 2 (m % 2) + b) + (m / 4) 512 + ((m / 2) % 2) 32
   const int offA0 = tile_off(l16, lq);
   const int offA1 = tile_off(16 + l16, lq);
   const int trq = l16 & 3;
-  const int offT0 = tile_off(lq * 4 + (l16 >> 2), trq >> 1) + (trq & 1) * 4;
-  const int offT1 = tile_off(16 + lq * 4 + (l16 >> 2), trq >> 1) + (trq & 1) * 4;
+  const int tr0 = lq * 4 + (l16 >> 2), tr1 = 16 + tr0;
+  const int offT0e = tile_off(tr0, trq >> 1) + (trq & 1) * 4, offT0o = tile_off(tr0, 2 + (trq >> 1)) + (trq & 1) * 4;
+  const int offT1e = tile_off(tr1, trq >> 1) + (trq & 1) * 4, offT1o = tile_off(tr1, 2 + (trq >> 1)) + (trq & 1) * 4;
+  auto kvt = [&](const bf16* kvb, int m) {   // KV^T fragment of column block m
+    const int o = (m >> 2) * kSegElems + ((m >> 1) & 1) * 32;
+    return join(tr_read(&kvb[((m & 1) ? offT0o : offT0e) + o]), tr_read(&kvb[((m & 1) ? offT1o : offT1e) + o]));
+  };
   // the same key rows of the exchange ([key][head], heads 4(l16 % 4)..+3)
   const int offX0 = (lq * 4 + (l16 >> 2)) * kXS + trq * 4;
   const int offX1 = (16 + lq * 4 + (l16 >> 2)) * kXS + trq * 4;
   bf16* dump = static_cast<bf16*>(w.dump);
-  const int gpar = lane >> 5;
-  const int grow = ((lane & 31) - 8 * gpar) & 31;   // the row this lane gathers in every pair
+  const int grow = wv * 8 + (lane >> 3);            // the row this lane gathers (row group wv)
+  const int gcol = seg_chunk(lane) * 8;
   // phase-B / dQ column block c of this wave (16 columns)
   auto col_block = [&](int c) { return c < 8 ? wv * 128 + c * 16 : 512 + wv * 16; };
 
@@ -294,7 +316,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     bf16* xw = sm.xds[it & 1];
     bf16* pw = sm.xp[it & 1];
     const int kn = k0 + kNT;   // next tile
-    const bf16* gsrc = row_ptr(p, sm.rows[(kn + grow < cnt) ? kn + grow : k0], g) + gpar * 8;
+    const bf16* gsrc = row_ptr(p, sm.rows[(kn + grow < cnt) ? kn + grow : k0], g) + gcol;
+    bf16* gdst = kvn + group_base(wv);
 
     // ---- phase A: S^T and dP^T for the wave's 16 heads, two key halves ---
     // P = exp(scale S - lse), dS = P (dP - D) for keys 16b + 4lq + r, head
@@ -317,7 +340,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
       constexpr int kPF = 2;   // KV fragments in flight ahead of their MFMAs
       bf16x8 f[kPF + 1];
 #pragma unroll
-      for (int kk = 0; kk < kPF; ++kk) f[kk] = *reinterpret_cast<const bf16x8*>(&kvb[off + kk * 1024]);
+      for (int kk = 0; kk < kPF; ++kk)
+        f[kk] = *reinterpret_cast<const bf16x8*>(&kvb[off + (kk >> 1) * kSegElems + (kk & 1) * 32]);
       f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = S;
       // phase B of the previous tile, key half b (for the first tile the
       // products run on stale exchange data and go to the dump row)
@@ -330,12 +354,15 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
           br[cc] = b_chain(hb, cc);
           if (cc >= 2 && (cc & 1) == 0) b_put_pair(hb, cc - 2, br[cc - 2], br[cc - 1]);
         }
-        if (kk + kPF < 18) f[(kk + kPF) % (kPF + 1)] = *reinterpret_cast<const bf16x8*>(&kvb[off + (kk + kPF) * 1024]);
+        if (kk + kPF < 18) {
+          const int k2 = kk + kPF;
+          f[k2 % (kPF + 1)] = *reinterpret_cast<const bf16x8*>(&kvb[off + (k2 >> 1) * kSegElems + (k2 & 1) * 32]);
+        }
         if (b == 0 && (kk & 1) == 0) {
           // next tile's rows: one direct load every other step (for the
           // last tile a harmless reload into the free buffer)
-          const int j = wv + 4 * (kk >> 1);
-          __builtin_amdgcn_global_load_lds((gbl_void*)(gsrc + j * 16), (lds_void*)(kvn + j * 512), 16, 0, 0);
+          const int sg = kk >> 1;
+          __builtin_amdgcn_global_load_lds((gbl_void*)(gsrc + sg * 64), (lds_void*)(gdst + sg * kSegElems), 16, 0, 0);
         }
         const bf16x8 a = f[kk % (kPF + 1)];
         S = mfma16x16x32(a, QA[kk], S);
@@ -364,14 +391,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
       bf16x8 fa[kPF + 1];
 #pragma unroll
       for (int c = 0; c < kPF; ++c) {
-        const int m = col_block(c) >> 4;
-        fa[c] = join(tr_read(&kvb[offT0 + m * 512]), tr_read(&kvb[offT1 + m * 512]));
+        fa[c] = kvt(kvb, col_block(c) >> 4);
       }
 #pragma unroll
       for (int c = 0; c < 9; ++c) {
         if (c + kPF < 9) {
-          const int m = col_block(c + kPF) >> 4;
-          fa[(c + kPF) % (kPF + 1)] = join(tr_read(&kvb[offT0 + m * 512]), tr_read(&kvb[offT1 + m * 512]));
+          fa[(c + kPF) % (kPF + 1)] = kvt(kvb, col_block(c + kPF) >> 4);
         }
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) dQ[c * 4 + hb] = mfma16x16x32(fa[c % (kPF + 1)], bt[hb], dQ[c * 4 + hb]);
