@@ -43,8 +43,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     ("mla_token_8k", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
-        "sha256": "a83bca329a5de0ebee012405569ce6f4841c55620c61fbd93721c8d6475233bf",
-        "fetch_bytes": 8074726270, "write_bytes": 17518854048,
+        "sha256": "bb66d355b3ccdddc2bcd127d0cff64496f07f64a3ae115dc496d89bf906d4c06",
+        "fetch_bytes": 8904087247, "write_bytes": 17519406976,
     },
 }
 
