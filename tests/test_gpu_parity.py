@@ -88,14 +88,15 @@ def test_bwd_edge_shuffled_padding_duplicates_empty_rows(mode):
     assert np.all(got["dq"].reshape(ref["dq"].shape)[40] == 0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mode", list(MODES))
-def test_bwd_block_edge_varlen_ragged_heads_duplicates(mode):
+def test_bwd_block_edge_varlen_ragged_heads_duplicates(mode, d):
     """Block selection, varlen TND with ragged last blocks (lengths 200 and
     75, block 32), 20 query heads over 2 kv heads (a 16-head and a 4-head
-    chunk on the key-major path), shuffled -1 padding, a duplicated block,
-    an out-of-range block, and tokens with no block at all."""
+    chunk on the key-major and block dQ paths), shuffled -1 padding, a
+    duplicated block, an out-of-range block, and tokens with no block."""
     wl = _wl(name="edge_block", select=W.SEL_BLOCK, layout=W.LAYOUT_TND, seqlens=(200, 75), n_q_heads=40,
-             n_kv_heads=2, d_qk=64, d_v=64, topk=4, block_size=32, index_policy="own_block_plus_uniform")
+             n_kv_heads=2, d_qk=d, d_v=d, topk=4, block_size=32, index_policy="own_block_plus_uniform")
     inp = W.make_inputs(wl)
     idx = inp["idx"].numpy().copy()
     rng = np.random.default_rng(5)

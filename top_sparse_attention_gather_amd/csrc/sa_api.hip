@@ -304,7 +304,7 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     w.det = 1;
     w.dq_only = 1;
     if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
-    SA_TRY_HIP(sa::launch_bwd_rows(p, w, s));
+    SA_TRY_HIP(sa::blk_dq_supported(p) ? sa::launch_blk_dq(p, w, s) : sa::launch_bwd_rows(p, w, s));
     if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
     sa::BlkArgs ba;
     std::memset(&ba, 0, sizeof(ba));

@@ -39,6 +39,8 @@ constexpr int kIds = 512;    // query token ids staged in LDS at a time
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
 
 __device__ __forceinline__ i16x4 tr_read4(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
@@ -234,6 +236,163 @@ __global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// dQ of block selection (the query-major half of the same backward): one
+// workgroup per (token, kv head, 16-head chunk).  The row's selected blocks
+// are walked one at a time; each block's K and V rows are brought into LDS
+// with direct global->LDS loads (double-buffered, one block ahead), and
+// wave w takes the block's rows 16w..16w+15:
+//   S^T = K Q^T and dP^T = V dO^T (16x16x32 MFMA; Q / dO of the 16 heads are
+//   the B operands, resident in registers; lane: head l16, keys 4lq + i, so
+//   each lane needs one head's lse and D),
+//   P = exp(scale S - lse), dS = P (dP - D) in registers,
+//   dQ += dS K (16x16x16 MFMA: the result layout of S^T is exactly the A
+//   operand, K comes from transposing LDS reads).
+// The four waves' dQ partial sums are added through LDS at the end.
+// LDS rows of a block are 256 B (128 columns) with the 16-byte chunk c of
+// row r at position c ^ (r % 16): 16 rows of one chunk hit 16 bank quads.
+constexpr int kDqMaxSlots = 256;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void blk_dq_kernel(Params p, BwdBuffers w) {
+  static_assert(D == 128, "row layout assumes 16 chunks of 16 bytes");
+  constexpr int NK = D / 32, NC = D / 16;
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][64 * D];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][64 * D];
+  __shared__ int sBlk[kDqMaxSlots];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int row = w.t0 * p.Hkv + blockIdx.x;     // (token, kv head)
+  const int t = row / p.Hkv, g = row - t * p.Hkv;
+  const int h0 = g * p.G + blockIdx.y * kHeads;
+  const int Gc = min(kHeads, p.G - blockIdx.y * kHeads);
+  const SeqPos sp = seq_pos(p, t);
+  const int* irow = p.idx + (size_t)row * p.topk;
+
+  // the row's usable blocks, in slot order (a block past the sequence or
+  // wholly after the query is unused; duplicates are kept); every thread
+  // votes, so every thread reaches the barriers
+  __shared__ int sW[4];
+  bool ok = false;
+  int blk = -1;
+  if (tid < p.topk) {
+    blk = irow[tid];
+    ok = blk >= 0 && (long long)blk * p.bs < sp.kv_len && (!p.causal || (long long)blk * p.bs <= sp.tl);
+  }
+  const unsigned long long m = __ballot(ok);
+  if (lane == 0) sW[wv] = __popcll(m);
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < wv; ++i) base += sW[i];
+  if (ok) sBlk[base + __popcll(m & ((1ull << lane) - 1ull))] = blk;
+  const int nb = sW[0] + sW[1] + sW[2] + sW[3];
+  __syncthreads();
+
+  // Q / dO of head l16 as B operands (columns 32kk + 8lq .. +8)
+  const bool hv = l16 < Gc;
+  const size_t hrow = (size_t)t * p.Hq + h0 + (hv ? l16 : 0);
+  bf16x8 QB[NK], OB[NK];
+  {
+    const bf16x8 z = {};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(p.q + hrow * D + kk * 32 + lq * 8);
+      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.dO + hrow * D + kk * 32 + lq * 8);
+      QB[kk] = hv ? qv : z;
+      OB[kk] = hv ? ov : z;
+    }
+  }
+  const float lse = hv ? p.lse[hrow] : INFINITY;
+  const float Dh = hv ? w.D[hrow] : 0.f;
+  const float kLog2e = 1.4426950408889634f;
+  const float sl2 = p.scale * kLog2e, lse2 = lse * kLog2e;
+  const bool live = lse > -INFINITY && lse < INFINITY;
+
+  // direct loads of one block: 16 loads of 1 KiB (4 rows) for K and for V;
+  // wave w issues loads 4w..4w+3 of each.  Lane: row 4n + lane / 16,
+  // position lane % 16 <- chunk (lane % 16) ^ (row % 16).
+  auto load_block = [&](int bi, int buf) {
+    const long long j0 = (long long)sBlk[bi] * p.bs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = wv * 4 + i;
+      const int r = n * 4 + (lane >> 4);
+      const long long jr = j0 + min(r, p.bs - 1);
+      const int jl = (int)min(jr, (long long)sp.kv_len - 1);
+      const int ch = (lane & 15) ^ (r & 15);
+      const size_t src = ((size_t)(sp.kv_base + jl) * p.Hkv + g) * D + ch * 8;
+      __builtin_amdgcn_global_load_lds((gbl_void*)(p.k + src), (lds_void*)(&sK[buf][n * 4 * D]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void*)(p.v + src), (lds_void*)(&sV[buf][n * 4 * D]), 16, 0, 0);
+    }
+  };
+
+  f32x4 dQ[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) dQ[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int r0 = wv * 16;                        // the wave's block rows
+  // LDS element offsets: A-operand rows r0 + l16 (chunk 4kk + lq), and the
+  // transposing reads of rows r0 + 4lq + l16/4, columns 16c + 4(l16 % 4)
+  const int ra = r0 + l16;
+  const int rt = r0 + lq * 4 + (l16 >> 2);
+  const int tq = l16 & 3;
+
+  if (nb > 0) load_block(0, 0);
+  for (int bi = 0; bi < nb; ++bi) {
+    const int buf = bi & 1;
+    // this block's loads are done and every wave has left the other buffer
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (bi + 1 < nb) load_block(bi + 1, buf ^ 1);
+    if (r0 < p.bs) {
+      f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = S;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const int off = ra * D + (((kk * 4 + lq) ^ (ra & 15)) * 8);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&sK[buf][off]);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&sV[buf][off]);
+        S = mfma16x16x32(ka, QB[kk], S);
+        dP = mfma16x16x32(va, OB[kk], dP);
+      }
+      // lane: head l16, block rows r0 + 4lq + i
+      const long long jb = (long long)sBlk[bi] * p.bs;
+      i16x4 dSa;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = r0 + lq * 4 + i;
+        const long long jl = jb + rr;
+        const bool v = live && rr < p.bs && jl < sp.kv_len && (!p.causal || jl <= sp.tl);
+        const float pr = v ? __builtin_amdgcn_exp2f(S[i] * sl2 - lse2) : 0.f;
+        dSa[i] = bf16_bits((bf16)(pr * (dP[i] - Dh)));
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int ch = c * 2 + (tq >> 1);
+        const i16x4 kb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(&sK[buf][rt * D + ((ch ^ (rt & 15)) * 8) + (tq & 1) * 4]));
+        dQ[c] = mfma16x16x16(dSa, kb, dQ[c]);
+      }
+    }
+  }
+
+  // sum the waves' partial dQ (rows: heads 4lq + i, columns 16c + l16)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&sK[0][0]);   // 4 x 16 x D fp32 = 32 KiB
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wv * kHeads + lq * 4 + i) * D + c * 16 + l16] = dQ[c][i];
+  __syncthreads();
+  for (int e = tid; e < kHeads * D; e += kThreads) {
+    const int h = e / D, col = e - h * D;
+    if (h < Gc) {
+      const float v = red[h * D + col] + red[(kHeads + h) * D + col] + red[(2 * kHeads + h) * D + col] +
+                      red[(3 * kHeads + h) * D + col];
+      w.dq[((size_t)t * p.Hq + h0 + h) * D + col] = (bf16)(v * p.scale);
+    }
+  }
+}
+
 // dK / dV = sum over the slices in slice order, rounded to bf16.
 __global__ void blk_sum_cast_kernel(const float* __restrict__ part, int n_slices, long long n_rows, int d,
                                     bf16* __restrict__ dk, bf16* __restrict__ dv) {
@@ -272,6 +431,16 @@ hipError_t launch_blk_dkv(const Params& p, const BlkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(blk_dkv_kernel<64>, grid, dim3(kThreads), 0, s, p, a);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+bool blk_dq_supported(const Params& p) {
+  return blk_dkv_supported(p) && p.dqk == 128 && p.topk <= kDqMaxSlots && p.bs % 16 == 0;
+}
+
+hipError_t launch_blk_dq(const Params& p, const BwdBuffers& w, hipStream_t s) {
+  dim3 grid((unsigned)(w.Tc * p.Hkv), (unsigned)((p.G + kHeads - 1) / kHeads));
+  hipLaunchKernelGGL(blk_dq_kernel<128>, grid, dim3(kThreads), 0, s, p, w);
   return hipGetLastError();
 }
 

@@ -144,6 +144,34 @@ __global__ __launch_bounds__(kThreads) void slot_keys_kernel(Params p, long long
   if (key != sentinel) atomicAdd(&counts[key], 1);
 }
 
+// Same keys, with the counts first gathered in an LDS histogram (few keys:
+// one global atomic per used bin and workgroup instead of one per slot).
+// Each workgroup takes a contiguous range of slots.
+constexpr int kHistKeys = 8192;
+
+__global__ __launch_bounds__(kThreads) void slot_keys_hist_kernel(Params p, long long slot0, long long n,
+                                                                  long long per_block, int n_keys,
+                                                                  const int* __restrict__ blk_base, int sentinel,
+                                                                  int* __restrict__ keys, int* __restrict__ counts) {
+  __shared__ int hist[kHistKeys];
+  for (int i = threadIdx.x; i < n_keys; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  const long long i0 = blockIdx.x * per_block;
+  const long long i1 = std::min(n, i0 + per_block);
+  for (long long i = i0 + threadIdx.x; i < i1; i += kThreads) {
+    const long long slot = slot0 + i;
+    const int row = (int)(slot / p.topk);
+    const int t = row / p.Hkv, g = row - t * p.Hkv;
+    const SeqPos s = seq_pos(p, t);
+    const int key = slot_key(p, s, g, p.idx[slot], blk_base, sentinel);
+    keys[i] = key;
+    if (key != sentinel) atomicAdd(&hist[key], 1);
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < n_keys; k += kThreads)
+    if (hist[k]) atomicAdd(&counts[k], hist[k]);
+}
+
 // ---------------------------------------------------------------------------
 // LSD radix sort passes.
 
@@ -266,7 +294,13 @@ hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_key
   const int sentinel = (int)n_keys;
   hipError_t e;
   if ((e = launch_fill_zero(reinterpret_cast<float*>(c.counts), (size_t)(n_keys + 1), s)) != hipSuccess) return e;
-  if (n > 0) {
+  if (n > 0 && n_keys <= kHistKeys) {
+    // about 512 workgroups, each with a contiguous slot range
+    const long long per = std::max<long long>(kThreads, (n + 511) / 512);
+    const unsigned nb = (unsigned)((n + per - 1) / per);
+    hipLaunchKernelGGL(slot_keys_hist_kernel, dim3(nb), dim3(kThreads), 0, s, p, slot0, n, per, (int)n_keys, blk_base,
+                       sentinel, c.keys_a, c.counts);
+  } else if (n > 0) {
     hipLaunchKernelGGL(slot_keys_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, p,
                        slot0, n, blk_base, sentinel, c.keys_a, c.counts);
   }

@@ -90,6 +90,10 @@ int blk_dkv_splits(long long n_keys, int n_hc);
 hipError_t launch_blk_dkv(const Params& p, const BlkArgs& a, hipStream_t s);
 hipError_t launch_blk_sum_cast(const float* part, int n_slices, long long n_rows, int d, bf16* dk, bf16* dv,
                                hipStream_t s);
+// dQ of block selection, query-major (d = 128, up to 256 slots, block_size a
+// multiple of 16 and at most 64)
+bool blk_dq_supported(const Params& p);
+hipError_t launch_blk_dq(const Params& p, const BwdBuffers& w, hipStream_t s);
 
 // Shared-KV 576/512 backward with 64 heads per workgroup (bf16 partials).
 bool mla_bwd_supported(const Params& p);
