@@ -183,10 +183,12 @@ sa_status_t sparse_attn_bwd(const sa_desc_t* desc, const sa_bwd_args_t* args,
 
 /* Same as sparse_attn_bwd, and additionally records the caller's events
  * (hipEvent_t passed as void*, either may be NULL) on `stream` immediately
- * before and after the main row kernel -- the kernel that gathers the
- * selected rows and runs the five MFMA products -- so a caller can time that
- * kernel alone with hipEventElapsedTime.  Same errors as sparse_attn_bwd;
- * a failed event record is SA_ERR_HIP. */
+ * before and after the dominant kernel, so a caller can time that kernel
+ * alone with hipEventElapsedTime: the row kernel that gathers the selected
+ * rows and runs the MFMA products (all launches of it when tokens are
+ * processed in chunks), or, for block selection in deterministic mode, the
+ * dQ pass over the selected blocks.  Same errors as sparse_attn_bwd; a failed event
+ * record is SA_ERR_HIP. */
 sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* args, void* workspace,
                                   size_t workspace_bytes, void* stream, void* ev_main_start,
                                   void* ev_main_stop);

@@ -96,8 +96,9 @@ Params make_params(const sa_desc_t* d);
 struct BwdLayout {
   size_t D, sink_term, acc_k, acc_v, acc_cmp;                   // atomic mode
   size_t blk_base, row_ptr, entries, csr_ws, partial, dump, acc;   // deterministic mode
-  size_t bpart;                                                 // block key-major slices
-  int Tc, n_hc, RW, fast, blk_km, n_split, n_hc_blk;
+  size_t bpart, bchunk, bcnt, bscan;                            // block key-major chunks
+  long long max_chunks;
+  int Tc, n_hc, RW, fast, blk_km, n_hc_blk;
   size_t total;
 };
 
@@ -135,7 +136,7 @@ BwdLayout bwd_layout(const sa_desc_t* d, const Params& p) {
   const long long nk = csr_keys_bound(d);
   if (L.blk_km) {
     L.n_hc_blk = sa::blk_dkv_head_chunks(p);
-    L.n_split = sa::blk_dkv_splits(nk, L.n_hc_blk);
+    L.max_chunks = sa::blk_max_chunks(nk, (long long)T * Hkv * d->topk);
   }
   L.blk_base = off;
   off += align_up((size_t)(d->batch + 1) * 4);
@@ -152,8 +153,15 @@ BwdLayout bwd_layout(const sa_desc_t* d, const Params& p) {
   L.acc = off;
   if (!L.blk_km) off += align_up((size_t)(rows_kv(d) + rows_cmp(d)) * Hkv * L.RW * sizeof(float));
   L.bpart = off;
-  if (L.blk_km)
-    off += align_up((size_t)L.n_hc_blk * L.n_split * rows_kv(d) * Hkv * (size_t)(2 * d->d_qk) * sizeof(float));
+  if (L.blk_km) {
+    off += align_up((size_t)L.n_hc_blk * L.max_chunks * 64 * (size_t)(2 * d->d_qk) * sizeof(float));
+    L.bchunk = off;
+    off += align_up((size_t)(nk + 1) * 4);
+    L.bcnt = off;
+    off += align_up((size_t)(nk + 1) * 4);
+    L.bscan = off;
+    off += align_up((size_t)sa::scan_bsum_ints(nk + 1) * 4);
+  }
   L.total = off;
   return L;
 }
@@ -303,6 +311,7 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     if (has_slots) SA_TRY_HIP(sa::launch_csr_transpose(p, 0, p.T, nk, blk_base, row_ptr, entries, ws + L.csr_ws, s));
     w.det = 1;
     w.dq_only = 1;
+    // the timed "main" kernel of this path: the dQ pass (the larger one)
     if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
     SA_TRY_HIP(sa::blk_dq_supported(p) ? sa::launch_blk_dq(p, w, s) : sa::launch_bwd_rows(p, w, s));
     if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
@@ -313,18 +322,18 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     ba.blk_base = blk_base;
     ba.D = w.D;
     ba.part = reinterpret_cast<float*>(ws + L.bpart);
-    ba.rows_kv = rows_kv(desc);
-    ba.n_split = L.n_split;
+    ba.chunk_base = reinterpret_cast<int*>(ws + L.bchunk);
+    ba.max_chunks = L.max_chunks;
     ba.n_hc = L.n_hc_blk;
-    ba.n_keys = has_slots ? nk : 0;
+    ba.n_keys = nk;
     const long long nrows = rows_kv(desc) * (long long)Hkv;
-    if (ba.n_keys) {
+    if (!has_slots) SA_TRY_HIP(sa::launch_fill_zero(reinterpret_cast<float*>(row_ptr), (size_t)(nk + 1), s));
+    SA_TRY_HIP(sa::launch_blk_chunks(row_ptr, nk, reinterpret_cast<int*>(ws + L.bcnt), ba.chunk_base,
+                                     reinterpret_cast<int*>(ws + L.bscan), s));
+    if (has_slots) {
       SA_TRY_HIP(sa::launch_blk_dkv(p, ba, s));
-    } else {
-      SA_TRY_HIP(sa::launch_fill_zero(ba.part, (size_t)nrows * 2 * desc->d_qk * L.n_split * L.n_hc_blk, s));
     }
-    SA_TRY_HIP(sa::launch_blk_sum_cast(ba.part, L.n_split * L.n_hc_blk, nrows, desc->d_qk,
-                                       static_cast<bf16*>(a->dk), static_cast<bf16*>(a->dv), s));
+    SA_TRY_HIP(sa::launch_blk_sum_cast(p, ba, nrows, static_cast<bf16*>(a->dk), static_cast<bf16*>(a->dv), s));
     return SA_OK;
   }
   w.det = 1;

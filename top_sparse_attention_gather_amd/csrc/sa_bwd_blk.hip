@@ -34,7 +34,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kHeads = 16;   // query heads per workgroup
-constexpr int kPD = 4;       // queries fetched ahead (the query loop below is unrolled by 4)
+constexpr int kPD = 8;       // queries fetched ahead (the query loop below is unrolled by kPD)
 constexpr int kIds = 512;    // query token ids staged in LDS at a time
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -46,9 +46,30 @@ __device__ __forceinline__ i16x4 tr_read4(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+// f(integral_constant<int, U>) for U = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>());
+    unroll<B + 1, E>(f);
+  }
+}
+
+// LDS rows of the staged Q / dO (one per head): D columns, 16-byte chunk c
+// of row r at slot (c + rot(r)) mod D/8, rot(r) = 2 (r % 8) + (r / 8) % 2.
+// The 16 rows of a fragment read (one chunk) then take 16 distinct slots,
+// and each 32-lane pass of the transposing reads (8 rows x 32 bytes) covers
+// 8 disjoint 32-byte bank ranges.
+template <int D>
+__device__ __forceinline__ int qrow_off(int r, int col) {
+  constexpr int CPR = D / 8;
+  const int rot = 2 * (r & 7) + ((r >> 3) & 1);
+  return r * D + (((col >> 3) + rot) & (CPR - 1)) * 8 + (col & 7);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) {
-  constexpr int QS = D + 8;        // LDS row stride: 16-byte rows land 4 banks apart
+  constexpr int QS = D;            // LDS row stride (rows rotated, see qrow_off)
   constexpr int NK = D / 32;       // 16x16x32 steps over d
   constexpr int NC = D / 16;       // 16-column blocks of dK / dV
   constexpr int CPR = D / 8;       // 16-byte chunks per head row
@@ -59,10 +80,21 @@ __global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) 
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
-  const long long bkey = blockIdx.x;
-  const int hc = blockIdx.y / a.n_split, split = blockIdx.y - hc * a.n_split;
+  // chunk w of the list of block key `bkey` (chunk_base is ascending)
+  const long long wch = blockIdx.x;
+  const int hc = blockIdx.y;
+  if (wch >= a.chunk_base[a.n_keys]) return;         // past the last chunk (uniform)
+  long long bkey = 0;
+  {
+    long long lo = 0, hi = a.n_keys;                 // largest key with chunk_base[key] <= wch
+    while (hi - lo > 1) {
+      const long long mid = (lo + hi) >> 1;
+      if (a.chunk_base[mid] <= wch) lo = mid; else hi = mid;
+    }
+    bkey = lo;
+  }
+  const int cidx = (int)(wch - a.chunk_base[bkey]);
   const int bn = (int)(bkey / p.Hkv), g = (int)(bkey - (long long)bn * p.Hkv);
-  if (bn >= a.blk_base[p.B]) return;                 // past the last block (uniform)
   int b = 0;
   {
     int lo = 0, hi = p.B;                            // largest b with blk_base[b] <= bn
@@ -78,9 +110,8 @@ __global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) 
   const int q_base = p.layout == kLayoutBSND ? b * p.Sq : p.cu_q[b];
   const int h0 = g * p.G + hc * kHeads;
   const int Gc = min(kHeads, p.G - hc * kHeads);
-  const int eb0 = a.row_ptr[bkey], n_all = a.row_ptr[bkey + 1] - eb0;
-  const int eb = eb0 + (int)((long long)n_all * split / a.n_split);
-  const int ee = eb0 + (int)((long long)n_all * (split + 1) / a.n_split);
+  const int eb = a.row_ptr[bkey] + cidx * kBlkChunk;
+  const int ee = min(a.row_ptr[bkey + 1], eb + kBlkChunk);
 
   // the wave's 16 block rows; this lane's row (B operand n index)
   const int r0 = wv * 16;
@@ -136,8 +167,8 @@ __global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) 
         // rows past the head chunk are zero (the select is made here, not at
         // the load, so that the load's latency is not waited for early)
         const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(&sQ[buf][h * QS + col]) = h < Gc ? qn[u][i] : z;
-        *reinterpret_cast<u32x4*>(&sdO[buf][h * QS + col]) = h < Gc ? dn[u][i] : z;
+        *reinterpret_cast<u32x4*>(&sQ[buf][qrow_off<D>(h, col)]) = h < Gc ? qn[u][i] : z;
+        *reinterpret_cast<u32x4*>(&sdO[buf][qrow_off<D>(h, col)]) = h < Gc ? dn[u][i] : z;
       }
     }
     if (tid < kHeads) {
@@ -158,10 +189,7 @@ __global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) 
     // the part is walked in groups of kPD queries; positions past the end
     // reload the last query and contribute nothing, so the sequence of
     // loads has no branches and the compiler can count them in flight
-    fetch(0, 0);
-    fetch(min(1, n - 1), 1);
-    fetch(min(2, n - 1), 2);
-    fetch(min(3, n - 1), 3);
+    unroll<0, kPD>([&](auto U) { fetch(min(decltype(U)::value, n - 1), decltype(U)::value); });
     put(0, 0);
     __syncthreads();
     // one query of the list; U: its ring slot (compile time, so the ring
@@ -177,8 +205,9 @@ __global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) 
         f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = S;
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sQ[buf][l16 * QS + kk * 32 + lq * 8]);
-          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&sdO[buf][l16 * QS + kk * 32 + lq * 8]);
+          const int ao = qrow_off<D>(l16, kk * 32 + lq * 8);
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sQ[buf][ao]);
+          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&sdO[buf][ao]);
           S = mfma16x16x32(aq, Kf[kk], S);
           dP = mfma16x16x32(ad, Vf[kk], dP);
         }
@@ -197,8 +226,9 @@ __global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) 
         // dV[key][d] += P^T dO, dK[key][d] += dS^T Q (head sum inside the MFMA)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const i16x4 bo = tr_read4(&sdO[buf][trow * QS + c * 16 + tcol]);
-          const i16x4 bq = tr_read4(&sQ[buf][trow * QS + c * 16 + tcol]);
+          const int to = qrow_off<D>(trow, c * 16 + tcol);
+          const i16x4 bo = tr_read4(&sdO[buf][to]);
+          const i16x4 bq = tr_read4(&sQ[buf][to]);
           dV[c] = mfma16x16x16(Pa, bo, dV[c]);
           dK[c] = mfma16x16x16(dSa, bq, dK[c]);
         }
@@ -208,24 +238,20 @@ __global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) 
       __syncthreads();
     };
     for (int i0 = 0; i0 < n; i0 += kPD) {
-      query(i0, std::integral_constant<int, 0>());
-      query(i0 + 1, std::integral_constant<int, 1>());
-      query(i0 + 2, std::integral_constant<int, 2>());
-      query(i0 + 3, std::integral_constant<int, 3>());
+      unroll<0, kPD>([&](auto U) { query(i0 + decltype(U)::value, U); });
     }
   }
 
-  // this slice's dK|dV rows of the block: lane holds rows r0 + 4lq + i,
-  // columns 16c + l16
+  // this chunk's dK|dV rows of the block (slot [hc][wch], 64 rows): lane
+  // holds rows r0 + 4lq + i, columns 16c + l16
   if (r0 < p.bs) {
-    const size_t slice = (size_t)hc * a.n_split + split;
-    const long long rows_total = a.rows_kv;
+    float* slot = a.part + ((size_t)hc * a.max_chunks + wch) * 64 * (2 * D);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = r0 + lq * 4 + i;
       const int jr = jb * p.bs + rr;
       if (rr < p.bs && jr < kv_len) {
-        float* dst = a.part + ((slice * rows_total + kv_base + jr) * p.Hkv + g) * (2 * D);
+        float* dst = slot + rr * (2 * D);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           dst[c * 16 + l16] = dK[c][i] * p.scale;
@@ -393,18 +419,44 @@ __global__ __launch_bounds__(kThreads) void blk_dq_kernel(Params p, BwdBuffers w
   }
 }
 
-// dK / dV = sum over the slices in slice order, rounded to bf16.
-__global__ void blk_sum_cast_kernel(const float* __restrict__ part, int n_slices, long long n_rows, int d,
-                                    bf16* __restrict__ dk, bf16* __restrict__ dv) {
+// Chunks of every block key's list: cnt[k] = ceil(len_k / kBlkChunk).
+__global__ void blk_chunk_count_kernel(const int* __restrict__ row_ptr, long long n_keys, int* __restrict__ cnt) {
+  const long long k = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  if (k < n_keys) cnt[k] = (row_ptr[k + 1] - row_ptr[k] + kBlkChunk - 1) / kBlkChunk;
+}
+
+// dK / dV of every kv row = sum over its block key's chunks (head chunk
+// outer, chunk order inner), rounded to bf16; rows whose block no query
+// selected get 0.
+__global__ void blk_sum_cast_kernel(Params p, BlkArgs a, long long n_rows, bf16* __restrict__ dk,
+                                    bf16* __restrict__ dv) {
+  const int d = p.dqk;
   const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
-  const long long per = n_rows * 2 * d;
-  if (i >= per) return;
+  if (i >= n_rows * 2 * d) return;
+  const long long rg = i / (2 * d);                  // (kv row, kv head)
+  const int c = (int)(i - rg * 2 * d);
+  const long long j = rg / p.Hkv;
+  const int g = (int)(rg - j * p.Hkv);
+  int b = 0;
+  if (p.layout == kLayoutBSND) {
+    b = (int)(j / p.Skv);
+  } else {
+    int lo = 0, hi = p.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.cu_kv[mid] <= j) lo = mid; else hi = mid;
+    }
+    b = lo;
+  }
+  const int jl = (int)(j - (p.layout == kLayoutBSND ? (long long)b * p.Skv : p.cu_kv[b]));
+  const long long bkey = (long long)(a.blk_base[b] + jl / p.bs) * p.Hkv + g;
+  const int rr = jl % p.bs;
+  const long long w0 = a.chunk_base[bkey], w1 = a.chunk_base[bkey + 1];
   float acc = 0.f;
-  for (int s = 0; s < n_slices; ++s) acc += part[(size_t)s * per + i];
-  const long long row = i / (2 * d);
-  const int c = (int)(i - row * 2 * d);
-  if (c < d) dk[row * d + c] = (bf16)acc;
-  else dv[row * d + (c - d)] = (bf16)acc;
+  for (int hc = 0; hc < a.n_hc; ++hc)
+    for (long long w = w0; w < w1; ++w) acc += a.part[(((size_t)hc * a.max_chunks + w) * 64 + rr) * (2 * d) + c];
+  if (c < d) dk[rg * d + c] = (bf16)acc;
+  else dv[rg * d + (c - d)] = (bf16)acc;
 }
 
 }  // namespace
@@ -416,15 +468,21 @@ bool blk_dkv_supported(const Params& p) {
 
 int blk_dkv_head_chunks(const Params& p) { return (p.G + kHeads - 1) / kHeads; }
 
-int blk_dkv_splits(long long n_keys, int n_hc) {
-  // about 1024 workgroups in all, at most 16 slices per key
-  const long long per = std::max<long long>(1, n_keys * n_hc);
-  return (int)std::min<long long>(16, std::max<long long>(1, (1024 + per - 1) / per));
+long long blk_max_chunks(long long n_keys, long long n_slots) {
+  return n_keys + (n_slots + kBlkChunk - 1) / kBlkChunk;
+}
+
+hipError_t launch_blk_chunks(const int* row_ptr, long long n_keys, int* cnt, int* chunk_base, int* scan_ws,
+                             hipStream_t s) {
+  if (n_keys > 0)
+    hipLaunchKernelGGL(blk_chunk_count_kernel, dim3((unsigned)((n_keys + 255) / 256)), dim3(256), 0, s, row_ptr,
+                       n_keys, cnt);
+  return launch_scan_excl(cnt, n_keys, chunk_base, n_keys + 1, scan_ws, s);
 }
 
 hipError_t launch_blk_dkv(const Params& p, const BlkArgs& a, hipStream_t s) {
-  if (a.n_keys == 0) return hipSuccess;
-  dim3 grid((unsigned)a.n_keys, (unsigned)(a.n_hc * a.n_split));
+  if (a.n_keys == 0 || a.max_chunks == 0) return hipSuccess;
+  dim3 grid((unsigned)a.max_chunks, (unsigned)a.n_hc);
   if (p.dqk == 128)
     hipLaunchKernelGGL(blk_dkv_kernel<128>, grid, dim3(kThreads), 0, s, p, a);
   else if (p.dqk == 64)
@@ -444,12 +502,11 @@ hipError_t launch_blk_dq(const Params& p, const BwdBuffers& w, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_blk_sum_cast(const float* part, int n_slices, long long n_rows, int d, bf16* dk, bf16* dv,
+hipError_t launch_blk_sum_cast(const Params& p, const BlkArgs& a, long long n_rows, bf16* dk, bf16* dv,
                                hipStream_t s) {
-  const long long n = n_rows * 2 * d;
+  const long long n = n_rows * 2 * p.dqk;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(blk_sum_cast_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, n_slices, n_rows,
-                     d, dk, dv);
+  hipLaunchKernelGGL(blk_sum_cast_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, a, n_rows, dk, dv);
   return hipGetLastError();
 }
 

@@ -266,6 +266,12 @@ hipError_t scan_excl(const int* in, long long n, int* out, long long n_out, int*
 
 }  // namespace
 
+hipError_t launch_scan_excl(const int* in, long long n, int* out, long long n_out, int* bsum, hipStream_t s) {
+  return scan_excl(in, n, out, n_out, bsum, s);
+}
+
+long long scan_bsum_ints(long long n) { return (n + kScanChunk - 1) / kScanChunk; }
+
 size_t csr_workspace_bytes(long long n, long long n_keys, int batch) {
   const long long nb_tiles = (n + kTile - 1) / kTile;
   const long long hist_n = 256 * nb_tiles;

@@ -69,27 +69,37 @@ hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk
 }  // namespace sa
 
 namespace sa {
-// Key-major dK/dV of block selection (separate K/V, d_qk = d_v): one
-// workgroup per (block key, head chunk, slice of the key's CSR list), each
-// writing fp32 dK|dV rows of its block into its own slice of `part`
-// ([n_slices][kv rows][Hkv][2 d]); the slices are then summed in order.
+// Key-major dK/dV of block selection (separate K/V, d_qk = d_v): every
+// block key's CSR list is cut into chunks of kBlkChunk queries; one
+// workgroup per (chunk, 16-head chunk) writes the fp32 dK|dV rows of its
+// block into its own slot of `part` ([n_hc][max_chunks][64][2 d]); the
+// chunks of a key are then summed in chunk order.
+constexpr int kBlkChunk = 64;
 struct BlkArgs {
   const int* row_ptr;
   const int* entries;
   const int* blk_base;
-  const float* D;   // [T][Hq] softmax-grad term
+  const float* D;        // [T][Hq] softmax-grad term
+  int* chunk_base;       // [n_keys + 1]: first chunk of every key (exclusive scan)
   float* part;
-  long long rows_kv;  // kv rows of all sequences
-  int n_split;      // slices of every key's list
-  int n_hc;         // head chunks of 16
-  long long n_keys; // CSR keys (bound)
+  long long max_chunks;  // bound on the number of chunks (grid size)
+  long long n_keys;      // CSR keys (bound)
+  int n_hc;              // head chunks of 16
 };
 bool blk_dkv_supported(const Params& p);
 int blk_dkv_head_chunks(const Params& p);
-int blk_dkv_splits(long long n_keys, int n_hc);
+long long blk_max_chunks(long long n_keys, long long n_slots);
+// chunk_base from row_ptr (uses `cnt` [n_keys + 1] and `scan_ws` scratch)
+hipError_t launch_blk_chunks(const int* row_ptr, long long n_keys, int* cnt, int* chunk_base, int* scan_ws,
+                             hipStream_t s);
 hipError_t launch_blk_dkv(const Params& p, const BlkArgs& a, hipStream_t s);
-hipError_t launch_blk_sum_cast(const float* part, int n_slices, long long n_rows, int d, bf16* dk, bf16* dv,
+// n_rows: kv rows * Hkv
+hipError_t launch_blk_sum_cast(const Params& p, const BlkArgs& a, long long n_rows, bf16* dk, bf16* dv,
                                hipStream_t s);
+// exclusive scan of in[0..n) into out[0..n_out) (out past n: the total);
+// `bsum` holds scan_bsum_ints(max(n, n_out)) ints
+hipError_t launch_scan_excl(const int* in, long long n, int* out, long long n_out, int* bsum, hipStream_t s);
+long long scan_bsum_ints(long long n);
 // dQ of block selection, query-major (d = 128, up to 256 slots, block_size a
 // multiple of 16 and at most 64)
 bool blk_dq_supported(const Params& p);
