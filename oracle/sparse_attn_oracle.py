@@ -26,6 +26,10 @@ What it computes, and where the pages define it:
       dK[u] += scale * dS^T Q,   dV[u] += P^T dO  (scatter into gathered rows)
       MLA (shared KV): dKV = scale * dS^T Q + P^T dO  (P^T dO in the first d_v cols)
       dSinks[h] = sum over rows of -P_sink * D,  P_sink = exp(sink_h - lse)
+* Softmax L1-norm side outputs (SparseFlashMlaGrad README, parameter
+  table; aclnnSparseLightningIndexerGradKLLoss, "Formula": the target
+  distribution p): P summed over the group's heads, L1-normalised over the
+  ori entries and, separately, over the cmp entries.
 * CSR transpose of the index lists (no passage on the pages: it is the
   bookkeeping for a deterministic key-major reduction): for every key, the
   flat ids p = (t * Hkv + g) * K + slot of the valid entries naming it, in
@@ -52,7 +56,11 @@ design notes):
       gradient contribution;
   R11 cu_seqlens are cumulative ([B+1], cu[0] = 0);
   R12 index values and window positions are sequence-local;
-  R15 GQA: query head h uses kv head h // G; indices are per (token, kv head).
+  R15 GQA: query head h uses kv head h // G; indices are per (token, kv head);
+  R16 the softmax L1-norm outputs sum the backward's P (given lse, sinks in
+      the denominator) over the G heads of a kv head and normalise the ori
+      and the cmp entries separately; they are laid out by virtual position
+      (slot, block row, window offset) with 0 where nothing is selected.
 """
 from __future__ import annotations
 
@@ -115,6 +123,14 @@ class Problem:
         """Ordered multiset of (source, global row) selected by token t for kv
         head g.  source 0 = the primary K/V (ori) rows, 1 = cmp_kv rows.
         Slot order is kept; unused and masked slots are dropped."""
+        srcs, rows, _ = self.selection_positions(t, g)
+        return srcs, rows
+
+    def selection_positions(self, t: int, g: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """selection(t, g) plus the virtual position of every entry: the
+        index slot (token), slot * block_size + row in block (block), or the
+        window offset followed by window length + slot (window+cmp).  These
+        are the columns of the softmax L1-norm outputs."""
         b = int(self.seq_of[t])
         tl = t - int(self.cu[b])                  # position within the sequence
         n_kv = int(self.cu[b + 1] - self.cu[b])   # Sq = Skv per sequence here
@@ -125,17 +141,19 @@ class Problem:
             if self.causal:
                 keep &= j <= tl
             rows = base + j[keep]
-            return np.zeros(rows.size, dtype=np.int64), rows
+            return np.zeros(rows.size, dtype=np.int64), rows, np.flatnonzero(keep)
         if self.select == SEL_BLOCK:
             bs = self.block_size
             blk = self.idx[t, g].astype(np.int64)
+            slots = np.flatnonzero(blk >= 0)
             blk = blk[blk >= 0]
             j = (blk[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)   # block-major
             keep = j < n_kv
             if self.causal:
                 keep &= j <= tl
             rows = base + j[keep]
-            return np.zeros(rows.size, dtype=np.int64), rows
+            pos = (slots[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)[keep]
+            return np.zeros(rows.size, dtype=np.int64), rows, pos
         # window over the ori rows, then the gathered cmp rows
         w = np.arange(tl - self.win_left, tl + self.win_right + 1, dtype=np.int64)
         keep = (w >= 0) & (w < n_kv)
@@ -150,7 +168,8 @@ class Problem:
             keepc &= r * j + r - 1 <= tl
         cmp = int(self.cu_cmp[b]) + j[keepc]
         srcs = np.concatenate([np.zeros(ori.size, np.int64), np.ones(cmp.size, np.int64)])
-        return srcs, np.concatenate([ori, cmp])
+        pos = np.concatenate([np.flatnonzero(keep), w.size + np.flatnonzero(keepc)])
+        return srcs, np.concatenate([ori, cmp]), pos
 
     def gather(self, srcs: np.ndarray, rows: np.ndarray, g: int) -> Tuple[np.ndarray, np.ndarray]:
         """fp64 K_sel [n, d_qk] and V_sel [n, d_v] for a selection."""
@@ -280,6 +299,66 @@ def sparse_bwd(pb: Problem, O: torch.Tensor, lse: torch.Tensor,
     if dsinks is not None:
         out["dsinks"] = dsinks
     return out
+
+
+def softmax_l1_norm(pb: Problem, lse: torch.Tensor,
+                    tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Softmax L1-norm side outputs in fp64.
+
+    SparseFlashMlaGrad README, parameter table: two fp32 outputs holding the
+    softmax of the query against the ori KV and against the cmp KV;
+    aclnnSparseLightningIndexerGradKLLoss, "Formula": the indexer's target
+    distribution is the main attention's probabilities summed over the heads
+    and then L1-normalised along the context.  For every (t, g):
+
+        P_h   = exp(scale * q_h K_sel^T - lse_h)   for the G heads of group g
+        p     = sum over h of P_h                  (one value per selected entry)
+        ori_j = p_j / sum of p over the ori entries   (source 0)
+        cmp_j = p_j / sum of p over the cmp entries   (source 1, window+cmp)
+
+    Readings: P is the backward's P (the given lse, sinks included, so a
+    head's mass may be below one); each set is normalised on its own; the
+    outputs are laid out by virtual position (selection_positions) --
+    ori [T, Hkv, n_ori] with n_ori = topk (token), topk * block_size (block)
+    or the window length (window+cmp), and cmp [T, Hkv, topk] -- and a
+    position that selects nothing, or a set whose mass is zero, holds 0.
+    A duplicated slot has its own position and its own value.
+    """
+    toks = range(pb.T) if tokens is None else tokens
+    nwin = pb.win_left + 1 + pb.win_right
+    if pb.select == SEL_TOKEN:
+        n_ori = pb.K
+    elif pb.select == SEL_BLOCK:
+        n_ori = pb.K * pb.block_size
+    else:
+        n_ori = nwin
+    ori = np.zeros((pb.T, pb.Hkv, n_ori))
+    cmp = np.zeros((pb.T, pb.Hkv, pb.K)) if pb.select == SEL_WINDOW_CMP else None
+    for t in toks:
+        q_t = _f64(pb.q[t])
+        l_t = lse[t].to(torch.float64).numpy() if isinstance(lse, torch.Tensor) else np.asarray(lse[t], np.float64)
+        for g in range(pb.Hkv):
+            hs = slice(g * pb.G, (g + 1) * pb.G)
+            srcs, rows, pos = pb.selection_positions(t, g)
+            if rows.size == 0:
+                continue
+            Lg = l_t[hs]
+            finite = np.isfinite(Lg)
+            K, _ = pb.gather(srcs, rows, g)
+            S = pb.scale * (q_t[hs] @ K.T)
+            P = np.where(finite[:, None], np.exp(S - np.where(finite, Lg, 0.0)[:, None]), 0.0)
+            p = P.sum(axis=0)                                     # heads summed
+            for src, out, off in ((0, ori, 0), (1, cmp, nwin)):
+                m = srcs == src
+                if out is None or not m.any():
+                    continue
+                tot = p[m].sum()
+                if tot > 0:
+                    out[t, g, pos[m] - off] = p[m] / tot
+    res = {"ori": ori}
+    if cmp is not None:
+        res["cmp"] = cmp
+    return res
 
 
 # ----------------------------------------------------------------------------

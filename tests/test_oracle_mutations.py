@@ -27,6 +27,14 @@ MUTATIONS = {
                     "z = np.exp(S - m[:, None]).sum(axis=1)"),
     "csr_unstable": ('order = np.argsort(keys[valid], kind="stable")',
                      'order = np.argsort(-valid)[np.argsort(keys[valid][np.argsort(-valid)], kind="stable")]'),
+    # softmax L1-norm side outputs
+    "l1_one_head": ("p = P.sum(axis=0)", "p = P[0]"),
+    "l1_joint_norm": ("tot = p[m].sum()", "tot = p.sum()"),
+    "l1_compacted_pos": ("out[t, g, pos[m] - off] = p[m] / tot", "out[t, g, np.arange(m.sum())] = p[m] / tot"),
+    "l1_no_lse": ("P = np.where(finite[:, None], np.exp(S - np.where(finite, Lg, 0.0)[:, None]), 0.0)",
+                  "P = np.exp(S)"),
+    "l1_block_pos_compacted": ("pos = (slots[:, None] * bs + np.arange(bs)[None, :])",
+                               "pos = (np.arange(slots.size)[:, None] * bs + np.arange(bs)[None, :])"),
 }
 
 
@@ -95,7 +103,20 @@ def _selection_ok(mod, mode):
 def test_pins_catch_planted_mistake(name):
     mod = _mutant(name)
     caught = []
-    if name == "csr_unstable":
+    if name.startswith("l1_"):
+        from tests import test_oracle_l1_pins as L1
+        pins = [lambda m=m, sh=sh: L1.pin_full_coverage(mod, m, sh) for m in ("token_gqa", "block_gqa", "mla")
+                for sh in (False, True)]
+        pins += [lambda m=m: L1.pin_identical_heads(mod, m)
+                 for m in ("token_gqa", "block_gqa", "mla", "wcmp_sinks", "token_sinks")]
+        pins.append(lambda: L1.pin_empty_and_duplicate(mod))
+        for pin in pins:
+            try:
+                pin()
+                caught.append(False)
+            except AssertionError:
+                caught.append(True)
+    elif name == "csr_unstable":
         caught.append(not _csr_ok(mod, "token_gqa"))
     elif name in ("causal_off_by_one", "window_short"):
         caught.append(not _selection_ok(mod, "token_gqa" if name == "causal_off_by_one" else "wcmp_sinks"))
