@@ -120,6 +120,8 @@ typedef struct sa_desc {
   int32_t has_sinks;    /* 1: per-head sink logits in the softmax denominator */
   int32_t dkv_mode;     /* SA_DKV_ATOMIC or SA_DKV_DETERMINISTIC */
   float scale;          /* softmax scale (finite, > 0) */
+  int32_t softmax_l1;   /* 1: the backward also writes the softmax L1-norm
+                           side outputs (sa_bwd_args_t); 0: it does not */
 } sa_desc_t;
 
 /* Device pointers for the backward.  Unused fields may be NULL.
@@ -146,6 +148,25 @@ typedef struct sa_bwd_args {
   void* dkv;
   void* d_cmp_kv;
   float* dsinks;
+  /* Softmax L1-norm side outputs (desc->softmax_l1 = 1), fp32, written in
+   * full (SparseFlashMlaGrad README, parameter table: the softmax of the
+   * query against the ori KV and against the cmp KV; the target
+   * distribution of aclnnSparseLightningIndexerGradKLLoss, "Formula": the
+   * main attention's probabilities summed over heads, then L1-normalised
+   * along the context).  For every (t, g), with P the backward's P (given
+   * lse, sinks in the denominator):
+   *   p[pos] = sum over the G query heads of kv head g of P[h][pos]
+   *   ori[t][g][pos] = p[pos] / (sum of p over the ori positions)
+   *   cmp[t][g][j]   = p[win + j] / (sum of p over the cmp positions)
+   * Columns are the virtual positions of the selection: ori is
+   * [T, n_kv_heads, n_ori] with n_ori = topk (SA_SEL_TOKEN), topk *
+   * block_size (SA_SEL_BLOCK, slot-major) or win = win_left + 1 +
+   * win_right (SA_SEL_WINDOW_CMP, key t - win_left + pos); cmp is
+   * [T, n_kv_heads, topk] (SA_SEL_WINDOW_CMP only, NULL otherwise).  A
+   * position that selects no key (unused slot, masked, past the sequence)
+   * and every position of a set whose sum is 0 holds 0.  Deterministic. */
+  float* ori_softmax_l1;
+  float* cmp_softmax_l1;
 } sa_bwd_args_t;
 
 /* Device pointers for the forward (o, lse out; the rest as above). */
@@ -166,7 +187,8 @@ typedef struct sa_fwd_args {
 
 /* Phase 1 of the backward: validates `desc` (host only, no HIP call) and
  * returns in *bytes the device workspace that sparse_attn_bwd needs for
- * it (fp32 accumulators, the softmax-grad term D, CSR buffers).
+ * it (fp32 accumulators, the softmax-grad term D, CSR buffers, and with
+ * softmax_l1 the per-head-group sums behind the L1-norm outputs).
  * Errors: SA_ERR_NULL_PTR, SA_ERR_BAD_SHAPE, SA_ERR_BAD_ARG,
  * SA_ERR_UNSUPPORTED (e.g. a head dim the kernels are not built for). */
 sa_status_t sparse_attn_bwd_workspace_size(const sa_desc_t* desc, size_t* bytes);

@@ -78,6 +78,7 @@ def test_phase1_validation_codes():
         "unbuilt head dim": (dict(d_qk=96, d_v=96), 3),
         "no batch": (dict(batch=0), 2),
         "topk 0": (dict(topk=0), 2),
+        "bad softmax_l1 flag": (dict(softmax_l1=2), 7),
     }
     for name, (over, code) in cases.items():
         if name == "heads not divisible":
@@ -88,6 +89,18 @@ def test_phase1_validation_codes():
     assert B.load().sparse_attn_bwd_workspace_size(None, None) == 1
     st = B.load().sparse_attn_bwd_workspace_size(ctypes.byref(B.make_desc(wl)), None)
     assert st == 1
+
+
+def test_softmax_l1_workspace():
+    """The L1-norm sums take one fp32 plane per head group of the P kernel:
+    T * Hkv * positions * 4 bytes more for the 64-head MLA kernel."""
+    wl = W.WORKLOADS["mla_token_8k"]
+    for mode in (B.DKV_ATOMIC, B.DKV_DETERMINISTIC):
+        st0, n0 = _ws(B.make_desc(wl, mode))
+        st1, n1 = _ws(B.make_desc(wl, mode, softmax_l1=1))
+        assert st0 == st1 == 0
+        planes = 1 if mode == B.DKV_DETERMINISTIC else 4    # 64 heads: 1 MLA group, 4 row-kernel chunks
+        assert n1 - n0 == planes * wl.total_q * wl.n_kv_heads * wl.topk * 4
 
 
 def test_window_cmp_requires_shared_kv():

@@ -1,7 +1,9 @@
 """GPU parity: the HIP backward (through the C ABI) against the fp64 oracle
 on the same seeded inputs.  Bar per tensor: max|err| <= 1e-2 * max|ref| +
 1e-3 and relative Frobenius error <= 5e-3 (atomic dK/dV order varies, so
-only the tolerance is promised)."""
+only the tolerance is promised).  The softmax L1-norm side outputs are
+checked against the oracle's to the same bar, with and without them the
+gradients must match."""
 import numpy as np
 import pytest
 import torch
@@ -50,11 +52,27 @@ SMALL = {
 
 MODES = {"atomic": B.DKV_ATOMIC, "det": B.DKV_DETERMINISTIC}
 
+_ORACLE = {}
 
+
+def _oracle_small(name):
+    """Oracle results of a SMALL case (with L1 outputs), computed once."""
+    if name not in _ORACLE:
+        _ORACLE[name] = U.oracle_case(SMALL[name], l1=True)
+    return _ORACLE[name]
+
+
+@pytest.mark.parametrize("l1", [False, True], ids=["grads", "grads+l1"])
 @pytest.mark.parametrize("mode", list(MODES))
 @pytest.mark.parametrize("name", list(SMALL))
-def test_bwd_parity_small(name, mode):
-    U.run_full_case(SMALL[name], dkv_mode=MODES[mode])
+def test_bwd_parity_small(name, mode, l1):
+    inputs, Ob, Lb, ref = _oracle_small(name)
+    if not l1:
+        ref = {k: v for k, v in ref.items() if not k.endswith("_l1")}
+    res, got, _ = U.run_full_case(SMALL[name], dkv_mode=MODES[mode], l1=l1, oracle=(inputs, Ob, Lb, ref))
+    if l1:
+        assert "ori_softmax_l1" in res
+        assert ("cmp_softmax_l1" in res) == (SMALL[name].select == W.SEL_WINDOW_CMP)
 
 
 @pytest.mark.parametrize("name", ["token_gqa_d128_g20", "block_gqa_d128", "mla_wcmp_sinks_varlen"])
@@ -63,7 +81,7 @@ def test_bwd_deterministic_mode_is_bitwise_repeatable(name):
     inp = W.make_inputs(wl)
     pb, Ob, Lb = U.oracle_fwd_rounded(inp)
     U.say(f"[det] {name}")
-    runs = [U.gpu_bwd(wl, inp, Ob, Lb, B.DKV_DETERMINISTIC) for _ in range(3)]
+    runs = [U.gpu_bwd(wl, inp, Ob, Lb, B.DKV_DETERMINISTIC, l1=True) for _ in range(3)]
     for k in runs[0]:
         for r in runs[1:]:
             assert np.array_equal(runs[0][k].view(np.uint32), r[k].view(np.uint32)), k
@@ -84,8 +102,11 @@ def test_bwd_edge_shuffled_padding_duplicates_empty_rows(mode):
     idx[40] = -1                                  # no valid key
     idx[41, 0, :] = -1
     inp["idx"] = torch.from_numpy(idx)
-    res, got, ref = U.run_full_case(wl, inputs=inp, dkv_mode=MODES[mode])
+    res, got, ref = U.run_full_case(wl, inputs=inp, dkv_mode=MODES[mode], l1=True)
     assert np.all(got["dq"].reshape(ref["dq"].shape)[40] == 0)
+    l1 = got["ori_softmax_l1"].reshape(ref["ori_l1"].shape)
+    assert np.all(l1[40] == 0) and np.all(l1[41] == 0)
+    assert l1[90, 0, 0] == l1[90, 0, 1] > 0       # a duplicate repeats its twin's value
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -107,8 +128,11 @@ def test_bwd_block_edge_varlen_ragged_heads_duplicates(mode, d):
     idx[151, 1, 2] = 999                          # out of range -> unused
     idx[30] = -1                                  # no block for either kv head
     inp["idx"] = torch.from_numpy(idx)
-    res, got, ref = U.run_full_case(wl, inputs=inp, dkv_mode=MODES[mode])
+    res, got, ref = U.run_full_case(wl, inputs=inp, dkv_mode=MODES[mode], l1=True)
     assert np.all(got["dq"].reshape(ref["dq"].shape)[30] == 0)
+    l1 = got["ori_softmax_l1"].reshape(ref["ori_l1"].shape)
+    assert np.all(l1[30] == 0)
+    np.testing.assert_array_equal(l1[150, 0, :32], l1[150, 0, 32:64])   # duplicated block
 
 
 def test_bwd_empty_query_is_noop():
@@ -156,7 +180,7 @@ def test_fwd_parity_small(name):
     np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
 
 
-def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINISTIC):
+def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINISTIC, l1=False):
     """Full-size run where only the compared rows need the oracle: GPU
     forward supplies O/lse for all tokens, the oracle's own O/lse replace
     them for the last n_tail tokens (and a few early ones); compared are dq
@@ -166,7 +190,7 @@ def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINI
     inp = W.make_inputs(wl)
     T = wl.total_q
     dev = B.device_tensors(inp)
-    desc = B.make_desc(wl, dkv_mode)
+    desc = B.make_desc(wl, dkv_mode, softmax_l1=int(l1))
     U.say(f"[full] {wl.name}: GPU forward")
     o, lse = B.sparse_attn_fwd(desc, dev)
     rng = np.random.default_rng(seed)
@@ -189,12 +213,19 @@ def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINI
     L_full[torch.from_numpy(toks)] = Lb
     U.say(f"[full] {wl.name}: oracle backward on {toks.size} tokens")
     ref = O.sparse_bwd(pb, O_full, L_full, tokens=toks.tolist())
+    if l1:
+        U.say(f"[full] {wl.name}: oracle softmax L1-norm on {toks.size} tokens")
+        ref.update({k + "_l1": v for k, v in O.softmax_l1_norm(pb, L_full, tokens=toks.tolist()).items()})
     for k in got:
         assert np.isfinite(got[k]).all(), k
     key = "dkv" if wl.kv_shared else "dk"
     rows = {"dq": toks, key: np.arange(T - n_tail, T)}
     if not wl.kv_shared:
         rows["dv"] = np.arange(T - n_tail, T)
+    if l1:
+        rows["ori_softmax_l1"] = toks
+        if wl.select == W.SEL_WINDOW_CMP:
+            rows["cmp_softmax_l1"] = toks
     if wl.select == W.SEL_WINDOW_CMP:
         # cmp row c of the last sequence is visible only to tokens whose
         # local position is >= cmp_ratio * c + cmp_ratio - 1
@@ -221,6 +252,14 @@ def test_bwd_parity_mla_cmp_sinks_varlen_full_size_sampled(mode):
 @pytest.mark.parametrize("mode", list(MODES))
 def test_bwd_parity_mla_8k_full_size_sampled(mode):
     _tail_splice_case(W.WORKLOADS["mla_token_8k"], dkv_mode=MODES[mode])
+
+
+@pytest.mark.parametrize("name", ["mla_token_8k", "nsa_block_gqa", "mla_cmp_sinks_varlen"])
+def test_softmax_l1_full_size_sampled(name):
+    """Softmax L1-norm outputs at full size in the deterministic launch
+    configuration (MLA kernel, block dQ kernel, window + cmp), sampled
+    token rows, with the gradients of the same call."""
+    _tail_splice_case(W.WORKLOADS[name], dkv_mode=B.DKV_DETERMINISTIC, l1=True)
 
 
 def test_bwd_parity_mla_32k_full_size_sampled():

@@ -32,7 +32,8 @@ class SaDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "layout", "batch", "seqlen_q", "seqlen_kv", "total_q", "total_kv", "total_cmp", "n_q_heads",
         "n_kv_heads", "d_qk", "d_v", "kv_shared", "select", "topk", "block_size", "mask_causal",
-        "win_left", "win_right", "cmp_ratio", "has_sinks", "dkv_mode")] + [("scale", ctypes.c_float)]
+        "win_left", "win_right", "cmp_ratio", "has_sinks", "dkv_mode")] + [("scale", ctypes.c_float),
+                                                                           ("softmax_l1", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -41,7 +42,8 @@ _P = ctypes.c_void_p
 class SaBwdArgs(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "q", "k", "v", "kv", "cmp_kv", "o", "d_o", "lse", "sinks", "topk_indices", "cu_seqlens_q",
-        "cu_seqlens_kv", "cu_seqlens_cmp", "dq", "dk", "dv", "dkv", "d_cmp_kv", "dsinks")]
+        "cu_seqlens_kv", "cu_seqlens_cmp", "dq", "dk", "dv", "dkv", "d_cmp_kv", "dsinks", "ori_softmax_l1",
+        "cmp_softmax_l1")]
 
 
 class SaFwdArgs(ctypes.Structure):
@@ -150,6 +152,17 @@ def alloc_bwd_outputs(desc: SaDesc, tensors: Dict[str, torch.Tensor]) -> Dict[st
         out["d_cmp_kv"] = torch.empty_like(tensors["cmp_kv"])
     if desc.has_sinks:
         out["dsinks"] = torch.empty(desc.n_q_heads, dtype=torch.float32, device=dev)
+    if desc.softmax_l1:
+        T = q.numel() // (desc.n_q_heads * desc.d_qk)
+        if desc.select == W.SEL_TOKEN:
+            n_ori = desc.topk
+        elif desc.select == W.SEL_BLOCK:
+            n_ori = desc.topk * desc.block_size
+        else:
+            n_ori = desc.win_left + 1 + desc.win_right
+        out["ori_softmax_l1"] = torch.empty((T, desc.n_kv_heads, n_ori), dtype=torch.float32, device=dev)
+        if desc.select == W.SEL_WINDOW_CMP:
+            out["cmp_softmax_l1"] = torch.empty((T, desc.n_kv_heads, desc.topk), dtype=torch.float32, device=dev)
     return out
 
 
@@ -171,7 +184,7 @@ def sparse_attn_bwd(desc: SaDesc, tensors: Dict[str, torch.Tensor], outputs: Opt
     for name in ("q", "k", "v", "kv", "cmp_kv", "o", "d_o", "lse", "sinks", "topk_indices", "cu_seqlens_q",
                  "cu_seqlens_kv", "cu_seqlens_cmp"):
         setattr(a, name, _ptr(tensors.get(name)))
-    for name in ("dq", "dk", "dv", "dkv", "d_cmp_kv", "dsinks"):
+    for name in ("dq", "dk", "dv", "dkv", "d_cmp_kv", "dsinks", "ori_softmax_l1", "cmp_softmax_l1"):
         setattr(a, name, _ptr(outputs.get(name)))
     if events is None:
         _check("sparse_attn_bwd", lib.sparse_attn_bwd(ctypes.byref(desc), ctypes.byref(a), _ptr(workspace),

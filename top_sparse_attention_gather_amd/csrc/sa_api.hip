@@ -40,6 +40,7 @@ sa_status_t validate(const sa_desc_t* d) {
   if (d->mask_causal != 0 && d->mask_causal != 1) return SA_ERR_BAD_ARG;
   if (d->has_sinks != 0 && d->has_sinks != 1) return SA_ERR_BAD_ARG;
   if (!std::isfinite(d->scale)) return SA_ERR_BAD_ARG;
+  if (d->softmax_l1 != 0 && d->softmax_l1 != 1) return SA_ERR_BAD_ARG;
   if (d->batch < 1 || d->n_q_heads < 0 || d->n_kv_heads < 1) return SA_ERR_BAD_SHAPE;
   if (d->n_q_heads % d->n_kv_heads != 0) return SA_ERR_BAD_SHAPE;
   if (d->d_qk <= 0 || d->d_v <= 0) return SA_ERR_BAD_SHAPE;
@@ -95,6 +96,8 @@ Params make_params(const sa_desc_t* d);
 
 struct BwdLayout {
   size_t D, sink_term, acc_k, acc_v, acc_cmp;                   // atomic mode
+  size_t l1;                                                    // softmax L1-norm head-chunk sums
+  int n_hg_l1;
   size_t blk_base, row_ptr, entries, csr_ws, partial, dump, acc;   // deterministic mode
   size_t bpart, bchunk, bcnt, bscan;                            // block key-major chunks
   long long max_chunks;
@@ -111,6 +114,14 @@ BwdLayout bwd_layout(const sa_desc_t* d, const Params& p) {
   off += align_up(T * Hq * sizeof(float));
   L.sink_term = off;
   if (d->has_sinks) off += align_up(T * Hq * sizeof(float));
+  // head chunks of the kernel that computes P (it writes one plane of
+  // softmax L1-norm sums per chunk)
+  const bool det = d->dkv_mode == SA_DKV_DETERMINISTIC;
+  if (det && sa::mla_bwd_supported(p)) L.n_hg_l1 = sa::mla_bwd_head_groups(p);
+  else if (det && sa::blk_dkv_supported(p) && sa::blk_dq_supported(p)) L.n_hg_l1 = sa::blk_dkv_head_chunks(p);
+  else L.n_hg_l1 = sa::bwd_rows_head_chunks(p);
+  L.l1 = off;
+  if (d->softmax_l1) off += align_up((size_t)L.n_hg_l1 * T * Hkv * (size_t)n_positions_host(d) * sizeof(float));
   if (d->dkv_mode == SA_DKV_ATOMIC) {
     L.acc_k = off;
     off += align_up((size_t)rows_kv(d) * Hkv * d->d_qk * sizeof(float));
@@ -243,6 +254,12 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   if (desc->kv_shared ? !a->dkv : (!a->dk || !a->dv)) return SA_ERR_NULL_PTR;
   if (desc->select == SA_SEL_WINDOW_CMP && !a->d_cmp_kv) return SA_ERR_NULL_PTR;
   if (desc->has_sinks && !a->dsinks) return SA_ERR_NULL_PTR;
+  if (desc->softmax_l1) {
+    if (!a->ori_softmax_l1 || (desc->select == SA_SEL_WINDOW_CMP && desc->topk > 0 && !a->cmp_softmax_l1))
+      return SA_ERR_NULL_PTR;
+    if (((uintptr_t)a->ori_softmax_l1 & 3u) != 0 || ((uintptr_t)a->cmp_softmax_l1 & 3u) != 0)
+      return SA_ERR_MISALIGNED;
+  }
   if (!workspace) return SA_ERR_NULL_PTR;
   if (workspace_bytes < need) return SA_ERR_WORKSPACE_TOO_SMALL;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return SA_ERR_MISALIGNED;
@@ -271,8 +288,14 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   w.sink_term = desc->has_sinks ? reinterpret_cast<float*>(ws + L.sink_term) : nullptr;
   w.dq = static_cast<bf16*>(a->dq);
   w.dsinks = a->dsinks;
+  w.l1 = desc->softmax_l1 ? reinterpret_cast<float*>(ws + L.l1) : nullptr;
   w.t0 = 0;
   w.Tc = p.T;
+  // softmax L1-norm outputs from the head-chunk sums the P kernel wrote
+  auto l1_norm = [&]() -> hipError_t {
+    if (!w.l1) return hipSuccess;
+    return sa::launch_l1_norm(p, w.l1, L.n_hg_l1, a->ori_softmax_l1, a->cmp_softmax_l1, s);
+  };
 
   const size_t Hkv = (size_t)desc->n_kv_heads;
   SA_TRY_HIP(sa::launch_preprocess(p, w, s));
@@ -291,6 +314,7 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
     SA_TRY_HIP(sa::launch_bwd_rows(p, w, s));
     if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
+    SA_TRY_HIP(l1_norm());
     SA_TRY_HIP(sa::launch_cast_bf16(w.acc_k, static_cast<bf16*>(desc->kv_shared ? a->dkv : a->dk), nk, s));
     if (nv) SA_TRY_HIP(sa::launch_cast_bf16(w.acc_v, static_cast<bf16*>(a->dv), nv, s));
     if (nc) SA_TRY_HIP(sa::launch_cast_bf16(w.acc_cmp, static_cast<bf16*>(a->d_cmp_kv), nc, s));
@@ -315,6 +339,7 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
     SA_TRY_HIP(sa::blk_dq_supported(p) ? sa::launch_blk_dq(p, w, s) : sa::launch_bwd_rows(p, w, s));
     if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
+    SA_TRY_HIP(l1_norm());
     sa::BlkArgs ba;
     std::memset(&ba, 0, sizeof(ba));
     ba.row_ptr = row_ptr;
@@ -370,6 +395,7 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     SA_TRY_HIP(sa::launch_reduce(p, r, s));
     first = false;
   }
+  SA_TRY_HIP(l1_norm());
   bf16* out_a = static_cast<bf16*>(desc->kv_shared ? a->dkv : a->dk);
   bf16* out_b = desc->kv_shared ? nullptr : static_cast<bf16*>(a->dv);
   SA_TRY_HIP(sa::launch_split_cast(acc, r.n_kv_out, L.RW, desc->d_qk, out_a, out_b, s));

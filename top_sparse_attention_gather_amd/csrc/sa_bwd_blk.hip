@@ -286,6 +286,7 @@ __global__ __launch_bounds__(kThreads) void blk_dq_kernel(Params p, BwdBuffers w
   __shared__ __attribute__((aligned(16))) bf16 sK[2][64 * D];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][64 * D];
   __shared__ int sBlk[kDqMaxSlots];
+  __shared__ int sSlot[kDqMaxSlots];   // index slot of every usable block (L1-norm positions)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -312,7 +313,10 @@ __global__ __launch_bounds__(kThreads) void blk_dq_kernel(Params p, BwdBuffers w
   __syncthreads();
   int base = 0;
   for (int i = 0; i < wv; ++i) base += sW[i];
-  if (ok) sBlk[base + __popcll(m & ((1ull << lane) - 1ull))] = blk;
+  if (ok) {
+    sBlk[base + __popcll(m & ((1ull << lane) - 1ull))] = blk;
+    sSlot[base + __popcll(m & ((1ull << lane) - 1ull))] = tid;
+  }
   const int nb = sW[0] + sW[1] + sW[2] + sW[3];
   __syncthreads();
 
@@ -383,6 +387,7 @@ __global__ __launch_bounds__(kThreads) void blk_dq_kernel(Params p, BwdBuffers w
       // lane: head l16, block rows r0 + 4lq + i
       const long long jb = (long long)sBlk[bi] * p.bs;
       i16x4 dSa;
+      float prs[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = r0 + lq * 4 + i;
@@ -390,6 +395,21 @@ __global__ __launch_bounds__(kThreads) void blk_dq_kernel(Params p, BwdBuffers w
         const bool v = live && rr < p.bs && jl < sp.kv_len && (!p.causal || jl <= sp.tl);
         const float pr = v ? __builtin_amdgcn_exp2f(S[i] * sl2 - lse2) : 0.f;
         dSa[i] = bf16_bits((bf16)(pr * (dP[i] - Dh)));
+        prs[i] = pr;
+      }
+      if (w.l1) {
+        // softmax L1-norm: P summed over the chunk's 16 heads (a 16-lane
+        // row); lane l16 < 4 writes block row r0 + 4lq + l16 at its virtual
+        // position slot * bs + row (rows past the block's end are skipped)
+        float hs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hs[i] = row16_sum(prs[i]);
+        const int i = l16 & 3;
+        const float mine = i == 0 ? hs[0] : i == 1 ? hs[1] : i == 2 ? hs[2] : hs[3];
+        const int rr = r0 + lq * 4 + i;
+        if (l16 < 4 && rr < p.bs)
+          w.l1[((size_t)blockIdx.y * p.T * p.Hkv + row) * ((size_t)p.topk * p.bs) + (size_t)sSlot[bi] * p.bs + rr] =
+              mine;
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {

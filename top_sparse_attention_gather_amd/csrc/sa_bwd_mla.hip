@@ -84,6 +84,7 @@ struct __attribute__((aligned(16))) MlaSmem {
   int rows[kMaxPos];
   int vpos[kMaxPos];
   int wave[4];
+  float l1s[4][kNT];               // softmax L1-norm: P summed over each wave's 16 heads, per key
 };
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -119,6 +120,9 @@ __device__ __forceinline__ void gather_tile(const Params& p, const MlaSmem& sm, 
     __builtin_amdgcn_global_load_lds((gbl_void*)(src + sg * 64), (lds_void*)(d + sg * kSegElems), 16, 0, 0);
 }
 
+// L1: also write the head sums of P behind the softmax L1-norm outputs
+// (SparseFlashMlaGrad README, parameter table).
+template <bool L1>
 __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffers w) {
   __shared__ MlaSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -135,7 +139,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
                     (((size_t)blockIdx.y * w.Tc * p.Hkv + blockIdx.x) * w.npos) * kDQK;
 
   // ---- compacted selection (positions and their row codes) --------------
-  const int cnt = compact_positions_batched<kMaxPos / 256>(p, s, irow, n_positions(p), sm.rows, sm.wave, sm.vpos);
+  const int npos = n_positions(p);
+  const int cnt = compact_positions_batched<kMaxPos / 256>(p, s, irow, npos, sm.rows, sm.wave, sm.vpos);
 
   // ---- lse / D of the wave's heads (phase-A layout: head = 16 wv + l16) ---
   const int hA = h0 + wv * 16 + l16;
@@ -241,6 +246,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   const int offX0 = (lq * 4 + (l16 >> 2)) * kXS + trq * 4;
   const int offX1 = (16 + lq * 4 + (l16 >> 2)) * kXS + trq * 4;
   bf16* dump = static_cast<bf16*>(w.dump);
+  float* l1_row = L1 ? w.l1 + ((size_t)blockIdx.y * p.T * p.Hkv + row) * npos : nullptr;
   const int grow = wv * 8 + (lane >> 3);            // the row this lane gathers (row group wv)
   const int gcol = seg_chunk(lane) * 8;
   // phase-B / dQ column block c of this wave (16 columns)
@@ -323,6 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     // P = exp(scale S - lse), dS = P (dP - D) for keys 16b + 4lq + r, head
     // l16; scale dS and P into the exchange
     auto softmax_grad = [&](int b, const f32x4& S, const f32x4& dP) {
+      float prs[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = b * 16 + lq * 4 + r;
@@ -331,6 +338,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
         const float ds = pr * (dP[r] - Dv);
         xw[key * kXS + wv * 16 + l16] = (bf16)(ds * p.scale);
         pw[key * kXS + wv * 16 + l16] = (bf16)pr;
+        prs[r] = pr;
+      }
+      if constexpr (L1) {
+        // sum over the wave's 16 heads (the lanes of a 16-lane row); the
+        // lanes with l16 % 4 == r store key 4lq + r (equal values, no branch)
+        float hs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hs[r] = row16_sum(prs[r]);
+        const int r = l16 & 3;
+        const float mine = r == 0 ? hs[0] : r == 1 ? hs[1] : r == 2 ? hs[2] : hs[3];
+        sm.l1s[wv][b * 16 + lq * 4 + r] = mine;
       }
     };
     f32x4 Sh0, Ph0;
@@ -379,6 +397,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     }
     // exchange written: an LDS-only barrier, so the gather stays in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    if constexpr (L1) {
+      // wave 0: the four waves' head sums of key `lane % 32`, to the key's
+      // virtual position (lanes without a key of the tile: to the dump row)
+      if (wv == 0) {
+        const int key = lane & 31;
+        const float v = sm.l1s[0][key] + sm.l1s[1][key] + sm.l1s[2][key] + sm.l1s[3][key];
+        const bool ok = lane < nvalid;
+        float* dst = ok ? l1_row + sm.vpos[k0 + key] : reinterpret_cast<float*>(dump) + lane;
+        *dst = v;
+      }
+    }
 
     // ---- dQ^T[cols][h] += KV^T[cols][keys] (scale dS^T)[keys][h] ---------
     // keys of k-group lq: 4lq..4lq+3 and 16+4lq..16+4lq+3 on both operands
@@ -452,7 +482,8 @@ int mla_bwd_head_groups(const Params& p) { return p.G / kHeads; }
 
 hipError_t launch_bwd_mla(const Params& p, const BwdBuffers& w, hipStream_t s) {
   dim3 grid((unsigned)(w.Tc * p.Hkv), (unsigned)(p.G / kHeads));
-  hipLaunchKernelGGL(mla_bwd_kernel, grid, dim3(kThreads), 0, s, p, w);
+  if (w.l1) hipLaunchKernelGGL(mla_bwd_kernel<true>, grid, dim3(kThreads), 0, s, p, w);
+  else hipLaunchKernelGGL(mla_bwd_kernel<false>, grid, dim3(kThreads), 0, s, p, w);
   return hipGetLastError();
 }
 

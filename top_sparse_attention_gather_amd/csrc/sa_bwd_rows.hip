@@ -93,6 +93,55 @@ __global__ void cast_bf16_kernel(const float* __restrict__ src, bf16* __restrict
     dst[i] = (bf16)src[i];
 }
 
+// Softmax L1-norm outputs (SparseFlashMlaGrad README, parameter table;
+// aclnnSparseLightningIndexerGradKLLoss, "Formula": the head-summed main
+// attention probabilities, L1-normalised along the context).  One
+// workgroup per (token, kv head) row: the head-chunk sums of every used
+// position are added in chunk order (unused positions count 0 and are not
+// read), each thread keeps a strided partial of the ori and of the cmp
+// total, a fixed tree adds them, and a second pass writes value / total
+// (0 when the total is 0).  Repeatable: no atomics, a fixed order.
+__global__ __launch_bounds__(kThreads) void l1_norm_kernel(Params p, const float* __restrict__ l1, int n_hg,
+                                                           float* __restrict__ ori, float* __restrict__ cmp) {
+  __shared__ float red[2][kThreads];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;   // (token, kv head)
+  const SeqPos s = seq_pos(p, row / p.Hkv);
+  const int* irow = p.idx + (size_t)row * p.topk;
+  const int npos = n_positions(p);
+  const int n_ori = p.select == kSelWindowCmp ? p.win_left + 1 + p.win_right : npos;
+  const size_t plane = (size_t)p.T * p.Hkv * npos;
+  const float* src = l1 + (size_t)row * npos;
+  auto value = [&](int pos) {
+    float v = 0.f;
+    if (decode_position(p, s, irow, pos) >= 0)
+      for (int c = 0; c < n_hg; ++c) v += src[(size_t)c * plane + pos];
+    return v;
+  };
+  float so = 0.f, sc = 0.f;
+  for (int pos = tid; pos < npos; pos += kThreads) {
+    const float v = value(pos);
+    if (pos < n_ori) so += v;
+    else sc += v;
+  }
+  red[0][tid] = so;
+  red[1][tid] = sc;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) {
+      red[0][tid] += red[0][tid + w];
+      red[1][tid] += red[1][tid + w];
+    }
+    __syncthreads();
+  }
+  const float to = red[0][0], tc = red[1][0];
+  for (int pos = tid; pos < npos; pos += kThreads) {
+    const float v = value(pos);
+    if (pos < n_ori) ori[(size_t)row * n_ori + pos] = to > 0.f ? v / to : 0.f;
+    else cmp[(size_t)row * p.topk + (pos - n_ori)] = tc > 0.f ? v / tc : 0.f;
+  }
+}
+
 template <int DQK, int DV, bool SHARED>
 __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers w) {
   constexpr int QS = DQK + 8;   // LDS row stride (elements) of Q and K tiles
@@ -228,8 +277,18 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
           sPt[j * TS + h] = pb;
           sdSt[j * TS + h] = db;
         }
+        if (w.l1) sS[e] = pv;   // fp32 P for the head sums (only this thread read sS[e])
       }
       __syncthreads();
+
+      // ---- softmax L1-norm: sum of P over the chunk's heads per key ------
+      // (heads past Gc have lse = +inf, so P = 0 there)
+      if (w.l1 && tid < kNT && k0 + tid < cnt) {
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < kHC; ++h) acc += sS[h * kNT + tid];
+        w.l1[((size_t)blockIdx.y * p.T * p.Hkv + row) * npos + sVpos[k0 + tid]] = acc;
+      }
 
       // ---- dQ += dS K (column blocks split over the 4 waves) ----------------
       {
@@ -362,6 +421,13 @@ hipError_t launch_fill_zero(float* ptr, size_t n, hipStream_t s) {
   }
   const size_t rest = n - n4 * 4;
   if (rest) hipLaunchKernelGGL(fill_zero_tail_kernel, dim3(1), dim3(64), 0, s, ptr + n4 * 4, rest);
+  return hipGetLastError();
+}
+
+hipError_t launch_l1_norm(const Params& p, const float* l1, int n_hg, float* ori, float* cmp, hipStream_t s) {
+  const long long rows = (long long)p.T * p.Hkv;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(l1_norm_kernel, dim3((unsigned)rows), dim3(kThreads), 0, s, p, l1, n_hg, ori, cmp);
   return hipGetLastError();
 }
 

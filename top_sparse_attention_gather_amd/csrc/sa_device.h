@@ -193,6 +193,23 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
 
 __device__ __forceinline__ short bf16_bits(bf16 x) { return __builtin_bit_cast(short, x); }
 
+// Sum over each row of 16 lanes, the result in all 16 (DPP: swap
+// neighbours, swap pairs, mirror within 8, mirror within 16).  Every lane
+// of a row ends with the same bits: each step adds two operands whose
+// order differs between lanes only by commutation.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x141>(v);   // row_half_mirror
+  v += dpp_f32<0x140>(v);   // row_mirror
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);

@@ -26,6 +26,11 @@ struct BwdBuffers {
   // (shared KV: dKV [dqk]; separate: dK [dqk] then dV [dv])
   void* partial;
   void* dump;        // one never-read row: target of the stores of unused tile rows
+  // softmax L1-norm outputs: the row kernels write, for every (token, kv
+  // head) row and used virtual position, the sum of P over the workgroup's
+  // heads to l1[(head chunk * T * Hkv + row) * npos + position] (null: not
+  // requested); the normalisation pass sums the head chunks
+  float* l1;
   int det;
   int dq_only;       // row kernel: dQ only (dK/dV come from the key-major block kernel)
   int t0, Tc, npos, RW;
@@ -65,6 +70,11 @@ hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_key
 
 hipError_t launch_reduce(const Params& p, const ReduceArgs& r, hipStream_t s);
 hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk, bf16* a, bf16* b, hipStream_t s);
+
+// Softmax L1-norm outputs from the head-chunk sums `l1` ([n_hg][T * Hkv]
+// [npos]): per (token, kv head) row, the chunk sums of every used position
+// are added in chunk order, then divided by the ori (resp. cmp) total.
+hipError_t launch_l1_norm(const Params& p, const float* l1, int n_hg, float* ori, float* cmp, hipStream_t s);
 
 }  // namespace sa
 
