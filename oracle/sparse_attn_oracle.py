@@ -57,7 +57,7 @@ design notes):
   R11 cu_seqlens are cumulative ([B+1], cu[0] = 0);
   R12 index values and window positions are sequence-local;
   R15 GQA: query head h uses kv head h // G; indices are per (token, kv head);
-  R16 the softmax L1-norm outputs sum the backward's P (given lse, sinks in
+  R18 the softmax L1-norm outputs sum the backward's P (given lse, sinks in
       the denominator) over the G heads of a kv head and normalise the ori
       and the cmp entries separately; they are laid out by virtual position
       (slot, block row, window offset) with 0 where nothing is selected.
