@@ -30,6 +30,11 @@ What it computes, and where the pages define it:
   table; aclnnSparseLightningIndexerGradKLLoss, "Formula": the target
   distribution p): P summed over the group's heads, L1-normalised over the
   ori entries and, separately, over the cmp entries.
+* Sparse lightning-indexer gradient with the KL loss
+  (aclnnSparseLightningIndexerGradKLLoss, "Formula"; the dense page's
+  "Formulas" 1-4): index score I = W ReLU(q~ K~^T) over the selected rows,
+  loss = KL(p || softmax(I)), dI = softmax(I) - p, and dW, dq~, dK~ by the
+  chain rule.
 * CSR transpose of the index lists (no passage on the pages: it is the
   bookkeeping for a deterministic key-major reduction): for every key, the
   flat ids p = (t * Hkv + g) * K + slot of the valid entries naming it, in
@@ -60,7 +65,10 @@ design notes):
   R18 the softmax L1-norm outputs sum the backward's P (given lse, sinks in
       the denominator) over the G heads of a kv head and normalise the ori
       and the cmp entries separately; they are laid out by virtual position
-      (slot, block row, window offset) with 0 where nothing is selected.
+      (slot, block row, window offset) with 0 where nothing is selected;
+  R19 the indexer's S~ is the raw product q~ K~^T (no scale); its softmax and
+      loss run over the selected rows; the target p is given per slot and
+      only used slots count; dI = softmax(I) - p as printed.
 """
 from __future__ import annotations
 
@@ -359,6 +367,74 @@ def softmax_l1_norm(pb: Problem, lse: torch.Tensor,
     if cmp is not None:
         res["cmp"] = cmp
     return res
+
+
+# ----------------------------------------------------------------------------
+# Sparse lightning-indexer gradient with the KL loss
+# ----------------------------------------------------------------------------
+
+def indexer_grad_kl(inputs: Dict[str, object], tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Gradient of the indexer's KL loss over the top-k selected rows, fp64.
+
+    aclnnSparseLightningIndexerGradKLLoss, "Formula", and the same steps on
+    aclnnDenseLightningIndexerGradKLLoss, "Formulas" 1-4, restricted to the
+    selected keys.  For every token t, over the rows j it selected (token
+    selection rules of `Problem.selection`, kv head 0):
+
+        S~ = q~_t K~_sel^T                    [heads, n]   (raw product)
+        I  = W_t ReLU(S~)                     [n]          (index score)
+        s  = softmax(I)                       over the selected rows
+        loss_t = sum_j p_j log(p_j / s_j)     (terms with p_j = 0 vanish)
+        dI = s - p
+        dW_t   = ReLU(S~) dI
+        dS~    = W_t[h] * [S~ > 0] * dI       (chain rule through the ReLU)
+        dq~_t  = dS~ K~_sel,   dK~[j] += dS~^T q~_t   (scatter into rows j)
+
+    p (`target` [T, 1, K]) is the target distribution by slot, taken as
+    given; only the used slots count.  Readings: S~ is the raw product (the
+    dense page's statement; the sparse page's "softmax of QK" is taken as a
+    garble), there is no scale, the softmax runs over the selected rows only,
+    duplicated slots are separate terms, a token with no used slot has loss 0
+    and no gradient.
+
+    Returns dq [T, H, d], dk [T_kv, d], dweights [T, H], loss_per_token [T]
+    and loss (the sum over tokens).
+    """
+    wl = inputs["workload"]
+    view = {"workload": wl, "idx": inputs["idx"], "cu_seqlens": inputs["cu_seqlens"],
+            "cu_seqlens_cmp": inputs["cu_seqlens_cmp"], "kv": inputs["k_idx"][:, None, :]}
+    pb = Problem(view)
+    q = inputs["q_idx"]
+    k = inputs["k_idx"]
+    W = _f64(inputs["weights"])
+    P = _f64(inputs["target"])[:, 0, :]
+    T, H, d = q.shape
+    dq = np.zeros((T, H, d))
+    dk = np.zeros((k.shape[0], d))
+    dW = np.zeros((T, H))
+    loss_t = np.zeros(T)
+    toks = range(T) if tokens is None else tokens
+    for t in toks:
+        _, rows, pos = pb.selection_positions(t, 0)
+        if rows.size == 0:
+            continue
+        qt = _f64(q[t])                                   # [H, d]
+        K = _f64(k[torch.from_numpy(rows)])               # [n, d]
+        S = qt @ K.T                                      # [H, n]
+        R = np.maximum(S, 0.0)
+        I = W[t] @ R                                      # [n]
+        m = I.max()
+        logs = I - m - np.log(np.exp(I - m).sum())        # log softmax over the selected rows
+        s_ = np.exp(logs)
+        p = P[t, pos]
+        nz = p > 0
+        loss_t[t] = float((p[nz] * (np.log(p[nz]) - logs[nz])).sum())
+        dI = s_ - p
+        dW[t] = R @ dI
+        dS = (W[t][:, None] * (S > 0)) * dI[None, :]
+        dq[t] = dS @ K
+        np.add.at(dk, rows, dS.T @ qt)
+    return {"dq": dq, "dk": dk, "dweights": dW, "loss_per_token": loss_t, "loss": float(loss_t.sum())}
 
 
 # ----------------------------------------------------------------------------

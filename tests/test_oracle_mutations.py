@@ -35,6 +35,13 @@ MUTATIONS = {
                   "P = np.exp(S)"),
     "l1_block_pos_compacted": ("pos = (slots[:, None] * bs + np.arange(bs)[None, :])",
                                "pos = (np.arange(slots.size)[:, None] * bs + np.arange(bs)[None, :])"),
+    # sparse lightning-indexer gradient with the KL loss
+    "idx_dI_sign": ("dI = s_ - p", "dI = p - s_"),
+    "idx_no_relu_mask": ("dS = (W[t][:, None] * (S > 0)) * dI[None, :]", "dS = W[t][:, None] * dI[None, :]"),
+    "idx_dW_no_relu": ("dW[t] = R @ dI", "dW[t] = S @ dI"),
+    "idx_reverse_kl": ("loss_t[t] = float((p[nz] * (np.log(p[nz]) - logs[nz])).sum())",
+                       "loss_t[t] = float((s_[nz] * (logs[nz] - np.log(p[nz]))).sum())"),
+    "idx_slot_not_position": ("p = P[t, pos]", "p = P[t, :pos.size]"),
 }
 
 
@@ -103,7 +110,18 @@ def _selection_ok(mod, mode):
 def test_pins_catch_planted_mistake(name):
     mod = _mutant(name)
     caught = []
-    if name.startswith("l1_"):
+    if name.startswith("idx_"):
+        from tests import test_oracle_indexer_pins as IX
+        pins = [lambda: IX.pin_finite_differences(mod), lambda: IX.pin_dense_autograd(mod, True),
+                lambda: IX.pin_dense_autograd(mod, False), lambda: IX.pin_zero_weights(mod),
+                lambda: IX.pin_self_consistent_target(mod), lambda: IX.pin_empty_token(mod)]
+        for pin in pins:
+            try:
+                pin()
+                caught.append(False)
+            except AssertionError:
+                caught.append(True)
+    elif name.startswith("l1_"):
         from tests import test_oracle_l1_pins as L1
         pins = [lambda m=m, sh=sh: L1.pin_full_coverage(mod, m, sh) for m in ("token_gqa", "block_gqa", "mla")
                 for sh in (False, True)]

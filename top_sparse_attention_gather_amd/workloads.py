@@ -147,6 +147,19 @@ WORKLOADS: Dict[str, Workload] = {
 WORKLOAD_ORDER = ["tiny_token_gqa", "nsa_block_gqa", "mla_token_8k", "mla_cmp_sinks_varlen",
                   "mla_token_32k_local"]
 
+# Sparse lightning-indexer gradient with the KL loss (the indexer that picks
+# the top-k rows: aclnnSparseLightningIndexerGradKLLoss).  n_q_heads is the
+# indexer's query heads per token, d_qk = d_v its head dim; the indexer key
+# is one row per token (n_kv_heads = 1).  The index lists use the same
+# policies as above; the target distribution is a random point of the
+# simplex over each token's used slots.
+INDEXER_WORKLOADS: Dict[str, Workload] = {
+    # 8K tokens, 64 indexer heads of dim 128, top-2048 uniform over the
+    # causal range (the index lists of the MLA 8K workload's shape).
+    "indexer_8k": _bsnd("indexer_8k", 1, 8192, 64, 1, 128, 128, True, 2048,
+                        select=SEL_TOKEN, index_policy="uniform_causal", seed=1006),
+}
+
 
 def small_workload(base: str, **overrides) -> Workload:
     """A copy of a named workload with some fields overridden (tests)."""
@@ -157,7 +170,7 @@ def small_workload(base: str, **overrides) -> Workload:
 # seeded generation
 # ----------------------------------------------------------------------------
 
-_STREAMS = ["q", "kv", "v", "do", "idx", "sinks", "cmp_noise"]
+_STREAMS = ["q", "kv", "v", "do", "idx", "sinks", "cmp_noise", "iq", "ik", "iw", "ip"]
 _CHUNK_ELEMS = 1 << 22
 
 
@@ -313,6 +326,35 @@ def make_inputs(wl: Workload, with_indices: bool = True, threads: int = 8) -> Di
     out["cu_seqlens_cmp"] = torch.from_numpy(wl.cu_seqlens_cmp())
     if with_indices:
         out["idx"] = torch.from_numpy(make_indices(wl))
+    return out
+
+
+def make_indexer_inputs(wl: Workload, with_indices: bool = True, threads: int = 8) -> Dict[str, object]:
+    """Seeded inputs of an indexer-gradient problem (CPU torch tensors).
+
+    Keys: q_idx [T, Hq, d] bf16 and k_idx [T_kv, d] bf16 (N(0, 1)),
+    weights [T, Hq] fp32 (N(0, 1 / (Hq d)), so the scores spread over a
+    few units), idx [T, 1, K] int32, target [T, 1, K] fp32 (per token a
+    Dirichlet(1) draw over the used slots, i.e. normalised Exp(1) weights,
+    0 on unused slots), cu_seqlens.
+    """
+    st = _streams(wl.seed)
+    T, Hq, d = wl.total_q, wl.n_q_heads, wl.d_qk
+    out: Dict[str, object] = {"workload": wl}
+    out["q_idx"] = _to_bf16(_normal_f32(st["iq"], (T, Hq, d), threads=threads))
+    out["k_idx"] = _to_bf16(_normal_f32(st["ik"], (wl.total_kv, d), threads=threads))
+    out["weights"] = torch.from_numpy(_normal_f32(st["iw"], (T, Hq), std=1.0 / math.sqrt(Hq * d),
+                                                  threads=threads))
+    out["cu_seqlens"] = torch.from_numpy(wl.cu_seqlens())
+    out["cu_seqlens_cmp"] = torch.from_numpy(wl.cu_seqlens_cmp())
+    if with_indices:
+        idx = make_indices(wl)
+        g = np.random.Generator(np.random.PCG64(st["ip"]))
+        u = g.standard_exponential(idx.shape, dtype=np.float32)
+        u[idx < 0] = 0.0
+        tot = u.sum(axis=-1, keepdims=True)
+        out["idx"] = torch.from_numpy(idx)
+        out["target"] = torch.from_numpy(np.where(tot > 0, u / np.where(tot > 0, tot, 1), 0).astype(np.float32))
     return out
 
 
