@@ -240,6 +240,71 @@ sa_status_t sparse_attn_csr_transpose(const sa_desc_t* desc, const int32_t* topk
                                       int32_t* row_ptr, int32_t* entries, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* ---- Sparse lightning-indexer gradient with the KL loss ------------------
+ *
+ * aclnnSparseLightningIndexerGradKLLoss, "Formula" (the same steps are
+ * spelled out on aclnnDenseLightningIndexerGradKLLoss, "Formulas" 1-4):
+ * the indexer scores the rows a query may attend to and is trained to match
+ * the main attention's head-summed, L1-normalised probabilities p (the
+ * softmax L1-norm output of sparse_attn_bwd).  For every query token t,
+ * over the rows j its index list selects (token selection rules above, one
+ * index list per token):
+ *   S~ = q~_t K~_sel^T   (raw product, no scale)        [n_heads, n]
+ *   I  = W_t ReLU(S~)                                    [n]
+ *   loss_t = sum_j p_j log(p_j / softmax(I)_j)   (terms with p_j = 0 vanish)
+ *   dI = softmax(I) - p       dW_t = ReLU(S~) dI
+ *   dS~ = W_t[h] [S~ > 0] dI  dq~_t = dS~ K~_sel   dK~[j] += dS~^T q~_t
+ * The softmax and the loss run over the selected rows only; p is read at
+ * the used slots (its values elsewhere are ignored); a token with no used
+ * slot has loss 0 and zero dq~ and dW.  dK~ is summed over tokens in a fixed
+ * order (bitwise repeatable); loss = sum over tokens of loss_t (fixed order,
+ * fp64 accumulation). */
+typedef struct sa_indexer_desc {
+  int32_t layout;       /* SA_LAYOUT_BSND or SA_LAYOUT_TND */
+  int32_t batch;        /* number of sequences (>= 1) */
+  int32_t seqlen_q;     /* BSND: query tokens per sequence */
+  int32_t seqlen_kv;    /* BSND: key rows per sequence */
+  int32_t total_q;      /* TND: total query tokens */
+  int32_t total_kv;     /* TND: total key rows */
+  int32_t n_heads;      /* indexer query heads per token (built: 1..64) */
+  int32_t d;            /* indexer head dim (built: 128) */
+  int32_t topk;         /* index slots per token (built: 1..2048) */
+  int32_t mask_causal;  /* 1: key position <= query position */
+} sa_indexer_desc_t;
+
+/* Device pointers of the indexer gradient (row-major, contiguous). */
+typedef struct sa_indexer_args {
+  const void* q;                  /* q~ [T, n_heads, d] bf16 */
+  const void* k;                  /* K~ [T_kv, d] bf16 */
+  const float* weights;           /* W [T, n_heads] fp32 */
+  const int32_t* topk_indices;    /* [T, topk] int32, sequence-local, negative = unused */
+  const float* target;            /* p [T, topk] fp32 by slot */
+  const int32_t* cu_seqlens_q;    /* TND only */
+  const int32_t* cu_seqlens_kv;   /* TND only */
+  void* dq;                       /* dq~ [T, n_heads, d] bf16 */
+  void* dk;                       /* dK~ [T_kv, d] bf16 */
+  float* dweights;                /* dW [T, n_heads] fp32 */
+  float* loss;                    /* [1] fp32: the summed loss */
+  float* loss_per_token;          /* [T] fp32, may be NULL */
+} sa_indexer_args_t;
+
+/* Phase 1: validates `desc` on the host and returns the workspace size
+ * (per-token losses, CSR buffers, bf16 partial dK~ rows, fp32 dK~
+ * accumulator).  SA_ERR_UNSUPPORTED outside the built sizes. */
+sa_status_t sparse_attn_indexer_grad_kl_workspace_size(const sa_indexer_desc_t* desc, size_t* bytes);
+
+/* Phase 2: enqueues the indexer gradient on `stream`; outputs are fully
+ * overwritten.  Same error behaviour as sparse_attn_bwd; an empty query
+ * returns SA_OK and launches nothing. */
+sa_status_t sparse_attn_indexer_grad_kl(const sa_indexer_desc_t* desc, const sa_indexer_args_t* args,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same, recording the caller's events (may be NULL) around the main kernel
+ * (all its launches when tokens are processed in chunks). */
+sa_status_t sparse_attn_indexer_grad_kl_timed(const sa_indexer_desc_t* desc, const sa_indexer_args_t* args,
+                                              void* workspace, size_t workspace_bytes, void* stream,
+                                              void* ev_main_start, void* ev_main_stop);
+
 /* Static string for a status code. */
 const char* sparse_attn_status_string(sa_status_t status);
 

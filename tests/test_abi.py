@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layout_matches_c(tmp_path):
     """Compile a C probe of the header with gcc and compare sizes/offsets."""
-    fields = {"sa_desc_t": B.SaDesc, "sa_bwd_args_t": B.SaBwdArgs, "sa_fwd_args_t": B.SaFwdArgs}
+    fields = {"sa_desc_t": B.SaDesc, "sa_bwd_args_t": B.SaBwdArgs, "sa_fwd_args_t": B.SaFwdArgs,
+              "sa_indexer_desc_t": B.SaIndexerDesc, "sa_indexer_args_t": B.SaIndexerArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "sparse_attn.h"', 'int main(void){']
     for cname, cls in fields.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -123,3 +124,28 @@ def test_status_strings():
     for code in range(8):
         s = B.sparse_attn_status_string(code)
         assert s.startswith(B.STATUS_NAMES[code])
+
+
+def test_indexer_phase1_validation_codes():
+    wl = W.INDEXER_WORKLOADS["indexer_8k"]
+    n = ctypes.c_size_t(0)
+    lib = B.load()
+
+    def ws(d):
+        return lib.sparse_attn_indexer_grad_kl_workspace_size(ctypes.byref(d), ctypes.byref(n))
+
+    assert ws(B.make_indexer_desc(wl)) == 0
+    # partial dK~ rows (bf16) + fp32 accumulator at least
+    assert n.value >= 8192 * 2048 * 128 * 2 + 8192 * 128 * 4
+    assert ws(B.make_indexer_desc(wl, layout=4)) == 7
+    assert ws(B.make_indexer_desc(wl, mask_causal=2)) == 7
+    assert ws(B.make_indexer_desc(wl, d=64)) == 3
+    assert ws(B.make_indexer_desc(wl, n_heads=65)) == 3
+    assert ws(B.make_indexer_desc(wl, topk=4096)) == 3
+    assert ws(B.make_indexer_desc(wl, topk=0)) == 2
+    assert ws(B.make_indexer_desc(wl, batch=0)) == 2
+    assert lib.sparse_attn_indexer_grad_kl_workspace_size(None, ctypes.byref(n)) == 1
+    # empty query: SA_OK, nothing launched
+    e = B.make_indexer_desc(W.small_workload("tiny_token_gqa", seqlens=(0,)), n_heads=4, d=128, topk=16)
+    a = B.SaIndexerArgs()
+    assert lib.sparse_attn_indexer_grad_kl(ctypes.byref(e), ctypes.byref(a), None, 0, None) == 0

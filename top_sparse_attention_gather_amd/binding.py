@@ -25,7 +25,8 @@ DKV_DETERMINISTIC = 1
 
 EXPORTED = ["sparse_attn_bwd_workspace_size", "sparse_attn_bwd", "sparse_attn_bwd_timed", "sparse_attn_fwd",
             "sparse_attn_csr_size",
-            "sparse_attn_csr_transpose", "sparse_attn_status_string", "sparse_attn_version"]
+            "sparse_attn_csr_transpose", "sparse_attn_indexer_grad_kl_workspace_size", "sparse_attn_indexer_grad_kl",
+            "sparse_attn_indexer_grad_kl_timed", "sparse_attn_status_string", "sparse_attn_version"]
 
 
 class SaDesc(ctypes.Structure):
@@ -50,6 +51,17 @@ class SaFwdArgs(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "q", "k", "v", "kv", "cmp_kv", "sinks", "topk_indices", "cu_seqlens_q", "cu_seqlens_kv",
         "cu_seqlens_cmp", "o", "lse")]
+
+
+class SaIndexerDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "layout", "batch", "seqlen_q", "seqlen_kv", "total_q", "total_kv", "n_heads", "d", "topk", "mask_causal")]
+
+
+class SaIndexerArgs(ctypes.Structure):
+    _fields_ = [(n, _P) for n in (
+        "q", "k", "weights", "topk_indices", "target", "cu_seqlens_q", "cu_seqlens_kv", "dq", "dk", "dweights",
+        "loss", "loss_per_token")]
 
 
 class SparseAttnError(RuntimeError):
@@ -80,11 +92,17 @@ def load() -> ctypes.CDLL:
     lib.sparse_attn_fwd.argtypes = [pd, ctypes.POINTER(SaFwdArgs), _P]
     lib.sparse_attn_csr_size.argtypes = [pd, _P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)]
     lib.sparse_attn_csr_transpose.argtypes = [pd, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    pi = ctypes.POINTER(SaIndexerDesc)
+    lib.sparse_attn_indexer_grad_kl_workspace_size.argtypes = [pi, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sparse_attn_indexer_grad_kl.argtypes = [pi, ctypes.POINTER(SaIndexerArgs), _P, ctypes.c_size_t, _P]
+    lib.sparse_attn_indexer_grad_kl_timed.argtypes = [pi, ctypes.POINTER(SaIndexerArgs), _P, ctypes.c_size_t, _P,
+                                                      _P, _P]
     lib.sparse_attn_status_string.argtypes = [ctypes.c_int]
     lib.sparse_attn_status_string.restype = ctypes.c_char_p
     lib.sparse_attn_version.restype = ctypes.c_int32
     for fn in ("sparse_attn_bwd_workspace_size", "sparse_attn_bwd", "sparse_attn_bwd_timed", "sparse_attn_fwd",
-               "sparse_attn_csr_size", "sparse_attn_csr_transpose"):
+               "sparse_attn_csr_size", "sparse_attn_csr_transpose", "sparse_attn_indexer_grad_kl_workspace_size",
+               "sparse_attn_indexer_grad_kl", "sparse_attn_indexer_grad_kl_timed"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -298,3 +316,74 @@ def sparse_attn_csr_transpose(desc: SaDesc, topk_indices: torch.Tensor, cu_seqle
                                          _stream(stream)))
     n_valid = int(row_ptr[-1].item())
     return row_ptr, entries[:n_valid]
+
+
+# ---- sparse lightning-indexer gradient with the KL loss --------------------
+
+def make_indexer_desc(wl: W.Workload, **over) -> SaIndexerDesc:
+    """Descriptor of an indexer workload (n_q_heads indexer heads, d_qk head dim)."""
+    d = SaIndexerDesc()
+    if wl.layout == W.LAYOUT_BSND:
+        d.layout, d.batch = W.LAYOUT_BSND, wl.batch
+        d.seqlen_q = d.seqlen_kv = wl.seqlens[0]
+    else:
+        d.layout, d.batch = W.LAYOUT_TND, wl.batch
+        d.total_q = d.total_kv = wl.total_q
+    d.n_heads, d.d, d.topk, d.mask_causal = wl.n_q_heads, wl.d_qk, wl.topk, 1
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def indexer_device_tensors(inputs: Dict[str, object], device="cuda") -> Dict[str, torch.Tensor]:
+    """Move an indexer generator dict to the device under the C ABI's names."""
+    wl = inputs["workload"]
+    out = {"q": inputs["q_idx"].to(device).contiguous(), "k": inputs["k_idx"].to(device).contiguous(),
+           "weights": inputs["weights"].to(device).contiguous(),
+           "topk_indices": inputs["idx"].to(device).contiguous(),
+           "target": inputs["target"].to(device).contiguous()}
+    if wl.layout == W.LAYOUT_TND:
+        out["cu_seqlens_q"] = inputs["cu_seqlens"].to(device)
+        out["cu_seqlens_kv"] = inputs["cu_seqlens"].to(device)
+    return out
+
+
+def sparse_attn_indexer_grad_kl_workspace_size(desc: SaIndexerDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check("sparse_attn_indexer_grad_kl_workspace_size",
+           load().sparse_attn_indexer_grad_kl_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def sparse_attn_indexer_grad_kl(desc: SaIndexerDesc, tensors: Dict[str, torch.Tensor],
+                                outputs: Optional[Dict[str, torch.Tensor]] = None,
+                                workspace: Optional[torch.Tensor] = None, stream=None,
+                                events=None) -> Dict[str, torch.Tensor]:
+    """Enqueue the indexer gradient; returns dq, dk (bf16), dweights,
+    loss_per_token and loss (fp32)."""
+    lib = load()
+    q, k = tensors["q"], tensors["k"]
+    dev = q.device
+    if outputs is None:
+        T = q.shape[0]
+        outputs = {"dq": torch.empty_like(q), "dk": torch.empty_like(k),
+                   "dweights": torch.empty((T, desc.n_heads), dtype=torch.float32, device=dev),
+                   "loss": torch.empty(1, dtype=torch.float32, device=dev),
+                   "loss_per_token": torch.empty(T, dtype=torch.float32, device=dev)}
+    need = sparse_attn_indexer_grad_kl_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    a = SaIndexerArgs()
+    for name in ("q", "k", "weights", "topk_indices", "target", "cu_seqlens_q", "cu_seqlens_kv"):
+        setattr(a, name, _ptr(tensors.get(name)))
+    for name in ("dq", "dk", "dweights", "loss", "loss_per_token"):
+        setattr(a, name, _ptr(outputs.get(name)))
+    if events is None:
+        _check("sparse_attn_indexer_grad_kl",
+               lib.sparse_attn_indexer_grad_kl(ctypes.byref(desc), ctypes.byref(a), _ptr(workspace),
+                                               workspace.numel(), _stream(stream)))
+    else:
+        _check("sparse_attn_indexer_grad_kl_timed",
+               lib.sparse_attn_indexer_grad_kl_timed(ctypes.byref(desc), ctypes.byref(a), _ptr(workspace),
+                                                     workspace.numel(), _stream(stream), events[0], events[1]))
+    return outputs

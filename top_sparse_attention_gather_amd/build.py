@@ -20,7 +20,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libsparse_attn.so")
 
 SOURCES = ["sa_api.hip", "sa_bwd_rows.hip", "sa_bwd_mla.hip", "sa_bwd_blk.hip", "sa_fwd_rows.hip", "sa_csr.hip",
-           "sa_reduce.hip"]
+           "sa_reduce.hip", "sa_indexer.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

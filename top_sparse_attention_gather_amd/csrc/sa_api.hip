@@ -226,9 +226,190 @@ sa_status_t check_inputs(const sa_desc_t* d, const void* q, const void* k, const
   return SA_OK;
 }
 
+// ---- sparse lightning-indexer gradient ---------------------------------------
+
+long long idx_total_q(const sa_indexer_desc_t* d) {
+  return d->layout == SA_LAYOUT_BSND ? (long long)d->batch * d->seqlen_q : (long long)d->total_q;
+}
+
+long long idx_rows_kv(const sa_indexer_desc_t* d) {
+  return d->layout == SA_LAYOUT_BSND ? (long long)d->batch * d->seqlen_kv : (long long)d->total_kv;
+}
+
+Params make_idx_params(const sa_indexer_desc_t* d) {
+  Params p;
+  std::memset(&p, 0, sizeof(p));
+  p.T = (int)idx_total_q(d);
+  p.Hq = d->n_heads;
+  p.Hkv = 1;
+  p.G = d->n_heads;
+  p.dqk = d->d;
+  p.dv = d->d;
+  p.topk = d->topk;
+  p.bs = 1;
+  p.select = SA_SEL_TOKEN;
+  p.causal = d->mask_causal;
+  p.cmp_ratio = 1;
+  p.layout = d->layout;
+  p.B = d->batch;
+  p.Sq = d->seqlen_q;
+  p.Skv = d->seqlen_kv;
+  p.scale = 1.f;
+  return p;
+}
+
+sa_status_t validate_idx(const sa_indexer_desc_t* d) {
+  if (!d) return SA_ERR_NULL_PTR;
+  if (d->layout != SA_LAYOUT_BSND && d->layout != SA_LAYOUT_TND) return SA_ERR_BAD_ARG;
+  if (d->mask_causal != 0 && d->mask_causal != 1) return SA_ERR_BAD_ARG;
+  if (d->batch < 1 || d->n_heads < 1 || d->d < 1 || d->topk < 1) return SA_ERR_BAD_SHAPE;
+  if (d->layout == SA_LAYOUT_BSND) {
+    if (d->seqlen_q < 0 || d->seqlen_kv < 0) return SA_ERR_BAD_SHAPE;
+  } else {
+    if (d->total_q < 0 || d->total_kv < 0) return SA_ERR_BAD_SHAPE;
+  }
+  const long long T = idx_total_q(d);
+  if (T > 0 && idx_rows_kv(d) < 1) return SA_ERR_BAD_SHAPE;
+  if (idx_rows_kv(d) >= (1LL << 30) || T >= (1LL << 31)) return SA_ERR_BAD_SHAPE;
+  if (!sa::idx_grad_supported(make_idx_params(d))) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+
+struct IdxLayout {
+  size_t loss_tok, blk_base, row_ptr, entries, csr_ws, partial, dump, acc, total;
+  int Tc;
+};
+
+IdxLayout idx_layout(const sa_indexer_desc_t* d) {
+  IdxLayout L;
+  std::memset(&L, 0, sizeof(L));
+  const size_t T = (size_t)idx_total_q(d), K = (size_t)d->topk, D = (size_t)d->d;
+  const long long nk = idx_rows_kv(d);
+  const size_t per_token = K * D * sizeof(uint16_t);   // bf16 partial rows
+  L.Tc = (int)std::min<size_t>(std::max<size_t>(T, 1), std::max<size_t>(1, kPartialCap / per_token));
+  size_t off = 0;
+  L.loss_tok = off;
+  off += align_up(T * sizeof(float));
+  L.blk_base = off;
+  off += align_up((size_t)(d->batch + 1) * 4);
+  L.row_ptr = off;
+  off += align_up((size_t)(nk + 1) * 4);
+  L.entries = off;
+  off += align_up((size_t)L.Tc * K * 4);
+  L.csr_ws = off;
+  off += align_up(sa::csr_workspace_bytes((long long)L.Tc * (long long)K, nk, d->batch));
+  L.partial = off;
+  off += align_up((size_t)L.Tc * per_token);
+  L.dump = off;
+  off += align_up(D * sizeof(uint16_t));
+  L.acc = off;
+  off += align_up((size_t)nk * D * sizeof(float));
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
+
+sa_status_t sparse_attn_indexer_grad_kl_workspace_size(const sa_indexer_desc_t* desc, size_t* bytes) {
+  if (!bytes) return SA_ERR_NULL_PTR;
+  const sa_status_t st = validate_idx(desc);
+  if (st != SA_OK) return st;
+  *bytes = idx_layout(desc).total;
+  return SA_OK;
+}
+
+sa_status_t sparse_attn_indexer_grad_kl_timed(const sa_indexer_desc_t* desc, const sa_indexer_args_t* a,
+                                              void* workspace, size_t workspace_bytes, void* stream,
+                                              void* ev_main_start, void* ev_main_stop) {
+  size_t need = 0;
+  sa_status_t st = sparse_attn_indexer_grad_kl_workspace_size(desc, &need);
+  if (st != SA_OK) return st;
+  if (!a) return SA_ERR_NULL_PTR;
+  if (idx_total_q(desc) == 0) return SA_OK;   // empty query: nothing to do
+  if (!a->q || !a->k || !a->weights || !a->topk_indices || !a->target || !a->dq || !a->dk || !a->dweights ||
+      !a->loss)
+    return SA_ERR_NULL_PTR;
+  if (desc->layout == SA_LAYOUT_TND && (!a->cu_seqlens_q || !a->cu_seqlens_kv)) return SA_ERR_NULL_PTR;
+  if (!workspace) return SA_ERR_NULL_PTR;
+  if (workspace_bytes < need) return SA_ERR_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return SA_ERR_MISALIGNED;
+  if (!aligned16(a->q) || !aligned16(a->k)) return SA_ERR_MISALIGNED;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const IdxLayout L = idx_layout(desc);
+  Params p = make_idx_params(desc);
+  p.k = static_cast<const bf16*>(a->k);
+  p.q = static_cast<const bf16*>(a->q);
+  p.idx = a->topk_indices;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_kv = a->cu_seqlens_kv;
+
+  sa::IdxArgs ia;
+  std::memset(&ia, 0, sizeof(ia));
+  ia.q = p.q;
+  ia.k = p.k;
+  ia.w = a->weights;
+  ia.target = a->target;
+  ia.dq = static_cast<bf16*>(a->dq);
+  ia.dw = a->dweights;
+  ia.loss_tok = a->loss_per_token ? a->loss_per_token : reinterpret_cast<float*>(ws + L.loss_tok);
+  ia.part = reinterpret_cast<bf16*>(ws + L.partial);
+  ia.dump = reinterpret_cast<bf16*>(ws + L.dump);
+  ia.H = desc->n_heads;
+
+  int* blk_base = reinterpret_cast<int*>(ws + L.blk_base);
+  int* row_ptr = reinterpret_cast<int*>(ws + L.row_ptr);
+  int* entries = reinterpret_cast<int*>(ws + L.entries);
+  float* acc = reinterpret_cast<float*>(ws + L.acc);
+  const long long nk = idx_rows_kv(desc);
+  sa::ReduceArgs r;
+  std::memset(&r, 0, sizeof(r));
+  r.partial = ia.part;
+  r.partial_bf16 = 1;
+  r.RW = desc->d;
+  r.npos = desc->topk;
+  r.n_hc = 1;
+  r.row_ptr = row_ptr;
+  r.entries = entries;
+  r.blk_base = blk_base;
+  r.n_kv_out = nk;
+  r.n_out_rows = nk;
+  r.acc = acc;
+  bool first = true;
+  for (int t0 = 0; t0 < p.T; t0 += L.Tc) {
+    const int t1 = std::min(p.T, t0 + L.Tc);
+    SA_TRY_HIP(sa::launch_csr_transpose(p, t0, t1, nk, blk_base, row_ptr, entries, ws + L.csr_ws, s));
+    ia.t0 = t0;
+    ia.Tc = t1 - t0;
+    if (ev_main_start && first) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
+    SA_TRY_HIP(sa::launch_idx_grad(p, ia, s));
+    if (ev_main_stop && t1 == p.T) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
+    r.t0 = t0;
+    r.Tc = t1 - t0;
+    r.accumulate = first ? 0 : 1;
+    SA_TRY_HIP(sa::launch_reduce(p, r, s));
+    first = false;
+  }
+  SA_TRY_HIP(sa::launch_cast_bf16(acc, static_cast<bf16*>(a->dk), (size_t)nk * desc->d, s));
+  // loss = fixed-order sum of the per-token losses (the dSinks reduction
+  // over one "head")
+  Params pl = p;
+  pl.Hq = 1;
+  BwdBuffers wl;
+  std::memset(&wl, 0, sizeof(wl));
+  wl.sink_term = ia.loss_tok;
+  wl.dsinks = a->loss;
+  SA_TRY_HIP(sa::launch_dsinks(pl, wl, s));
+  return SA_OK;
+}
+
+sa_status_t sparse_attn_indexer_grad_kl(const sa_indexer_desc_t* desc, const sa_indexer_args_t* args,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_attn_indexer_grad_kl_timed(desc, args, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
 
 sa_status_t sparse_attn_bwd_workspace_size(const sa_desc_t* desc, size_t* bytes) {
   if (!bytes) return SA_ERR_NULL_PTR;

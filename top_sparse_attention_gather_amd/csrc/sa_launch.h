@@ -115,6 +115,25 @@ long long scan_bsum_ints(long long n);
 bool blk_dq_supported(const Params& p);
 hipError_t launch_blk_dq(const Params& p, const BwdBuffers& w, hipStream_t s);
 
+// Sparse lightning-indexer gradient with the KL loss (d = 128, up to 64
+// heads, up to 2048 slots per token, one kv row table).  Tokens [t0, t0 +
+// Tc) write their dq~, dW and loss, and one bf16 partial dK~ row per
+// (token, slot) to part[(t - t0) * topk + slot][128].
+struct IdxArgs {
+  const bf16* q;         // [T][H][128]
+  const bf16* k;         // [T_kv][128]
+  const float* w;        // [T][H]
+  const float* target;   // [T][topk]
+  bf16* dq;              // [T][H][128]
+  float* dw;             // [T][H]
+  float* loss_tok;       // [T]
+  bf16* part;
+  bf16* dump;            // >= 256 bytes, never read
+  int H, t0, Tc;
+};
+bool idx_grad_supported(const Params& p);
+hipError_t launch_idx_grad(const Params& p, const IdxArgs& a, hipStream_t s);
+
 // Shared-KV 576/512 backward with 64 heads per workgroup (bf16 partials).
 bool mla_bwd_supported(const Params& p);
 int mla_bwd_head_groups(const Params& p);
