@@ -143,12 +143,105 @@ def cpu_baseline(inputs, wl, budget_s: float = 15.0, min_tokens: int = 8):
                       f"({flops / 1e12:.3f} TFLOP in {spent:.1f} s, forward excluded)"}
 
 
+def indexer_cpu_baseline(inputs, wl, budget_s: float = 15.0, min_tokens: int = 8):
+    """The fp64 oracle indexer gradient on the last tokens, as many as fit
+    the time budget; TFLOP/s of that sample."""
+    from oracle import sparse_attn_oracle as O   # the oracle is only timed here
+    try:
+        import threadpoolctl
+        threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    T = wl.total_q
+    idx = inputs["idx"].numpy()
+    done, flops, spent, chunk = 0, 0, 0.0, min_tokens
+    while spent < budget_s and done < T:
+        toks = list(range(T - done - chunk, T - done))
+        t0 = time.perf_counter()
+        O.indexer_grad_kl(inputs, tokens=toks)
+        spent += time.perf_counter() - t0
+        flops += int((idx[toks] >= 0).sum()) * 6 * wl.n_q_heads * wl.d_qk
+        done += chunk
+        chunk = min(2 * chunk, 64)
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle indexer_grad_kl on the last {done} of {T} query tokens of {wl.name} "
+                      f"({flops / 1e12:.4f} TFLOP in {spent:.1f} s)"}
+
+
+def bench_indexer(args):
+    """Sparse lightning-indexer gradient with the KL loss: one step = one
+    sparse_attn_indexer_grad_kl call (CSR, the per-token kernel, the dK~
+    reduction and cast, the loss sum).  FLOP: the three products S~ = q~K~^T,
+    dq~ = dS~K~ and dK~ = dS~^T q~, 2 H d each per valid (token, row)."""
+    wl = W.INDEXER_WORKLOADS[args.workload]
+    log(f"[bench] workload {wl.name}: generating inputs")
+    inputs = W.make_indexer_inputs(wl, threads=16)
+    idx = inputs["idx"].numpy()
+    pairs = int((idx >= 0).sum())
+    H, d, T, K = wl.n_q_heads, wl.d_qk, wl.total_q, wl.topk
+    flop = pairs * 6 * H * d
+    dev = B.indexer_device_tensors(inputs)
+    desc = B.make_indexer_desc(wl)
+    outputs = {"dq": torch.empty_like(dev["q"]), "dk": torch.empty_like(dev["k"]),
+               "dweights": torch.empty((T, H), dtype=torch.float32, device="cuda"),
+               "loss": torch.empty(1, dtype=torch.float32, device="cuda"),
+               "loss_per_token": torch.empty(T, dtype=torch.float32, device="cuda")}
+    ws = torch.empty(max(B.sparse_attn_indexer_grad_kl_workspace_size(desc), 256), dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        B.sparse_attn_indexer_grad_kl(desc, dev, outputs, ws)
+    torch.cuda.synchronize()
+    ev = B.HipEvents(args.steps)
+    stream = torch.cuda.current_stream()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        B.sparse_attn_indexer_grad_kl(desc, dev, outputs, ws, stream=stream, events=ev.pairs[i])
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_stop) / args.steps
+    kern_ms = float(np.mean([ev.elapsed_ms(i) for i in range(args.steps)]))
+    ev.close()
+    for k, v in outputs.items():
+        if not torch.isfinite(v.float()).all():
+            raise RuntimeError(f"non-finite values in {k}")
+    tflops = flop / (ms * 1e-3) / 1e12
+    # the per-token kernel's HBM bytes: q~, W, target, indices read once;
+    # dq~, dW and the bf16 partial dK~ rows written (the gathered K~ rows,
+    # 2 MB in all, are served from L2)
+    nbytes = T * H * d * 2 + T * H * 4 + T * K * 8 + T * H * d * 2 + T * H * 4 + pairs * d * 2
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    ktf = flop / (kern_ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.3f} ms/step, kernel {kern_ms:.3f} ms ({gbs:.0f} GB/s, {ktf:.1f} TFLOP/s)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = indexer_cpu_baseline(inputs, wl, budget_s=args.cpu_budget)
+    line = {
+        "metric": "sparse lightning-indexer grad + KL loss TFLOP/s (selected-row FLOPs), 1 GPU",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B={wl.batch} S={wl.seqlens[0]} indexer heads={H} d={d} top-{K}",
+                   "valid_pairs": pairs, "selected_row_tflop": round(flop / 1e12, 4),
+                   "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "parallelism": "single GPU"},
+        "roofline": {"kernel": "idx_grad_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
+                     "mfma_tflops": round(ktf, 2), "traffic": None, "kernel_ms": round(kern_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mla_token_8k", choices=W.WORKLOAD_ORDER)
+    ap.add_argument("--workload", default="mla_token_8k",
+                    choices=W.WORKLOAD_ORDER + list(W.INDEXER_WORKLOADS))
     ap.add_argument("--dkv-mode", default="deterministic", choices=["atomic", "deterministic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--softmax-l1", action="store_true",
@@ -174,6 +267,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
         return
 
+    if args.workload in W.INDEXER_WORKLOADS:
+        bench_indexer(args)
+        return
     wl = W.WORKLOADS[args.workload]
     mode = B.DKV_ATOMIC if args.dkv_mode == "atomic" else B.DKV_DETERMINISTIC
     log(f"[bench] workload {wl.name}: generating inputs")
