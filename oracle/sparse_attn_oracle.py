@@ -54,7 +54,8 @@ design notes):
       a masked key is simply absent;
   R7  index i names rows [i * block_size, (i + 1) * block_size);
   R8  any negative index is an unused slot; an index >= the sequence's row
-      count is also unused;
+      count is also unused; with per-row top-k lengths, slots at or past the
+      row's length are unused (lengths clamped to [0, K]);
   R9  duplicate indices form a multiset: each slot is its own softmax term
       and its own scatter;
   R10 a row with no valid key and no sink has lse = -inf, O = 0 and no
@@ -119,6 +120,11 @@ class Problem:
         self.cmp_kv = inputs.get("cmp_kv")
         self.sinks = inputs.get("sinks")
         self.idx = inputs["idx"].numpy()
+        # optional selectable slots per (token, kv head): slots at or past
+        # the length are unused (SparseFlashMlaGrad README, parameter table:
+        # the per-row top-k lengths)
+        tl = inputs.get("topk_len")
+        self.topk_len = None if tl is None else np.clip(np.asarray(tl, np.int64), 0, self.idx.shape[2])
         self.cu = inputs["cu_seqlens"].numpy().astype(np.int64)
         self.cu_cmp = inputs["cu_seqlens_cmp"].numpy().astype(np.int64)
         self.T = int(self.cu[-1])
@@ -141,6 +147,9 @@ class Problem:
         are the columns of the softmax L1-norm outputs."""
         b = int(self.seq_of[t])
         tl = t - int(self.cu[b])                  # position within the sequence
+        K = self.idx.shape[2]
+        n_sel = K if self.topk_len is None else int(self.topk_len[t, g])
+        usable = np.arange(K) < n_sel             # slots inside the row's length
         n_kv = int(self.cu[b + 1] - self.cu[b])   # Sq = Skv per sequence here
         base = int(self.cu[b])
         if self.select == SEL_TOKEN:
@@ -148,13 +157,14 @@ class Problem:
             keep = (j >= 0) & (j < n_kv)
             if self.causal:
                 keep &= j <= tl
+            keep &= usable
             rows = base + j[keep]
             return np.zeros(rows.size, dtype=np.int64), rows, np.flatnonzero(keep)
         if self.select == SEL_BLOCK:
             bs = self.block_size
             blk = self.idx[t, g].astype(np.int64)
-            slots = np.flatnonzero(blk >= 0)
-            blk = blk[blk >= 0]
+            slots = np.flatnonzero((blk >= 0) & usable)
+            blk = blk[slots]
             j = (blk[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)   # block-major
             keep = j < n_kv
             if self.causal:
@@ -174,6 +184,7 @@ class Problem:
         keepc = (j >= 0) & (j < n_cmp)
         if self.causal:
             keepc &= r * j + r - 1 <= tl
+        keepc &= usable
         cmp = int(self.cu_cmp[b]) + j[keepc]
         srcs = np.concatenate([np.zeros(ori.size, np.int64), np.ones(cmp.size, np.int64)])
         pos = np.concatenate([np.flatnonzero(keep), w.size + np.flatnonzero(keepc)])
@@ -476,6 +487,8 @@ def entry_keys(pb: Problem) -> np.ndarray:
         n_cmp = np.diff(pb.cu_cmp)[pb.seq_of][:, None, None]
         ok = (j >= 0) & (j < n_cmp) & ((r * j + r - 1 <= tl) if pb.causal else True)
         key = (pb.cu_cmp[pb.seq_of][:, None, None] + j) * Hkv + g
+    if pb.topk_len is not None:
+        ok &= np.arange(K)[None, None, :] < pb.topk_len[:, :, None]
     return np.where(ok, key, -1).reshape(-1)
 
 

@@ -42,6 +42,8 @@ MUTATIONS = {
     "idx_reverse_kl": ("loss_t[t] = float((p[nz] * (np.log(p[nz]) - logs[nz])).sum())",
                        "loss_t[t] = float((s_[nz] * (logs[nz] - np.log(p[nz]))).sum())"),
     "idx_slot_not_position": ("p = P[t, pos]", "p = P[t, :pos.size]"),
+    # per-row top-k lengths
+    "len_off_by_one": ("usable = np.arange(K) < n_sel", "usable = np.arange(K) <= n_sel"),
 }
 
 
@@ -136,6 +138,18 @@ def test_pins_catch_planted_mistake(name):
                 caught.append(True)
     elif name == "csr_unstable":
         caught.append(not _csr_ok(mod, "token_gqa"))
+    elif name.startswith("len_"):
+        from tests.test_oracle_pins import test_per_row_topk_lengths
+        for m in ("token_gqa", "block_gqa", "wcmp_sinks"):
+            saved = O.Problem
+            O.Problem = mod.Problem     # the pin builds problems through the module under test
+            try:
+                test_per_row_topk_lengths(m)
+                caught.append(False)
+            except AssertionError:
+                caught.append(True)
+            finally:
+                O.Problem = saved
     elif name in ("causal_off_by_one", "window_short"):
         caught.append(not _selection_ok(mod, "token_gqa" if name == "causal_off_by_one" else "wcmp_sinks"))
     else:

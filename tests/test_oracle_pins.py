@@ -206,8 +206,12 @@ def test_global_gradient_sums(mode):
             np.testing.assert_allclose(g["dv"][:, gi].sum(0), dv_sum, atol=1e-12)
 
 
-def _brute_selection(wl, idx, t, g):
-    """Rows selected by (t, g) from the rules, by plain loops (multiset)."""
+def _brute_selection(wl, idx, t, g, lens=None):
+    """Rows selected by (t, g) from the rules, by plain loops (multiset);
+    with `lens`, only slots below lens[t, g] count."""
+    if lens is not None:
+        idx = idx.copy()
+        idx[t, g, max(0, int(lens[t, g])):] = -1
     cu = wl.cu_seqlens()
     b = int(np.searchsorted(cu, t, side="right") - 1)
     tl = t - int(cu[b])
@@ -321,3 +325,39 @@ def test_empty_row_has_no_gradient():
     g = O.sparse_bwd(pb, Ob, Lb)
     assert np.all(g["dq"][3] == 0)
     assert all(np.isfinite(v).all() for v in g.values())
+
+
+@pytest.mark.parametrize("mode", ["token_gqa", "block_gqa", "wcmp_sinks"])
+def test_per_row_topk_lengths(mode):
+    """Per-row top-k lengths: slots at or past a row's length are unused.
+    Pinned by plain loops, and by the equivalence with writing -1 into those
+    slots (selection, CSR, forward and backward all identical)."""
+    wl = tiny(mode)
+    inp = to_f64_inputs(W.make_inputs(wl))
+    idx = inp["idx"].numpy()
+    rng = np.random.default_rng(9)
+    lens = rng.integers(-1, idx.shape[2] + 2, size=idx.shape[:2])      # includes < 0 and > K
+    with_len = dict(inp, topk_len=lens)
+    masked = dict(inp)
+    midx = idx.copy()
+    for t in range(idx.shape[0]):
+        for g in range(idx.shape[1]):
+            midx[t, g, max(0, int(lens[t, g])):] = -1
+    masked["idx"] = torch.from_numpy(midx)
+    pa, pm = O.Problem(with_len), O.Problem(masked)
+    for t in range(wl.total_q):
+        for g in range(wl.n_kv_heads):
+            sa, ra, qa = pa.selection_positions(t, g)
+            sm_, rm, qm = pm.selection_positions(t, g)
+            assert np.array_equal(sa, sm_) and np.array_equal(ra, rm) and np.array_equal(qa, qm)
+            got = sorted(zip(sa.tolist(), ra.tolist()))
+            assert got == _brute_selection(wl, idx, t, g, lens), (t, g)
+    for x, y in zip(O.csr_transpose(pa), O.csr_transpose(pm)):
+        assert np.array_equal(x, y)
+    oa, la = O.sparse_fwd(pa)
+    om, lm = O.sparse_fwd(pm)
+    assert np.array_equal(oa, om) and np.array_equal(la, lm)
+    ga = O.sparse_bwd(pa, torch.from_numpy(oa), torch.from_numpy(la))
+    gm = O.sparse_bwd(pm, torch.from_numpy(om), torch.from_numpy(lm))
+    for k in ga:
+        assert np.array_equal(ga[k], gm[k]), k
