@@ -127,7 +127,9 @@ typedef struct sa_desc {
 /* Device pointers for the backward.  Unused fields may be NULL.
  * Separate K/V: k, v in; dk, dv out.  Shared KV: kv in; dkv out.
  * SA_SEL_WINDOW_CMP: kv (ori) and cmp_kv in; dkv and d_cmp_kv out, and
- * topk_indices index cmp_kv rows.  Sinks: sinks in, dsinks out. */
+ * topk_indices index cmp_kv rows.  With topk = 0 this is window-only
+ * attention: cmp_kv, cu_seqlens_cmp and topk_indices may be NULL, and
+ * d_cmp_kv too when total_cmp = 0.  Sinks: sinks in, dsinks out. */
 typedef struct sa_bwd_args {
   const void* q;
   const void* k;
@@ -167,6 +169,12 @@ typedef struct sa_bwd_args {
    * and every position of a set whose sum is 0 holds 0.  Deterministic. */
   float* ori_softmax_l1;
   float* cmp_softmax_l1;
+  /* Optional per-row top-k lengths [T, n_kv_heads] int32 (SparseFlashMlaGrad
+   * README, parameter table: the selectable top-k length of each query row):
+   * index slots at or past a row's length are unused; values are clamped
+   * to [0, topk].  NULL: every slot may be used.  In SA_SEL_WINDOW_CMP they
+   * limit the cmp slots; the window is not affected. */
+  const int32_t* topk_lengths;
 } sa_bwd_args_t;
 
 /* Device pointers for the forward (o, lse out; the rest as above). */
@@ -183,6 +191,7 @@ typedef struct sa_fwd_args {
   const int32_t* cu_seqlens_cmp;
   void* o;
   float* lse;
+  const int32_t* topk_lengths;   /* as in sa_bwd_args_t (NULL: all slots) */
 } sa_fwd_args_t;
 
 /* Phase 1 of the backward: validates `desc` (host only, no HIP call) and

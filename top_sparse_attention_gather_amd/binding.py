@@ -44,13 +44,13 @@ class SaBwdArgs(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "q", "k", "v", "kv", "cmp_kv", "o", "d_o", "lse", "sinks", "topk_indices", "cu_seqlens_q",
         "cu_seqlens_kv", "cu_seqlens_cmp", "dq", "dk", "dv", "dkv", "d_cmp_kv", "dsinks", "ori_softmax_l1",
-        "cmp_softmax_l1")]
+        "cmp_softmax_l1", "topk_lengths")]
 
 
 class SaFwdArgs(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "q", "k", "v", "kv", "cmp_kv", "sinks", "topk_indices", "cu_seqlens_q", "cu_seqlens_kv",
-        "cu_seqlens_cmp", "o", "lse")]
+        "cu_seqlens_cmp", "o", "lse", "topk_lengths")]
 
 
 class SaIndexerDesc(ctypes.Structure):
@@ -166,7 +166,7 @@ def alloc_bwd_outputs(desc: SaDesc, tensors: Dict[str, torch.Tensor]) -> Dict[st
     else:
         out["dk"] = torch.empty_like(tensors["k"])
         out["dv"] = torch.empty_like(tensors["v"])
-    if desc.select == W.SEL_WINDOW_CMP:
+    if desc.select == W.SEL_WINDOW_CMP and desc.total_cmp > 0:
         out["d_cmp_kv"] = torch.empty_like(tensors["cmp_kv"])
     if desc.has_sinks:
         out["dsinks"] = torch.empty(desc.n_q_heads, dtype=torch.float32, device=dev)
@@ -179,7 +179,7 @@ def alloc_bwd_outputs(desc: SaDesc, tensors: Dict[str, torch.Tensor]) -> Dict[st
         else:
             n_ori = desc.win_left + 1 + desc.win_right
         out["ori_softmax_l1"] = torch.empty((T, desc.n_kv_heads, n_ori), dtype=torch.float32, device=dev)
-        if desc.select == W.SEL_WINDOW_CMP:
+        if desc.select == W.SEL_WINDOW_CMP and desc.topk > 0:
             out["cmp_softmax_l1"] = torch.empty((T, desc.n_kv_heads, desc.topk), dtype=torch.float32, device=dev)
     return out
 
@@ -200,7 +200,7 @@ def sparse_attn_bwd(desc: SaDesc, tensors: Dict[str, torch.Tensor], outputs: Opt
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=tensors["q"].device)
     a = SaBwdArgs()
     for name in ("q", "k", "v", "kv", "cmp_kv", "o", "d_o", "lse", "sinks", "topk_indices", "cu_seqlens_q",
-                 "cu_seqlens_kv", "cu_seqlens_cmp"):
+                 "cu_seqlens_kv", "cu_seqlens_cmp", "topk_lengths"):
         setattr(a, name, _ptr(tensors.get(name)))
     for name in ("dq", "dk", "dv", "dkv", "d_cmp_kv", "dsinks", "ori_softmax_l1", "cmp_softmax_l1"):
         setattr(a, name, _ptr(outputs.get(name)))
@@ -256,7 +256,7 @@ def sparse_attn_fwd(desc: SaDesc, tensors: Dict[str, torch.Tensor], o: Optional[
         lse = torch.empty((T, desc.n_q_heads), dtype=torch.float32, device=q.device)
     a = SaFwdArgs()
     for name in ("q", "k", "v", "kv", "cmp_kv", "sinks", "topk_indices", "cu_seqlens_q", "cu_seqlens_kv",
-                 "cu_seqlens_cmp"):
+                 "cu_seqlens_cmp", "topk_lengths"):
         setattr(a, name, _ptr(tensors.get(name)))
     a.o, a.lse = _ptr(o), _ptr(lse)
     _check("sparse_attn_fwd", lib.sparse_attn_fwd(ctypes.byref(desc), ctypes.byref(a), _stream(stream)))
@@ -279,6 +279,8 @@ def device_tensors(inputs: Dict[str, object], device="cuda") -> Dict[str, torch.
         if k in inputs:
             out[k] = inputs[k].to(device).contiguous()
     out["topk_indices"] = inputs["idx"].to(device).contiguous()
+    if inputs.get("topk_len") is not None:
+        out["topk_lengths"] = torch.as_tensor(inputs["topk_len"], dtype=torch.int32).to(device).contiguous()
     if wl.layout == W.LAYOUT_TND:
         out["cu_seqlens_q"] = inputs["cu_seqlens"].to(device)
         out["cu_seqlens_kv"] = inputs["cu_seqlens"].to(device)

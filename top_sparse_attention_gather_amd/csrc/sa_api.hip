@@ -218,7 +218,8 @@ sa_status_t check_inputs(const sa_desc_t* d, const void* q, const void* k, const
   if (d->kv_shared ? !kv : (!k || !v)) return SA_ERR_NULL_PTR;
   if (d->topk > 0 && !idx) return SA_ERR_NULL_PTR;
   if (d->layout == SA_LAYOUT_TND && (!cu_q || !cu_kv)) return SA_ERR_NULL_PTR;
-  if (d->select == SA_SEL_WINDOW_CMP && (!cmp_kv || !cu_cmp)) return SA_ERR_NULL_PTR;
+  // window+cmp: the cmp table is only read through index slots
+  if (d->select == SA_SEL_WINDOW_CMP && d->topk > 0 && (!cmp_kv || !cu_cmp)) return SA_ERR_NULL_PTR;
   if (d->has_sinks && !sinks) return SA_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(d->kv_shared ? kv : k) || (!d->kv_shared && !aligned16(v)) ||
       (cmp_kv && !aligned16(cmp_kv)))
@@ -433,7 +434,7 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   if (st != SA_OK) return st;
   if (!a->o || !a->d_o || !a->lse || !a->dq) return SA_ERR_NULL_PTR;
   if (desc->kv_shared ? !a->dkv : (!a->dk || !a->dv)) return SA_ERR_NULL_PTR;
-  if (desc->select == SA_SEL_WINDOW_CMP && !a->d_cmp_kv) return SA_ERR_NULL_PTR;
+  if (desc->select == SA_SEL_WINDOW_CMP && rows_cmp(desc) > 0 && !a->d_cmp_kv) return SA_ERR_NULL_PTR;
   if (desc->has_sinks && !a->dsinks) return SA_ERR_NULL_PTR;
   if (desc->softmax_l1) {
     if (!a->ori_softmax_l1 || (desc->select == SA_SEL_WINDOW_CMP && desc->topk > 0 && !a->cmp_softmax_l1))
@@ -461,7 +462,8 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   p.idx = a->topk_indices;
   p.cu_q = a->cu_seqlens_q;
   p.cu_kv = a->cu_seqlens_kv;
-  p.cu_cmp = a->cu_seqlens_cmp;
+  p.cu_cmp = desc->topk > 0 ? a->cu_seqlens_cmp : nullptr;
+  p.topk_len = a->topk_lengths;
 
   BwdBuffers w;
   std::memset(&w, 0, sizeof(w));
@@ -560,6 +562,8 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   r.n_kv_out = rows_kv(desc) * (long long)Hkv;
   r.n_out_rows = r.n_kv_out + rows_cmp(desc) * (long long)Hkv;
   r.acc = acc;
+  // no index slots (window only): every key list is empty
+  if (!has_slots) SA_TRY_HIP(sa::launch_fill_zero(reinterpret_cast<float*>(row_ptr), (size_t)(nk + 1), s));
   bool first = true;
   for (int t0 = 0; t0 < p.T; t0 += L.Tc) {
     const int t1 = std::min(p.T, t0 + L.Tc);
@@ -610,7 +614,8 @@ sa_status_t sparse_attn_fwd(const sa_desc_t* desc, const sa_fwd_args_t* a, void*
   p.idx = a->topk_indices;
   p.cu_q = a->cu_seqlens_q;
   p.cu_kv = a->cu_seqlens_kv;
-  p.cu_cmp = a->cu_seqlens_cmp;
+  p.cu_cmp = desc->topk > 0 ? a->cu_seqlens_cmp : nullptr;
+  p.topk_len = a->topk_lengths;
   SA_TRY_HIP(sa::launch_fwd_rows(p, static_cast<bf16*>(a->o), a->lse, reinterpret_cast<hipStream_t>(stream)));
   return SA_OK;
 }

@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void blk_dq_kernel(Params p, BwdBuffers w
   __shared__ int sW[4];
   bool ok = false;
   int blk = -1;
-  if (tid < p.topk) {
+  if (tid < row_len(p, row)) {
     blk = irow[tid];
     ok = blk >= 0 && (long long)blk * p.bs < sp.kv_len && (!p.causal || (long long)blk * p.bs <= sp.tl);
   }

@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
 
   // ---- compacted selection (positions and their row codes) --------------
   const int npos = n_positions(p);
-  const int cnt = compact_positions_batched<kMaxPos / 256>(p, s, irow, npos, sm.rows, sm.wave, sm.vpos);
+  const int cnt =
+      compact_positions_batched<kMaxPos / 256>(p, s, irow, npos, sm.rows, sm.wave, sm.vpos, row_len(p, row));
 
   // ---- lse / D of the wave's heads (phase-A layout: head = 16 wv + l16) ---
   const int hA = h0 + wv * 16 + l16;

@@ -112,9 +112,10 @@ __global__ __launch_bounds__(kThreads) void l1_norm_kernel(Params p, const float
   const int n_ori = p.select == kSelWindowCmp ? p.win_left + 1 + p.win_right : npos;
   const size_t plane = (size_t)p.T * p.Hkv * npos;
   const float* src = l1 + (size_t)row * npos;
+  const int len = row_len(p, row);
   auto value = [&](int pos) {
     float v = 0.f;
-    if (decode_position(p, s, irow, pos) >= 0)
+    if (decode_position(p, s, irow, pos, len) >= 0)
       for (int c = 0; c < n_hg; ++c) v += src[(size_t)c * plane + pos];
     return v;
   };
@@ -206,7 +207,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
   const int npos = n_positions(p);
   for (int pos0 = 0; pos0 < npos; pos0 += kMaxPos) {
     __syncthreads();
-    const int cnt = compact_positions(p, s, irow, pos0, min(kMaxPos, npos - pos0), sRows, sWave, sVpos);
+    const int cnt =
+        compact_positions(p, s, irow, pos0, min(kMaxPos, npos - pos0), sRows, sWave, sVpos, row_len(p, row));
     for (int k0 = 0; k0 < cnt; k0 += kNT) {
       // ---- gather the tile's K (and V) rows into LDS -----------------------
       for (int c = tid; c < kNT * (DQK / 8); c += kThreads) {

@@ -139,7 +139,9 @@ __global__ __launch_bounds__(kThreads) void slot_keys_kernel(Params p, long long
   const int row = (int)(slot / p.topk);
   const int t = row / p.Hkv, g = row - t * p.Hkv;
   const SeqPos s = seq_pos(p, t);
-  const int key = slot_key(p, s, g, p.idx[slot], blk_base, sentinel);
+  const int key = (int)(slot - (long long)row * p.topk) < row_len(p, row)
+                      ? slot_key(p, s, g, p.idx[slot], blk_base, sentinel)
+                      : sentinel;
   keys[i] = key;
   if (key != sentinel) atomicAdd(&counts[key], 1);
 }
@@ -163,7 +165,9 @@ __global__ __launch_bounds__(kThreads) void slot_keys_hist_kernel(Params p, long
     const int row = (int)(slot / p.topk);
     const int t = row / p.Hkv, g = row - t * p.Hkv;
     const SeqPos s = seq_pos(p, t);
-    const int key = slot_key(p, s, g, p.idx[slot], blk_base, sentinel);
+    const int key = (int)(slot - (long long)row * p.topk) < row_len(p, row)
+                        ? slot_key(p, s, g, p.idx[slot], blk_base, sentinel)
+                        : sentinel;
     keys[i] = key;
     if (key != sentinel) atomicAdd(&hist[key], 1);
   }

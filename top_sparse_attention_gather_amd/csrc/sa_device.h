@@ -42,6 +42,7 @@ struct Params {
   const int* cu_q;
   const int* cu_kv;
   const int* cu_cmp;
+  const int* topk_len;   // [T][Hkv] selectable slots per row, or null (all topk)
 };
 
 // Where a query token sits: its sequence, local position, and the first
@@ -68,7 +69,7 @@ __device__ __forceinline__ SeqPos seq_pos(const Params& p, int t) {
     s.kv_base = p.cu_kv[lo];
     s.kv_len = p.cu_kv[lo + 1] - p.cu_kv[lo];
   }
-  if (p.select == kSelWindowCmp) {
+  if (p.select == kSelWindowCmp && p.cu_cmp) {   // no cmp table without index slots
     s.cmp_base = p.cu_cmp[s.b];
     s.cmp_len = p.cu_cmp[s.b + 1] - p.cu_cmp[s.b];
   } else {
@@ -76,6 +77,14 @@ __device__ __forceinline__ SeqPos seq_pos(const Params& p, int t) {
     s.cmp_len = 0;
   }
   return s;
+}
+
+// Selectable index slots of row (token, kv head) = t * Hkv + g: all topk,
+// or the caller's per-row length clamped to [0, topk] (slots at or past it
+// are unused).
+__device__ __forceinline__ int row_len(const Params& p, int row) {
+  if (!p.topk_len) return p.topk;
+  return min(max(p.topk_len[row], 0), p.topk);
 }
 
 // Number of virtual positions of a (token, kv head) row before masking:
@@ -88,16 +97,19 @@ __device__ __forceinline__ int n_positions(const Params& p) {
 }
 
 // Decode virtual position `pos` of row (t, g): the encoded selected row, or
-// -1 when the slot is unused or masked.  `irow` points at idx[t][g][0].
+// -1 when the slot is unused or masked.  `irow` points at idx[t][g][0];
+// `len` is the row's selectable slot count (row_len).
 __device__ __forceinline__ int decode_position(const Params& p, const SeqPos& s,
-                                               const int* __restrict__ irow, int pos) {
+                                               const int* __restrict__ irow, int pos, int len = 0x7fffffff) {
   if (p.select == kSelToken) {
+    if (pos >= len) return -1;
     int j = irow[pos];
     if (j < 0 || j >= s.kv_len || (p.causal && j > s.tl)) return -1;
     return s.kv_base + j;
   }
   if (p.select == kSelBlock) {
     int slot = pos / p.bs;
+    if (slot >= len) return -1;
     int blk = irow[slot];
     if (blk < 0) return -1;
     long long j = (long long)blk * p.bs + (pos - slot * p.bs);
@@ -110,6 +122,7 @@ __device__ __forceinline__ int decode_position(const Params& p, const SeqPos& s,
     if (j < 0 || j >= s.kv_len || (p.causal && j > s.tl)) return -1;
     return s.kv_base + j;
   }
+  if (pos - nwin >= len) return -1;
   int j = irow[pos - nwin];
   if (j < 0 || j >= s.cmp_len) return -1;
   if (p.causal && (long long)p.cmp_ratio * j + p.cmp_ratio - 1 > s.tl) return -1;
@@ -122,13 +135,14 @@ __device__ __forceinline__ int decode_position(const Params& p, const SeqPos& s,
 // stores each used position's index.  Ends with a barrier.
 __device__ __forceinline__ int compact_positions(const Params& p, const SeqPos& s,
                                                  const int* __restrict__ irow, int pos0, int n,
-                                                 int* sRows, int* sWave, int* sVpos = nullptr) {
+                                                 int* sRows, int* sWave, int* sVpos = nullptr,
+                                                 int len = 0x7fffffff) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int total = 0;
   for (int base = 0; base < n; base += 256) {
     const int pos = base + tid;
     int code = -1;
-    if (pos < n) code = decode_position(p, s, irow, pos0 + pos);
+    if (pos < n) code = decode_position(p, s, irow, pos0 + pos, len);
     const unsigned long long m = __ballot(code >= 0);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
     if (lane == 0) sWave[w] = __popcll(m);
@@ -151,13 +165,13 @@ __device__ __forceinline__ int compact_positions(const Params& p, const SeqPos& 
 template <int ROUNDS>
 __device__ __forceinline__ int compact_positions_batched(const Params& p, const SeqPos& s,
                                                          const int* __restrict__ irow, int n, int* sRows,
-                                                         int* sWave, int* sVpos) {
+                                                         int* sWave, int* sVpos, int len = 0x7fffffff) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int code[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int pos = r * 256 + tid;
-    code[r] = pos < n ? decode_position(p, s, irow, pos) : -1;
+    code[r] = pos < n ? decode_position(p, s, irow, pos, len) : -1;
   }
   int total = 0;
 #pragma unroll

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __re
   const int npos = n_positions(p);
   for (int pos0 = 0; pos0 < npos; pos0 += kMaxPos) {
     __syncthreads();
-    const int cnt = compact_positions(p, s, irow, pos0, min(kMaxPos, npos - pos0), sRows, sWave);
+    const int cnt =
+        compact_positions(p, s, irow, pos0, min(kMaxPos, npos - pos0), sRows, sWave, nullptr, row_len(p, row));
     for (int k0 = 0; k0 < cnt; k0 += kNT) {
       for (int c = tid; c < kNT * (DQK / 8); c += kThreads) {
         const int r = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
