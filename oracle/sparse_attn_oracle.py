@@ -48,7 +48,9 @@ design notes):
   R4  lse is the natural-log LSE over the selected, masked logits (plus the
       sink logit when sinks are present); SimpleSoftmax(x, lse) = exp(x - lse);
   R5  sinks are one fp32 logit per query head, in the denominator only;
-  R6  masks: causal means key position <= query position (per sequence);
+  R6  masks: causal means key position <= query position (per sequence;
+      with the ends-aligned mode, query i of n_q sits at key position
+      i + n_kv - n_q, and padding rows past seqused take no part);
       window keys are [t - win_left, t + win_right] within [0, t]; cmp row j
       (covering ori tokens [r*j, r*j + r - 1]) is visible iff r*j + r - 1 <= t;
       a masked key is simply absent;
@@ -108,7 +110,11 @@ class Problem:
         self.block_size = wl.block_size
         self.win_left, self.win_right = wl.win_left, wl.win_right
         self.cmp_ratio = wl.cmp_ratio
-        self.causal = True
+        # 1: key position <= query position, positions counted from each
+        # sequence's start; 2: the query and kv sequences aligned at their
+        # ends (query i of n_q sits at key position i + n_kv - n_q)
+        self.mask = int(getattr(wl, "mask_causal", 1))
+        self.causal = self.mask != 0
         self.q = inputs.get("q")
         self.d_o = inputs.get("d_o")
         if wl.kv_shared:
@@ -126,7 +132,13 @@ class Problem:
         tl = inputs.get("topk_len")
         self.topk_len = None if tl is None else np.clip(np.asarray(tl, np.int64), 0, self.idx.shape[2])
         self.cu = inputs["cu_seqlens"].numpy().astype(np.int64)
+        self.cu_kv = np.asarray(inputs.get("cu_seqlens_kv", inputs["cu_seqlens"]), np.int64)
         self.cu_cmp = inputs["cu_seqlens_cmp"].numpy().astype(np.int64)
+        # optional per-sequence counts of the query / kv / cmp rows that take
+        # part (SparseFlashMlaGrad README, parameter table: seqused*): rows
+        # past them are padding
+        self.used = {k: (None if inputs.get(k) is None else np.asarray(inputs[k], np.int64))
+                     for k in ("seqused_q", "seqused_kv", "seqused_cmp")}
         self.T = int(self.cu[-1])
         self.K = self.idx.shape[2]
         # sequence id of every token
@@ -145,13 +157,13 @@ class Problem:
         index slot (token), slot * block_size + row in block (block), or the
         window offset followed by window length + slot (window+cmp).  These
         are the columns of the softmax L1-norm outputs."""
-        b = int(self.seq_of[t])
-        tl = t - int(self.cu[b])                  # position within the sequence
+        b, tl, n_kv, base, n_cmp_used = self.query_pos(t)
         K = self.idx.shape[2]
+        if tl is None:                            # a padding query row
+            e = np.zeros(0, dtype=np.int64)
+            return e, e, e
         n_sel = K if self.topk_len is None else int(self.topk_len[t, g])
         usable = np.arange(K) < n_sel             # slots inside the row's length
-        n_kv = int(self.cu[b + 1] - self.cu[b])   # Sq = Skv per sequence here
-        base = int(self.cu[b])
         if self.select == SEL_TOKEN:
             j = self.idx[t, g].astype(np.int64)
             keep = (j >= 0) & (j < n_kv)
@@ -179,7 +191,7 @@ class Problem:
             keep &= w <= tl
         ori = base + w[keep]
         r = self.cmp_ratio
-        n_cmp = int(self.cu_cmp[b + 1] - self.cu_cmp[b])
+        n_cmp = n_cmp_used
         j = self.idx[t, g].astype(np.int64)
         keepc = (j >= 0) & (j < n_cmp)
         if self.causal:
@@ -189,6 +201,25 @@ class Problem:
         srcs = np.concatenate([np.zeros(ori.size, np.int64), np.ones(cmp.size, np.int64)])
         pos = np.concatenate([np.flatnonzero(keep), w.size + np.flatnonzero(keepc)])
         return srcs, np.concatenate([ori, cmp]), pos
+
+    def query_pos(self, t: int):
+        """(sequence b, key position of query t or None for a padding row,
+        kv rows taking part, first kv row, cmp rows taking part)."""
+        b = int(self.seq_of[t])
+        i = t - int(self.cu[b])                   # index within the query sequence
+        n_q = int(self.cu[b + 1] - self.cu[b])
+        n_kv = int(self.cu_kv[b + 1] - self.cu_kv[b])
+        n_cmp = int(self.cu_cmp[b + 1] - self.cu_cmp[b])
+        if self.used["seqused_q"] is not None:
+            n_q = min(n_q, int(self.used["seqused_q"][b]))
+        if self.used["seqused_kv"] is not None:
+            n_kv = min(n_kv, int(self.used["seqused_kv"][b]))
+        if self.used["seqused_cmp"] is not None:
+            n_cmp = min(n_cmp, int(self.used["seqused_cmp"][b]))
+        if i >= n_q:
+            return b, None, n_kv, int(self.cu_kv[b]), n_cmp
+        pos = i + (n_kv - n_q if self.mask == 2 else 0)
+        return b, pos, n_kv, int(self.cu_kv[b]), n_cmp
 
     def gather(self, srcs: np.ndarray, rows: np.ndarray, g: int) -> Tuple[np.ndarray, np.ndarray]:
         """fp64 K_sel [n, d_qk] and V_sel [n, d_v] for a selection."""
@@ -413,6 +444,7 @@ def indexer_grad_kl(inputs: Dict[str, object], tokens: Optional[Sequence[int]] =
     """
     wl = inputs["workload"]
     view = {"workload": wl, "idx": inputs["idx"], "cu_seqlens": inputs["cu_seqlens"],
+            "cu_seqlens_kv": inputs.get("cu_seqlens_kv", inputs["cu_seqlens"]),
             "cu_seqlens_cmp": inputs["cu_seqlens_cmp"], "kv": inputs["k_idx"][:, None, :]}
     pb = Problem(view)
     q = inputs["q_idx"]
@@ -455,7 +487,7 @@ def indexer_grad_kl(inputs: Dict[str, object], tokens: Optional[Sequence[int]] =
 def _block_base(pb: Problem) -> np.ndarray:
     """First global block id of every sequence (ceil(len / bs) blocks each)."""
     bs = pb.block_size
-    nb = (np.diff(pb.cu) + bs - 1) // bs
+    nb = (np.diff(pb.cu_kv) + bs - 1) // bs
     return np.concatenate([[0], np.cumsum(nb)])
 
 
@@ -467,34 +499,40 @@ def entry_keys(pb: Problem) -> np.ndarray:
     id * Hkv + g with blocks numbered per sequence at ceil(len / bs) each;
     window+cmp: key = global cmp row * Hkv + g (the window part has no slot).
     A slot is used when its index is >= 0, inside its sequence and not fully
-    masked (token: j <= t; block: first row j * bs <= t; cmp: r*j + r - 1 <= t).
+    masked (token: j <= t; block: first row j * bs <= t; cmp: r*j + r - 1 <= t,
+    t the query's key position), inside the row's top-k length, and the
+    query row is not padding.
     """
     T, Hkv, K = pb.idx.shape
     j = pb.idx.astype(np.int64)
-    b = pb.seq_of[:, None, None]
-    tl = (np.arange(T) - pb.cu[pb.seq_of])[:, None, None]
-    n_kv = np.diff(pb.cu)[pb.seq_of][:, None, None]
-    g = np.arange(Hkv)[None, :, None]
-    if pb.select == SEL_TOKEN:
-        ok = (j >= 0) & (j < n_kv) & ((j <= tl) if pb.causal else True)
-        key = (pb.cu[pb.seq_of][:, None, None] + j) * Hkv + g
-    elif pb.select == SEL_BLOCK:
-        bs = pb.block_size
-        ok = (j >= 0) & (j * bs < n_kv) & ((j * bs <= tl) if pb.causal else True)
-        key = (_block_base(pb)[pb.seq_of][:, None, None] + j) * Hkv + g
-    else:
-        r = pb.cmp_ratio
-        n_cmp = np.diff(pb.cu_cmp)[pb.seq_of][:, None, None]
-        ok = (j >= 0) & (j < n_cmp) & ((r * j + r - 1 <= tl) if pb.causal else True)
-        key = (pb.cu_cmp[pb.seq_of][:, None, None] + j) * Hkv + g
-    if pb.topk_len is not None:
-        ok &= np.arange(K)[None, None, :] < pb.topk_len[:, :, None]
-    return np.where(ok, key, -1).reshape(-1)
+    out = np.full((T, Hkv, K), -1, dtype=np.int64)
+    bb = _block_base(pb)
+    r = pb.cmp_ratio
+    for t in range(T):
+        b, tl, n_kv, kv_base, n_cmp = pb.query_pos(t)
+        if tl is None:
+            continue
+        for g in range(Hkv):
+            jj = j[t, g]
+            if pb.select == SEL_TOKEN:
+                ok = (jj >= 0) & (jj < n_kv) & ((jj <= tl) if pb.causal else True)
+                key = (kv_base + jj) * Hkv + g
+            elif pb.select == SEL_BLOCK:
+                bs = pb.block_size
+                ok = (jj >= 0) & (jj * bs < n_kv) & ((jj * bs <= tl) if pb.causal else True)
+                key = (bb[b] + jj) * Hkv + g
+            else:
+                ok = (jj >= 0) & (jj < n_cmp) & ((r * jj + r - 1 <= tl) if pb.causal else True)
+                key = (int(pb.cu_cmp[b]) + jj) * Hkv + g
+            if pb.topk_len is not None:
+                ok &= np.arange(K) < pb.topk_len[t, g]
+            out[t, g] = np.where(ok, key, -1)
+    return out.reshape(-1)
 
 
 def n_keys(pb: Problem) -> int:
     if pb.select == SEL_TOKEN:
-        return int(pb.cu[-1]) * pb.Hkv
+        return int(pb.cu_kv[-1]) * pb.Hkv
     if pb.select == SEL_BLOCK:
         return int(_block_base(pb)[-1]) * pb.Hkv
     return int(pb.cu_cmp[-1]) * pb.Hkv

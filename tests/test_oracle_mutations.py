@@ -44,6 +44,9 @@ MUTATIONS = {
     "idx_slot_not_position": ("p = P[t, pos]", "p = P[t, :pos.size]"),
     # per-row top-k lengths
     "len_off_by_one": ("usable = np.arange(K) < n_sel", "usable = np.arange(K) <= n_sel"),
+    # query / kv sequences of different lengths
+    "align_ignored": ("pos = i + (n_kv - n_q if self.mask == 2 else 0)", "pos = i"),
+    "seqused_q_ignored": ("        if i >= n_q:\n", "        if i >= n_q + 10**9:\n"),
 }
 
 
@@ -138,6 +141,21 @@ def test_pins_catch_planted_mistake(name):
                 caught.append(True)
     elif name == "csr_unstable":
         caught.append(not _csr_ok(mod, "token_gqa"))
+    elif name.startswith(("align_", "seqused_")):
+        from tests import test_oracle_alignment_pins as AL
+        pins = [lambda m=m, a=a: AL.test_selection_s1_ne_s2_brute_force(m, a)
+                for m in ("token_gqa", "block_gqa", "wcmp_sinks") for a in (1, 2)]
+        pins += [lambda a=a: AL.test_seqused_equals_cut_sequences(a) for a in (1, 2)]
+        for pin in pins:
+            saved = O.Problem
+            O.Problem = mod.Problem
+            try:
+                pin()
+                caught.append(False)
+            except AssertionError:
+                caught.append(True)
+            finally:
+                O.Problem = saved
     elif name.startswith("len_"):
         from tests.test_oracle_pins import test_per_row_topk_lengths
         for m in ("token_gqa", "block_gqa", "wcmp_sinks"):

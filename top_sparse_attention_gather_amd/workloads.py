@@ -52,7 +52,7 @@ class Workload:
     name: str
     select: int                      # SEL_TOKEN / SEL_BLOCK / SEL_WINDOW_CMP
     layout: int                      # LAYOUT_BSND / LAYOUT_TND
-    seqlens: tuple                   # per-sequence query (= kv) lengths
+    seqlens: tuple                   # per-sequence query lengths (and kv lengths unless kv_seqlens)
     n_q_heads: int
     n_kv_heads: int
     d_qk: int
@@ -69,6 +69,8 @@ class Workload:
     kv_std: float = 1.0
     cmp_noise_std: float = 0.1
     seed: int = 0
+    kv_seqlens: tuple = ()           # per-sequence kv lengths when they differ from the query's
+    mask_causal: int = 1             # 1: key <= query position (top-left); 2: aligned at the ends (bottom-right)
 
     # -- derived sizes -------------------------------------------------
     @property
@@ -80,14 +82,23 @@ class Workload:
         return int(sum(self.seqlens))
 
     @property
+    def kv_lens(self) -> tuple:
+        return tuple(self.kv_seqlens) if self.kv_seqlens else tuple(self.seqlens)
+
+    @property
     def total_kv(self) -> int:
-        return int(sum(self.seqlens))
+        return int(sum(self.kv_lens))
 
     @property
     def cmp_seqlens(self) -> tuple:
         if self.select != SEL_WINDOW_CMP:
             return tuple(0 for _ in self.seqlens)
-        return tuple(s // self.cmp_ratio for s in self.seqlens)
+        return tuple(s // self.cmp_ratio for s in self.kv_lens)
+
+    def q_offset(self, b: int) -> int:
+        """Key position of query 0 of sequence b: 0 (top-left), or kv length
+        minus query length when the masks align the sequences' ends."""
+        return self.kv_lens[b] - self.seqlens[b] if self.mask_causal == 2 else 0
 
     @property
     def total_cmp(self) -> int:
@@ -103,6 +114,9 @@ class Workload:
 
     def cu_seqlens(self) -> np.ndarray:
         return np.concatenate([[0], np.cumsum(self.seqlens)]).astype(np.int32)
+
+    def cu_seqlens_kv(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.kv_lens)]).astype(np.int32)
 
     def cu_seqlens_cmp(self) -> np.ndarray:
         return np.concatenate([[0], np.cumsum(self.cmp_seqlens)]).astype(np.int32)
@@ -243,8 +257,14 @@ def make_indices(wl: Workload, rng: Optional[np.random.Generator] = None) -> np.
     T, Hkv, K = wl.total_q, wl.n_kv_heads, wl.topk
     out = np.full((T, Hkv, K), -1, dtype=np.int32)
     tok = 0
-    for L in wl.seqlens:
-        for t in range(L):
+    for b, L in enumerate(wl.seqlens):
+        Lkv = wl.kv_lens[b]
+        for tq in range(L):
+            # the last key the query may see (its own position in key
+            # coordinates, inside the kv sequence); none when negative
+            t = min(tq + wl.q_offset(b), Lkv - 1)
+            if t < 0:
+                continue
             for g in range(Hkv):
                 if wl.index_policy == "self_plus_uniform":
                     rows = _rows_self_plus_uniform(rng, t, K)
@@ -273,7 +293,7 @@ def make_indices(wl: Workload, rng: Optional[np.random.Generator] = None) -> np.
                     rows = np.array([t])
                 else:
                     raise ValueError(f"unknown index policy {wl.index_policy!r}")
-                out[tok + t, g, :rows.size] = rows
+                out[tok + tq, g, :rows.size] = rows
         tok += L
     return out
 
@@ -311,7 +331,7 @@ def make_inputs(wl: Workload, with_indices: bool = True, threads: int = 8) -> Di
         noise = _normal_f32(st["cmp_noise"], (wl.total_cmp, Hkv, wl.d_qk), std=wl.cmp_noise_std,
                             threads=threads)
         cmp = np.empty_like(noise)
-        cu, cuc = wl.cu_seqlens(), wl.cu_seqlens_cmp()
+        cu, cuc = wl.cu_seqlens_kv(), wl.cu_seqlens_cmp()
         r = wl.cmp_ratio
         for b in range(wl.batch):
             n = int(cuc[b + 1] - cuc[b])
@@ -323,6 +343,7 @@ def make_inputs(wl: Workload, with_indices: bool = True, threads: int = 8) -> Di
         g = np.random.Generator(np.random.PCG64(st["sinks"]))
         out["sinks"] = torch.from_numpy(g.standard_normal(Hq, dtype=np.float32))
     out["cu_seqlens"] = torch.from_numpy(wl.cu_seqlens())
+    out["cu_seqlens_kv"] = torch.from_numpy(wl.cu_seqlens_kv())
     out["cu_seqlens_cmp"] = torch.from_numpy(wl.cu_seqlens_cmp())
     if with_indices:
         out["idx"] = torch.from_numpy(make_indices(wl))
@@ -346,6 +367,7 @@ def make_indexer_inputs(wl: Workload, with_indices: bool = True, threads: int = 
     out["weights"] = torch.from_numpy(_normal_f32(st["iw"], (T, Hq), std=1.0 / math.sqrt(Hq * d),
                                                   threads=threads))
     out["cu_seqlens"] = torch.from_numpy(wl.cu_seqlens())
+    out["cu_seqlens_kv"] = torch.from_numpy(wl.cu_seqlens_kv())
     out["cu_seqlens_cmp"] = torch.from_numpy(wl.cu_seqlens_cmp())
     if with_indices:
         idx = make_indices(wl)
