@@ -36,8 +36,9 @@
  *     and may appear in any position; an index past the sequence's rows is
  *     also unused; duplicates count once per slot;
  *   - causal (mask_causal = 1): key position <= query position within the
- *     sequence (top-left aligned); in block mode the rows of a selected
- *     block past the query are masked individually;
+ *     sequence (top-left aligned); mask_causal = 2 aligns the query and kv
+ *     sequences at their ends (for seqlen_q != seqlen_kv); in block mode
+ *     the rows of a selected block past the query are masked individually;
  *   - window (select = SA_SEL_WINDOW_CMP): ori keys [t - win_left,
  *     t + win_right] inside the sequence and the causal range, followed by
  *     the cmp rows named by topk_indices; cmp row j covers ori tokens
@@ -113,7 +114,12 @@ typedef struct sa_desc {
   int32_t select;       /* SA_SEL_TOKEN / SA_SEL_BLOCK / SA_SEL_WINDOW_CMP */
   int32_t topk;         /* index slots per (token, kv head) */
   int32_t block_size;   /* rows per index in SA_SEL_BLOCK (1 = token) */
-  int32_t mask_causal;  /* 1: key position <= query position */
+  int32_t mask_causal;  /* 0: none; 1: key position <= query position, both
+                           counted from the sequence's start; 2: the same with
+                           query and kv sequences aligned at their ends (query
+                           i of n_q sits at key position i + n_kv - n_q; with
+                           seqused, the used lengths) -- windows and cmp
+                           visibility use that position too */
   int32_t win_left;     /* SA_SEL_WINDOW_CMP window: keys [t-win_left, t+win_right] */
   int32_t win_right;
   int32_t cmp_ratio;    /* SA_SEL_WINDOW_CMP: ori tokens per cmp row */
@@ -175,6 +181,14 @@ typedef struct sa_bwd_args {
    * to [0, topk].  NULL: every slot may be used.  In SA_SEL_WINDOW_CMP they
    * limit the cmp slots; the window is not affected. */
   const int32_t* topk_lengths;
+  /* Optional [batch] int32 counts of the query / kv / cmp rows of each
+   * sequence that take part (SparseFlashMlaGrad README, parameter table:
+   * seqused*); rows past them are padding: a padding query row selects
+   * nothing (dq = 0) and a padding kv / cmp row is never selected (its
+   * gradient is 0).  NULL: every row takes part. */
+  const int32_t* seqused_q;
+  const int32_t* seqused_kv;
+  const int32_t* seqused_cmp;
 } sa_bwd_args_t;
 
 /* Device pointers for the forward (o, lse out; the rest as above). */
@@ -192,6 +206,9 @@ typedef struct sa_fwd_args {
   void* o;
   float* lse;
   const int32_t* topk_lengths;   /* as in sa_bwd_args_t (NULL: all slots) */
+  const int32_t* seqused_q;      /* as in sa_bwd_args_t (NULL: all rows) */
+  const int32_t* seqused_kv;
+  const int32_t* seqused_cmp;
 } sa_fwd_args_t;
 
 /* Phase 1 of the backward: validates `desc` (host only, no HIP call) and

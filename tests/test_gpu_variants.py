@@ -96,3 +96,64 @@ def test_window_dense_cmp_ratio8(mode):
                     n_q_heads=64, n_kv_heads=1, d_qk=576, d_v=512, kv_shared=True, topk=26, win_left=31,
                     win_right=0, cmp_ratio=8, has_sinks=True, index_policy="full", seed=82)
     U.run_full_case(wl, dkv_mode=MODES[mode], l1=True)
+
+
+ALIGNED = {
+    # MLA token selection, one sequence of 96 queries over 160 kv rows
+    "mla_q96_kv160": W.Workload(name="mla_q96_kv160", select=W.SEL_TOKEN, layout=W.LAYOUT_BSND, seqlens=(96,),
+                                kv_seqlens=(160,), n_q_heads=64, n_kv_heads=1, d_qk=576, d_v=512, kv_shared=True,
+                                topk=64, kv_std=0.5, mask_causal=2, seed=83),
+    # block selection (d 128, blocks of 32), varlen with longer and equal kv sequences
+    "block_varlen": W.Workload(name="block_varlen", select=W.SEL_BLOCK, layout=W.LAYOUT_TND, seqlens=(128, 200),
+                               kv_seqlens=(256, 200), n_q_heads=16, n_kv_heads=1, d_qk=128, d_v=128,
+                               kv_shared=False, topk=5, block_size=32, index_policy="own_block_plus_uniform",
+                               mask_causal=2, seed=84),
+    # window + cmp with sinks, varlen, kv longer than the queries
+    "wcmp_varlen": W.Workload(name="wcmp_varlen", select=W.SEL_WINDOW_CMP, layout=W.LAYOUT_TND, seqlens=(64, 120),
+                              kv_seqlens=(100, 150), n_q_heads=64, n_kv_heads=1, d_qk=576, d_v=512, kv_shared=True,
+                              topk=12, win_left=31, win_right=0, cmp_ratio=4, has_sinks=True,
+                              index_policy="cmp_uniform_visible", mask_causal=2, seed=85),
+}
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("name", list(ALIGNED))
+def test_s1_ne_s2_ends_aligned(name, mode):
+    """Query and kv sequences of different lengths with the ends-aligned
+    causal mask (L1-norm outputs included)."""
+    U.run_full_case(ALIGNED[name], dkv_mode=MODES[mode], l1=True)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("name", list(ALIGNED))
+def test_seqused_padding(name, mode):
+    """seqused: padding query rows get dq = 0, padding kv / cmp rows are
+    never selected (gradient 0), against the oracle with the same counts."""
+    wl = ALIGNED[name]
+    if wl.layout == W.LAYOUT_BSND:
+        wl = dataclasses.replace(wl, layout=W.LAYOUT_TND)
+    inp = W.make_inputs(wl)
+    rng = np.random.default_rng(6)
+    inp["seqused_q"] = np.array([int(rng.integers(L // 2, L + 1)) for L in wl.seqlens], np.int32)
+    inp["seqused_kv"] = np.array([int(rng.integers(L // 2, L + 1)) for L in wl.kv_lens], np.int32)
+    if wl.select == W.SEL_WINDOW_CMP:
+        inp["seqused_cmp"] = np.array([int(rng.integers(c // 2, c + 1)) for c in wl.cmp_seqlens], np.int32)
+    res, got, ref = U.run_full_case(wl, inputs=inp, dkv_mode=MODES[mode], l1=True)
+    cq = wl.cu_seqlens()
+    pad = np.concatenate([np.arange(cq[b] + inp["seqused_q"][b], cq[b + 1]) for b in range(wl.batch)])
+    assert np.all(got["dq"].reshape(ref["dq"].shape)[pad] == 0)
+
+
+def test_fwd_s1_ne_s2_ends_aligned_seqused():
+    wl = ALIGNED["wcmp_varlen"]
+    inp = W.make_inputs(wl)
+    inp["seqused_q"] = np.array([50, 120], np.int32)
+    inp["seqused_kv"] = np.array([90, 141], np.int32)
+    U.say("[fwd aligned]")
+    out_ref, lse_ref = O.sparse_fwd(O.Problem(inp))
+    o, lse = B.sparse_attn_fwd(B.make_desc(wl), B.device_tensors(inp))
+    torch.cuda.synchronize()
+    check_close("wcmp_varlen:o", o.float().cpu().numpy(), out_ref)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse.cpu().numpy()), fin)
+    np.testing.assert_allclose(lse.cpu().numpy()[fin], lse_ref[fin], rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref[fin]).max()))

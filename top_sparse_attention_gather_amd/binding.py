@@ -44,13 +44,13 @@ class SaBwdArgs(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "q", "k", "v", "kv", "cmp_kv", "o", "d_o", "lse", "sinks", "topk_indices", "cu_seqlens_q",
         "cu_seqlens_kv", "cu_seqlens_cmp", "dq", "dk", "dv", "dkv", "d_cmp_kv", "dsinks", "ori_softmax_l1",
-        "cmp_softmax_l1", "topk_lengths")]
+        "cmp_softmax_l1", "topk_lengths", "seqused_q", "seqused_kv", "seqused_cmp")]
 
 
 class SaFwdArgs(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "q", "k", "v", "kv", "cmp_kv", "sinks", "topk_indices", "cu_seqlens_q", "cu_seqlens_kv",
-        "cu_seqlens_cmp", "o", "lse", "topk_lengths")]
+        "cu_seqlens_cmp", "o", "lse", "topk_lengths", "seqused_q", "seqused_kv", "seqused_cmp")]
 
 
 class SaIndexerDesc(ctypes.Structure):
@@ -125,16 +125,16 @@ def make_desc(wl: W.Workload, dkv_mode: int = DKV_ATOMIC, **over) -> SaDesc:
     d = SaDesc()
     if wl.layout == W.LAYOUT_BSND:
         d.layout, d.batch = W.LAYOUT_BSND, wl.batch
-        d.seqlen_q = d.seqlen_kv = wl.seqlens[0]
+        d.seqlen_q, d.seqlen_kv = wl.seqlens[0], wl.kv_lens[0]
     else:
         d.layout, d.batch = W.LAYOUT_TND, wl.batch
-        d.total_q = d.total_kv = wl.total_q
+        d.total_q, d.total_kv = wl.total_q, wl.total_kv
     d.total_cmp = wl.total_cmp
     d.n_q_heads, d.n_kv_heads, d.d_qk, d.d_v = wl.n_q_heads, wl.n_kv_heads, wl.d_qk, wl.d_v
     d.kv_shared = int(wl.kv_shared)
     d.select, d.topk = wl.select, wl.topk
     d.block_size = wl.block_size if wl.select == W.SEL_BLOCK else 1
-    d.mask_causal = 1
+    d.mask_causal = wl.mask_causal
     d.win_left, d.win_right, d.cmp_ratio = wl.win_left, wl.win_right, wl.cmp_ratio
     d.has_sinks = int(wl.has_sinks)
     d.dkv_mode = dkv_mode
@@ -200,7 +200,7 @@ def sparse_attn_bwd(desc: SaDesc, tensors: Dict[str, torch.Tensor], outputs: Opt
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=tensors["q"].device)
     a = SaBwdArgs()
     for name in ("q", "k", "v", "kv", "cmp_kv", "o", "d_o", "lse", "sinks", "topk_indices", "cu_seqlens_q",
-                 "cu_seqlens_kv", "cu_seqlens_cmp", "topk_lengths"):
+                 "cu_seqlens_kv", "cu_seqlens_cmp", "topk_lengths", "seqused_q", "seqused_kv", "seqused_cmp"):
         setattr(a, name, _ptr(tensors.get(name)))
     for name in ("dq", "dk", "dv", "dkv", "d_cmp_kv", "dsinks", "ori_softmax_l1", "cmp_softmax_l1"):
         setattr(a, name, _ptr(outputs.get(name)))
@@ -256,7 +256,7 @@ def sparse_attn_fwd(desc: SaDesc, tensors: Dict[str, torch.Tensor], o: Optional[
         lse = torch.empty((T, desc.n_q_heads), dtype=torch.float32, device=q.device)
     a = SaFwdArgs()
     for name in ("q", "k", "v", "kv", "cmp_kv", "sinks", "topk_indices", "cu_seqlens_q", "cu_seqlens_kv",
-                 "cu_seqlens_cmp", "topk_lengths"):
+                 "cu_seqlens_cmp", "topk_lengths", "seqused_q", "seqused_kv", "seqused_cmp"):
         setattr(a, name, _ptr(tensors.get(name)))
     a.o, a.lse = _ptr(o), _ptr(lse)
     _check("sparse_attn_fwd", lib.sparse_attn_fwd(ctypes.byref(desc), ctypes.byref(a), _stream(stream)))
@@ -283,9 +283,12 @@ def device_tensors(inputs: Dict[str, object], device="cuda") -> Dict[str, torch.
         out["topk_lengths"] = torch.as_tensor(inputs["topk_len"], dtype=torch.int32).to(device).contiguous()
     if wl.layout == W.LAYOUT_TND:
         out["cu_seqlens_q"] = inputs["cu_seqlens"].to(device)
-        out["cu_seqlens_kv"] = inputs["cu_seqlens"].to(device)
+        out["cu_seqlens_kv"] = inputs.get("cu_seqlens_kv", inputs["cu_seqlens"]).to(device)
     if wl.select == W.SEL_WINDOW_CMP:
         out["cu_seqlens_cmp"] = inputs["cu_seqlens_cmp"].to(device)
+    for k in ("seqused_q", "seqused_kv", "seqused_cmp"):
+        if inputs.get(k) is not None:
+            out[k] = torch.as_tensor(inputs[k], dtype=torch.int32).to(device).contiguous()
     return out
 
 
@@ -346,7 +349,7 @@ def indexer_device_tensors(inputs: Dict[str, object], device="cuda") -> Dict[str
            "target": inputs["target"].to(device).contiguous()}
     if wl.layout == W.LAYOUT_TND:
         out["cu_seqlens_q"] = inputs["cu_seqlens"].to(device)
-        out["cu_seqlens_kv"] = inputs["cu_seqlens"].to(device)
+        out["cu_seqlens_kv"] = inputs.get("cu_seqlens_kv", inputs["cu_seqlens"]).to(device)
     return out
 
 

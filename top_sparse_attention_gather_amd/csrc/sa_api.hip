@@ -37,7 +37,7 @@ sa_status_t validate(const sa_desc_t* d) {
   if (d->select < SA_SEL_TOKEN || d->select > SA_SEL_WINDOW_CMP) return SA_ERR_BAD_ARG;
   if (d->dkv_mode != SA_DKV_ATOMIC && d->dkv_mode != SA_DKV_DETERMINISTIC) return SA_ERR_BAD_ARG;
   if (d->kv_shared != 0 && d->kv_shared != 1) return SA_ERR_BAD_ARG;
-  if (d->mask_causal != 0 && d->mask_causal != 1) return SA_ERR_BAD_ARG;
+  if (d->mask_causal < 0 || d->mask_causal > 2) return SA_ERR_BAD_ARG;
   if (d->has_sinks != 0 && d->has_sinks != 1) return SA_ERR_BAD_ARG;
   if (!std::isfinite(d->scale)) return SA_ERR_BAD_ARG;
   if (d->softmax_l1 != 0 && d->softmax_l1 != 1) return SA_ERR_BAD_ARG;
@@ -464,6 +464,9 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   p.cu_kv = a->cu_seqlens_kv;
   p.cu_cmp = desc->topk > 0 ? a->cu_seqlens_cmp : nullptr;
   p.topk_len = a->topk_lengths;
+  p.used_q = a->seqused_q;
+  p.used_kv = a->seqused_kv;
+  p.used_cmp = a->seqused_cmp;
 
   BwdBuffers w;
   std::memset(&w, 0, sizeof(w));
@@ -616,6 +619,9 @@ sa_status_t sparse_attn_fwd(const sa_desc_t* desc, const sa_fwd_args_t* a, void*
   p.cu_kv = a->cu_seqlens_kv;
   p.cu_cmp = desc->topk > 0 ? a->cu_seqlens_cmp : nullptr;
   p.topk_len = a->topk_lengths;
+  p.used_q = a->seqused_q;
+  p.used_kv = a->seqused_kv;
+  p.used_cmp = a->seqused_cmp;
   SA_TRY_HIP(sa::launch_fwd_rows(p, static_cast<bf16*>(a->o), a->lse, reinterpret_cast<hipStream_t>(stream)));
   return SA_OK;
 }

@@ -105,9 +105,10 @@ __global__ __launch_bounds__(kThreads) void blk_dkv_kernel(Params p, BlkArgs a) 
     b = lo;
   }
   const int jb = bn - a.blk_base[b];                 // block index within the sequence
-  const int kv_base = p.layout == kLayoutBSND ? b * p.Skv : p.cu_kv[b];
-  const int kv_len = p.layout == kLayoutBSND ? p.Skv : p.cu_kv[b + 1] - p.cu_kv[b];
-  const int q_base = p.layout == kLayoutBSND ? b * p.Sq : p.cu_q[b];
+  const SeqLens SL = seq_lens(p, b);
+  const int kv_base = SL.kv_base;
+  const int kv_len = SL.kv_len;                      // used rows
+  const int q_base = SL.q_base - SL.off;             // token - q_base = key position
   const int h0 = g * p.G + hc * kHeads;
   const int Gc = min(kHeads, p.G - hc * kHeads);
   const int eb = a.row_ptr[bkey] + cidx * kBlkChunk;
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void blk_dq_kernel(Params p, BwdBuffers w
   __shared__ int sW[4];
   bool ok = false;
   int blk = -1;
-  if (tid < row_len(p, row)) {
+  if (sp.active && tid < row_len(p, row)) {
     blk = irow[tid];
     ok = blk >= 0 && (long long)blk * p.bs < sp.kv_len && (!p.causal || (long long)blk * p.bs <= sp.tl);
   }
@@ -471,7 +472,10 @@ __global__ void blk_sum_cast_kernel(Params p, BlkArgs a, long long n_rows, bf16*
   const int jl = (int)(j - (p.layout == kLayoutBSND ? (long long)b * p.Skv : p.cu_kv[b]));
   const long long bkey = (long long)(a.blk_base[b] + jl / p.bs) * p.Hkv + g;
   const int rr = jl % p.bs;
-  const long long w0 = a.chunk_base[bkey], w1 = a.chunk_base[bkey + 1];
+  // rows past the sequence's used kv rows take no part (their chunk rows
+  // are never written)
+  const long long w0 = a.chunk_base[bkey];
+  const long long w1 = jl < seq_lens(p, b).kv_len ? a.chunk_base[bkey + 1] : w0;
   float acc = 0.f;
   for (int hc = 0; hc < a.n_hc; ++hc)
     for (long long w = w0; w < w1; ++w) acc += a.part[(((size_t)hc * a.max_chunks + w) * 64 + rr) * (2 * d) + c];

@@ -104,6 +104,7 @@ __global__ __launch_bounds__(kThreads) void scan_apply_kernel(const int* __restr
 
 __device__ __forceinline__ int slot_key(const Params& p, const SeqPos& s, int g, int j,
                                         const int* __restrict__ blk_base, int sentinel) {
+  if (!s.active) return sentinel;
   if (p.select == kSelToken) {
     if (j < 0 || j >= s.kv_len || (p.causal && j > s.tl)) return sentinel;
     return (s.kv_base + j) * p.Hkv + g;

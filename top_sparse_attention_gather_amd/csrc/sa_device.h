@@ -43,21 +43,52 @@ struct Params {
   const int* cu_kv;
   const int* cu_cmp;
   const int* topk_len;   // [T][Hkv] selectable slots per row, or null (all topk)
+  // [B] query / kv / cmp rows of each sequence that take part (the rest is
+  // padding), or null (all of them)
+  const int* used_q;
+  const int* used_kv;
+  const int* used_cmp;
 };
 
-// Where a query token sits: its sequence, local position, and the first
-// row / row count of its sequence in the kv and cmp tables.
+// Rows of sequence b: first query row and the query rows taking part,
+// first kv row and the kv rows taking part, and the key position of query
+// 0 -- 0, or kv_len - q_len when the mask aligns the sequences' ends
+// (causal = 2).
+struct SeqLens {
+  int q_base, q_len, kv_base, kv_len, off;
+};
+
+__device__ __forceinline__ SeqLens seq_lens(const Params& p, int b) {
+  SeqLens L;
+  if (p.layout == kLayoutBSND) {
+    L.q_base = b * p.Sq;
+    L.q_len = p.Sq;
+    L.kv_base = b * p.Skv;
+    L.kv_len = p.Skv;
+  } else {
+    L.q_base = p.cu_q[b];
+    L.q_len = p.cu_q[b + 1] - p.cu_q[b];
+    L.kv_base = p.cu_kv[b];
+    L.kv_len = p.cu_kv[b + 1] - p.cu_kv[b];
+  }
+  if (p.used_q) L.q_len = min(L.q_len, max(p.used_q[b], 0));
+  if (p.used_kv) L.kv_len = min(L.kv_len, max(p.used_kv[b], 0));
+  L.off = p.causal == 2 ? L.kv_len - L.q_len : 0;
+  return L;
+}
+
+// Where a query token sits: its sequence, its position in key coordinates
+// (tl: the local index, shifted by the sequence's offset when the mask
+// aligns the ends), whether it takes part (not a padding row), and the
+// first row / used row count of its sequence in the kv and cmp tables.
 struct SeqPos {
-  int b, tl, kv_base, kv_len, cmp_base, cmp_len;
+  int b, tl, kv_base, kv_len, cmp_base, cmp_len, active;
 };
 
 __device__ __forceinline__ SeqPos seq_pos(const Params& p, int t) {
   SeqPos s;
   if (p.layout == kLayoutBSND) {
     s.b = t / p.Sq;
-    s.tl = t - s.b * p.Sq;
-    s.kv_base = s.b * p.Skv;
-    s.kv_len = p.Skv;
   } else {
     int lo = 0, hi = p.B;           // largest b with cu_q[b] <= t
     while (hi - lo > 1) {
@@ -65,13 +96,17 @@ __device__ __forceinline__ SeqPos seq_pos(const Params& p, int t) {
       if (p.cu_q[mid] <= t) lo = mid; else hi = mid;
     }
     s.b = lo;
-    s.tl = t - p.cu_q[lo];
-    s.kv_base = p.cu_kv[lo];
-    s.kv_len = p.cu_kv[lo + 1] - p.cu_kv[lo];
   }
+  const SeqLens L = seq_lens(p, s.b);
+  const int i = t - L.q_base;
+  s.active = i < L.q_len;
+  s.tl = i + L.off;
+  s.kv_base = L.kv_base;
+  s.kv_len = L.kv_len;
   if (p.select == kSelWindowCmp && p.cu_cmp) {   // no cmp table without index slots
     s.cmp_base = p.cu_cmp[s.b];
     s.cmp_len = p.cu_cmp[s.b + 1] - p.cu_cmp[s.b];
+    if (p.used_cmp) s.cmp_len = min(s.cmp_len, max(p.used_cmp[s.b], 0));
   } else {
     s.cmp_base = 0;
     s.cmp_len = 0;
@@ -101,6 +136,7 @@ __device__ __forceinline__ int n_positions(const Params& p) {
 // `len` is the row's selectable slot count (row_len).
 __device__ __forceinline__ int decode_position(const Params& p, const SeqPos& s,
                                                const int* __restrict__ irow, int pos, int len = 0x7fffffff) {
+  if (!s.active) return -1;   // a padding query row selects nothing
   if (p.select == kSelToken) {
     if (pos >= len) return -1;
     int j = irow[pos];

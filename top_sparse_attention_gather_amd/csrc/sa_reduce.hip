@@ -94,16 +94,18 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
       }
       b = lo;
     }
-    const int kv_base = p.layout == kLayoutBSND ? b * p.Skv : p.cu_kv[b];
-    const int q_base = p.layout == kLayoutBSND ? b * p.Sq : p.cu_q[b];
-    const int q_len = p.layout == kLayoutBSND ? p.Sq : p.cu_q[b + 1] - p.cu_q[b];
-    const int jl = (int)(jg - kv_base);
-    int tl_lo = max(0, jl - p.win_right);
-    int tl_hi = min(q_len - 1, jl + p.win_left);
-    if (p.causal) tl_lo = max(tl_lo, jl);
+    const SeqLens L = seq_lens(p, b);
+    const int jl = (int)(jg - L.kv_base);
+    // query i sits at key position i + L.off; its window is [pos - win_left,
+    // pos + win_right] (and <= pos when causal); kv rows past the used ones
+    // are in no window
+    int tl_lo = max(0, jl - p.win_right - L.off);
+    int tl_hi = min(L.q_len - 1, jl + p.win_left - L.off);
+    if (p.causal) tl_lo = max(tl_lo, jl - L.off);
+    if (jl >= L.kv_len) tl_hi = -1;
     // only query tokens of this chunk contribute
-    tl_lo = max(tl_lo, r.t0 - q_base);
-    tl_hi = min(tl_hi, r.t0 + r.Tc - 1 - q_base);
+    tl_lo = max(tl_lo, r.t0 - L.q_base);
+    tl_hi = min(tl_hi, r.t0 + r.Tc - 1 - L.q_base);
     for (int tb = tl_lo; tb <= tl_hi; tb += kBatch) {
       long long off[kBatch];
       bool ok[kBatch];
@@ -111,7 +113,7 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
       for (int u = 0; u < kBatch; ++u) {
         ok[u] = tb + u <= tl_hi;
         const int tl = ok[u] ? tb + u : tl_lo;
-        off[u] = offset_of((long long)(q_base + tl) * p.Hkv + g, jl - (tl - p.win_left));
+        off[u] = offset_of((long long)(L.q_base + tl) * p.Hkv + g, jl - (tl + L.off - p.win_left));
       }
       add_batch(off, ok);
     }
@@ -134,11 +136,12 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
         }
         b = lo;
       }
-      const int kv_base = p.layout == kLayoutBSND ? b * p.Skv : p.cu_kv[b];
-      const int jl = (int)(jg - kv_base);
+      const SeqLens L = seq_lens(p, b);
+      const int jl = (int)(jg - L.kv_base);
       const long long bkey = (long long)(r.blk_base[b] + jl / p.bs) * p.Hkv + g;
       const int off = jl % p.bs;
-      const int eb = r.row_ptr[bkey], ee = r.row_ptr[bkey + 1];
+      const int eb = r.row_ptr[bkey];
+      const int ee = jl < L.kv_len ? r.row_ptr[bkey + 1] : eb;   // rows past the used ones: nothing
       for (int e = eb; e < ee; e += kBatch) {
         long long offs[kBatch];
         bool ok[kBatch];
