@@ -43,8 +43,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     ("mla_token_8k", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
-        "sha256": "e52f497a9fd5e0c0dd76418c10612d9b72046c0076e6febb7fe5849395125305",
-        "fetch_bytes": 8872933131, "write_bytes": 17519510592,
+        "sha256": "8457a79e756ce2646dd19e8a9aec14aa82e336b5ea847db9d70e2cceaf36cc33",
+        "fetch_bytes": 9525765037, "write_bytes": 17519397696,
     },
 }
 
