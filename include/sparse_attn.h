@@ -52,7 +52,8 @@
  *   TND:   q [total_q, n_q_heads, d_qk], kv [total_kv, n_kv_heads, d], with
  *          cu_seqlens_q / cu_seqlens_kv int32 [batch + 1], cu[0] = 0.
  *   lse, D: [T, n_q_heads] fp32.  topk_indices: [T, n_kv_heads, topk] int32.
- *   q, k, v, kv, cmp_kv, o, d_o and all gradients except dsinks: bf16.
+ *   q, k, v, kv, cmp_kv, o, d_o and all gradients except dsinks: bf16, or
+ *   fp16 with desc->dtype = SA_DTYPE_FP16.
  *   sinks, dsinks: [n_q_heads] fp32.
  *
  * Error behaviour: every entry point returns a status and never aborts.
@@ -93,6 +94,7 @@ typedef enum sa_status {
 enum { SA_SEL_TOKEN = 0, SA_SEL_BLOCK = 1, SA_SEL_WINDOW_CMP = 2 };
 enum { SA_LAYOUT_BSND = 0, SA_LAYOUT_TND = 1 };
 enum { SA_DKV_ATOMIC = 0, SA_DKV_DETERMINISTIC = 1 };
+enum { SA_DTYPE_BF16 = 0, SA_DTYPE_FP16 = 1 };
 
 /* Static problem description (host memory, read during the call only).
  * Attribute names follow the SparseFlashMlaGrad parameter table
@@ -128,6 +130,13 @@ typedef struct sa_desc {
   float scale;          /* softmax scale (finite, > 0) */
   int32_t softmax_l1;   /* 1: the backward also writes the softmax L1-norm
                            side outputs (sa_bwd_args_t); 0: it does not */
+  int32_t dtype;        /* SA_DTYPE_BF16 or SA_DTYPE_FP16: the format of q, k,
+                           v, kv, cmp_kv, o, d_o and of dq, dk, dv, dkv,
+                           d_cmp_kv (SparseFlashMlaGrad README, parameter
+                           table: BFLOAT16 or FLOAT16); products on the
+                           matching MFMA with fp32 accumulation.  The 64-head
+                           MLA kernel and the block key-major kernels are
+                           built for bf16; fp16 runs the generic row kernel */
 } sa_desc_t;
 
 /* Device pointers for the backward.  Unused fields may be NULL.

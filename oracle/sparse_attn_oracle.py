@@ -273,13 +273,14 @@ def sparse_fwd(pb: Problem, tokens: Optional[Sequence[int]] = None) -> Tuple[np.
     return O, L
 
 
-def round_fwd_outputs(O: np.ndarray, lse: np.ndarray) -> Tuple[torch.Tensor, torch.Tensor]:
-    """O -> bf16 (round to nearest even), lse -> fp32: the stored forward
-    outputs that the backward receives as inputs."""
+def round_fwd_outputs(O: np.ndarray, lse: np.ndarray,
+                      dtype: torch.dtype = torch.bfloat16) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O -> bf16 (or `dtype`, round to nearest even), lse -> fp32: the stored
+    forward outputs that the backward receives as inputs."""
     # fp64 -> fp32 -> bf16: the bf16 value is the fp32 value's nearest-even
     # rounding (the stored O is an input to both backwards, so only the fact
     # that both receive the same array matters).
-    return (torch.from_numpy(O).to(torch.float32).to(torch.bfloat16),
+    return (torch.from_numpy(O).to(torch.float32).to(dtype),
             torch.from_numpy(lse).to(torch.float32))
 
 

@@ -19,7 +19,8 @@ def say(*a):
 def oracle_fwd_rounded(inputs, tokens=None):
     pb = O.Problem(inputs)
     out, lse = O.sparse_fwd(pb, tokens)
-    Ob, Lb = O.round_fwd_outputs(out, lse)
+    dt = torch.float16 if getattr(inputs["workload"], "dtype", "bf16") == "fp16" else torch.bfloat16
+    Ob, Lb = O.round_fwd_outputs(out, lse, dt)
     return pb, Ob, Lb
 
 

@@ -80,6 +80,8 @@ def test_phase1_validation_codes():
         "no batch": (dict(batch=0), 2),
         "topk 0": (dict(topk=0), 2),
         "bad softmax_l1 flag": (dict(softmax_l1=2), 7),
+        "bad dtype": (dict(dtype=2), 7),
+        "bad mask mode": (dict(mask_causal=3), 7),
     }
     for name, (over, code) in cases.items():
         if name == "heads not divisible":

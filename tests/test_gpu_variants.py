@@ -157,3 +157,25 @@ def test_fwd_s1_ne_s2_ends_aligned_seqused():
     fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(lse.cpu().numpy()), fin)
     np.testing.assert_allclose(lse.cpu().numpy()[fin], lse_ref[fin], rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref[fin]).max()))
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("name", ["token_gqa_d128_g20", "block_gqa_d128", "mla_64h", "mla_wcmp_sinks_varlen"])
+def test_fp16_inputs(name, mode):
+    """fp16 q, k/v/kv, cmp_kv, O, dO and gradients (fp16 MFMA, fp32
+    accumulation) against the oracle on the same fp16 values."""
+    wl = dataclasses.replace(SMALL[name], dtype="fp16")
+    res, got, ref = U.run_full_case(wl, dkv_mode=MODES[mode], l1=True)
+
+
+@pytest.mark.parametrize("name", ["block_gqa_d128", "mla_wcmp_sinks_varlen"])
+def test_fwd_fp16(name):
+    wl = dataclasses.replace(SMALL[name], dtype="fp16")
+    inp = W.make_inputs(wl)
+    U.say(f"[fwd fp16] {name}")
+    out_ref, lse_ref = O.sparse_fwd(O.Problem(inp))
+    o, lse = B.sparse_attn_fwd(B.make_desc(wl), B.device_tensors(inp))
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    check_close(f"{name}:o", o.float().cpu().numpy(), out_ref)
+    np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))

@@ -22,6 +22,8 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL_PTR", 2: "SA_ERR_BAD_SHAPE", 3: "SA_
                 7: "SA_ERR_BAD_ARG"}
 DKV_ATOMIC = 0
 DKV_DETERMINISTIC = 1
+DTYPE_BF16 = 0
+DTYPE_FP16 = 1
 
 EXPORTED = ["sparse_attn_bwd_workspace_size", "sparse_attn_bwd", "sparse_attn_bwd_timed", "sparse_attn_fwd",
             "sparse_attn_csr_size",
@@ -34,7 +36,8 @@ class SaDesc(ctypes.Structure):
         "layout", "batch", "seqlen_q", "seqlen_kv", "total_q", "total_kv", "total_cmp", "n_q_heads",
         "n_kv_heads", "d_qk", "d_v", "kv_shared", "select", "topk", "block_size", "mask_causal",
         "win_left", "win_right", "cmp_ratio", "has_sinks", "dkv_mode")] + [("scale", ctypes.c_float),
-                                                                           ("softmax_l1", ctypes.c_int32)]
+                                                                           ("softmax_l1", ctypes.c_int32),
+                                                                           ("dtype", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -139,6 +142,7 @@ def make_desc(wl: W.Workload, dkv_mode: int = DKV_ATOMIC, **over) -> SaDesc:
     d.has_sinks = int(wl.has_sinks)
     d.dkv_mode = dkv_mode
     d.scale = wl.softmax_scale
+    d.dtype = DTYPE_FP16 if wl.dtype == "fp16" else DTYPE_BF16
     for k, v in over.items():
         setattr(d, k, v)
     return d
@@ -251,7 +255,7 @@ def sparse_attn_fwd(desc: SaDesc, tensors: Dict[str, torch.Tensor], o: Optional[
     q = tensors["q"]
     T = q.numel() // (desc.n_q_heads * desc.d_qk)
     if o is None:
-        o = torch.empty((T, desc.n_q_heads, desc.d_v), dtype=torch.bfloat16, device=q.device)
+        o = torch.empty((T, desc.n_q_heads, desc.d_v), dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((T, desc.n_q_heads), dtype=torch.float32, device=q.device)
     a = SaFwdArgs()

@@ -41,6 +41,7 @@ sa_status_t validate(const sa_desc_t* d) {
   if (d->has_sinks != 0 && d->has_sinks != 1) return SA_ERR_BAD_ARG;
   if (!std::isfinite(d->scale)) return SA_ERR_BAD_ARG;
   if (d->softmax_l1 != 0 && d->softmax_l1 != 1) return SA_ERR_BAD_ARG;
+  if (d->dtype != SA_DTYPE_BF16 && d->dtype != SA_DTYPE_FP16) return SA_ERR_BAD_ARG;
   if (d->batch < 1 || d->n_q_heads < 0 || d->n_kv_heads < 1) return SA_ERR_BAD_SHAPE;
   if (d->n_q_heads % d->n_kv_heads != 0) return SA_ERR_BAD_SHAPE;
   if (d->d_qk <= 0 || d->d_v <= 0) return SA_ERR_BAD_SHAPE;
@@ -199,6 +200,7 @@ Params make_params(const sa_desc_t* d) {
   p.B = d->batch;
   p.Sq = d->seqlen_q;
   p.Skv = d->seqlen_kv;
+  p.fp16 = d->dtype == SA_DTYPE_FP16 ? 1 : 0;
   p.scale = d->scale;
   return p;
 }
@@ -394,7 +396,7 @@ sa_status_t sparse_attn_indexer_grad_kl_timed(const sa_indexer_desc_t* desc, con
     SA_TRY_HIP(sa::launch_reduce(p, r, s));
     first = false;
   }
-  SA_TRY_HIP(sa::launch_cast_bf16(acc, static_cast<bf16*>(a->dk), (size_t)nk * desc->d, s));
+  SA_TRY_HIP(sa::launch_cast(acc, a->dk, (size_t)nk * desc->d, 0, s));
   // loss = fixed-order sum of the per-token losses (the dSinks reduction
   // over one "head")
   Params pl = p;
@@ -501,9 +503,9 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     SA_TRY_HIP(sa::launch_bwd_rows(p, w, s));
     if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
     SA_TRY_HIP(l1_norm());
-    SA_TRY_HIP(sa::launch_cast_bf16(w.acc_k, static_cast<bf16*>(desc->kv_shared ? a->dkv : a->dk), nk, s));
-    if (nv) SA_TRY_HIP(sa::launch_cast_bf16(w.acc_v, static_cast<bf16*>(a->dv), nv, s));
-    if (nc) SA_TRY_HIP(sa::launch_cast_bf16(w.acc_cmp, static_cast<bf16*>(a->d_cmp_kv), nc, s));
+    SA_TRY_HIP(sa::launch_cast(w.acc_k, desc->kv_shared ? a->dkv : a->dk, nk, p.fp16, s));
+    if (nv) SA_TRY_HIP(sa::launch_cast(w.acc_v, a->dv, nv, p.fp16, s));
+    if (nc) SA_TRY_HIP(sa::launch_cast(w.acc_cmp, a->d_cmp_kv, nc, p.fp16, s));
     return SA_OK;
   }
 
@@ -586,10 +588,10 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   SA_TRY_HIP(l1_norm());
   bf16* out_a = static_cast<bf16*>(desc->kv_shared ? a->dkv : a->dk);
   bf16* out_b = desc->kv_shared ? nullptr : static_cast<bf16*>(a->dv);
-  SA_TRY_HIP(sa::launch_split_cast(acc, r.n_kv_out, L.RW, desc->d_qk, out_a, out_b, s));
+  SA_TRY_HIP(sa::launch_split_cast(acc, r.n_kv_out, L.RW, desc->d_qk, out_a, out_b, p.fp16, s));
   if (desc->select == SA_SEL_WINDOW_CMP)
-    SA_TRY_HIP(sa::launch_cast_bf16(acc + r.n_kv_out * L.RW, static_cast<bf16*>(a->d_cmp_kv),
-                                    (size_t)(r.n_out_rows - r.n_kv_out) * L.RW, s));
+    SA_TRY_HIP(sa::launch_cast(acc + r.n_kv_out * L.RW, a->d_cmp_kv, (size_t)(r.n_out_rows - r.n_kv_out) * L.RW,
+                               p.fp16, s));
   return SA_OK;
 }
 
@@ -622,7 +624,7 @@ sa_status_t sparse_attn_fwd(const sa_desc_t* desc, const sa_fwd_args_t* a, void*
   p.used_q = a->seqused_q;
   p.used_kv = a->seqused_kv;
   p.used_cmp = a->seqused_cmp;
-  SA_TRY_HIP(sa::launch_fwd_rows(p, static_cast<bf16*>(a->o), a->lse, reinterpret_cast<hipStream_t>(stream)));
+  SA_TRY_HIP(sa::launch_fwd_rows(p, a->o, a->lse, reinterpret_cast<hipStream_t>(stream)));
   return SA_OK;
 }
 

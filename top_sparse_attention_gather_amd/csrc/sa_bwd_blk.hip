@@ -486,7 +486,7 @@ __global__ void blk_sum_cast_kernel(Params p, BlkArgs a, long long n_rows, bf16*
 }  // namespace
 
 bool blk_dkv_supported(const Params& p) {
-  return p.select == kSelBlock && !p.shared && p.dqk == p.dv && (p.dqk == 64 || p.dqk == 128) && p.bs >= 1 &&
+  return !p.fp16 && p.select == kSelBlock && !p.shared && p.dqk == p.dv && (p.dqk == 64 || p.dqk == 128) && p.bs >= 1 &&
          p.bs <= 64;
 }
 

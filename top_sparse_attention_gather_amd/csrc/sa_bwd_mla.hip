@@ -475,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
 }  // namespace
 
 bool mla_bwd_supported(const Params& p) {
-  return p.shared && p.dqk == kDQK && p.dv == kDV && p.G % kHeads == 0 && p.select != kSelBlock &&
+  return !p.fp16 && p.shared && p.dqk == kDQK && p.dv == kDV && p.G % kHeads == 0 && p.select != kSelBlock &&
          (p.select == kSelToken ? p.topk : p.win_left + 1 + p.win_right + p.topk) <= kMaxPos;
 }
 

@@ -27,8 +27,9 @@ constexpr int kMaxPos = 2048;  // positions compacted per pass
 
 // ---------------------------------------------------------------------------
 // D = rowsum(dO * O) per (token, head); with sinks also the row's dSinks term
-// -exp(sink_h - lse) * D.  TPR threads per row, 8 bf16 per thread per step.
-template <int TPR>
+// -exp(sink_h - lse) * D.  TPR threads per row, 8 elements (bf16 or fp16,
+// E) per thread per step.
+template <int TPR, typename E>
 __global__ __launch_bounds__(kThreads) void preprocess_kernel(Params p, float* __restrict__ D,
                                                               float* __restrict__ sink_term) {
   const int rows = p.T * p.Hq;
@@ -36,13 +37,13 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(Params p, float* _
   const int sub = threadIdx.x % TPR;
   float acc = 0.f;
   if (row < rows) {
-    const uint4* po = reinterpret_cast<const uint4*>(p.o + (size_t)row * p.dv);
-    const uint4* pd = reinterpret_cast<const uint4*>(p.dO + (size_t)row * p.dv);
+    const uint4* po = reinterpret_cast<const uint4*>(reinterpret_cast<const E*>(p.o) + (size_t)row * p.dv);
+    const uint4* pd = reinterpret_cast<const uint4*>(reinterpret_cast<const E*>(p.dO) + (size_t)row * p.dv);
     for (int c = sub; c < p.dv / 8; c += TPR) {
       uint4 a = po[c];
       uint4 b = pd[c];
-      const bf16* ea = reinterpret_cast<const bf16*>(&a);
-      const bf16* eb = reinterpret_cast<const bf16*>(&b);
+      const E* ea = reinterpret_cast<const E*>(&a);
+      const E* eb = reinterpret_cast<const E*>(&b);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc += (float)ea[i] * (float)eb[i];
     }
@@ -87,10 +88,11 @@ __global__ __launch_bounds__(kThreads) void dsinks_kernel(Params p, const float*
   if (threadIdx.x == 0) dsinks[h] = (float)part[0];
 }
 
-__global__ void cast_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, size_t n) {
+template <typename E>
+__global__ void cast_kernel(const float* __restrict__ src, E* __restrict__ dst, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
-    dst[i] = (bf16)src[i];
+    dst[i] = (E)src[i];
 }
 
 // Softmax L1-norm outputs (SparseFlashMlaGrad README, parameter table;
@@ -143,8 +145,10 @@ __global__ __launch_bounds__(kThreads) void l1_norm_kernel(Params p, const float
   }
 }
 
-template <int DQK, int DV, bool SHARED>
+template <int DQK, int DV, bool SHARED, typename E>
 __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers w) {
+  typedef typename Elem<E>::V8 V8;
+  typedef typename Elem<E>::V4 V4;
   constexpr int QS = DQK + 8;   // LDS row stride (elements) of Q and K tiles
   constexpr int VS = DV + 8;    // of dO and V tiles
   constexpr int PS = kNT + 8;   // of P / dS  [head][key]
@@ -154,16 +158,16 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
   constexpr int NQB_W = (NQB + 3) / 4;
   static_assert(DQK % 32 == 0 && DV % 32 == 0 && DV <= DQK, "head dims");
 
-  __shared__ __attribute__((aligned(16))) bf16 sQ[kHC * QS];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[kHC * VS];
-  __shared__ __attribute__((aligned(16))) bf16 sK[kNT * QS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[SHARED ? 8 : kNT * VS];
+  __shared__ __attribute__((aligned(16))) E sQ[kHC * QS];
+  __shared__ __attribute__((aligned(16))) E sdO[kHC * VS];
+  __shared__ __attribute__((aligned(16))) E sK[kNT * QS];
+  __shared__ __attribute__((aligned(16))) E sV[SHARED ? 8 : kNT * VS];
   __shared__ float sS[kHC * kNT];
   __shared__ float sdP[kHC * kNT];
-  __shared__ __attribute__((aligned(16))) bf16 sP[kHC * PS];
-  __shared__ __attribute__((aligned(16))) bf16 sdS[kHC * PS];
-  __shared__ __attribute__((aligned(16))) bf16 sPt[kNT * TS];
-  __shared__ __attribute__((aligned(16))) bf16 sdSt[kNT * TS];
+  __shared__ __attribute__((aligned(16))) E sP[kHC * PS];
+  __shared__ __attribute__((aligned(16))) E sdS[kHC * PS];
+  __shared__ __attribute__((aligned(16))) E sPt[kNT * TS];
+  __shared__ __attribute__((aligned(16))) E sdSt[kNT * TS];
   __shared__ int sRows[kMaxPos];
   __shared__ int sVpos[kMaxPos];
   __shared__ float sL[kHC], sD[kHC];
@@ -177,21 +181,24 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
   const int Gc = min(kHC, p.G - blockIdx.y * kHC);
   const SeqPos s = seq_pos(p, t);
   const int* irow = p.idx + (size_t)row * p.topk;
-  const bf16* Kbase = SHARED ? p.k : p.k;
-  const bf16* Vbase = SHARED ? p.k : p.v;
-  const bf16 zero = (bf16)0.f;
+  const E* Qg = reinterpret_cast<const E*>(p.q);
+  const E* dOg = reinterpret_cast<const E*>(p.dO);
+  const E* Cg = reinterpret_cast<const E*>(p.cmp);
+  const E* Kbase = reinterpret_cast<const E*>(p.k);
+  const E* Vbase = reinterpret_cast<const E*>(SHARED ? p.k : p.v);
+  E* dQg = reinterpret_cast<E*>(w.dq);
 
   // Q and dO of the chunk's heads (zero rows past Gc), lse and D.
   for (int c = tid; c < kHC * (DQK / 8); c += kThreads) {
     const int h = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (h < Gc) v = *reinterpret_cast<const uint4*>(p.q + ((size_t)t * p.Hq + h0 + h) * DQK + col);
+    if (h < Gc) v = *reinterpret_cast<const uint4*>(Qg + ((size_t)t * p.Hq + h0 + h) * DQK + col);
     *reinterpret_cast<uint4*>(&sQ[h * QS + col]) = v;
   }
   for (int c = tid; c < kHC * (DV / 8); c += kThreads) {
     const int h = c / (DV / 8), col = (c % (DV / 8)) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (h < Gc) v = *reinterpret_cast<const uint4*>(p.dO + ((size_t)t * p.Hq + h0 + h) * DV + col);
+    if (h < Gc) v = *reinterpret_cast<const uint4*>(dOg + ((size_t)t * p.Hq + h0 + h) * DV + col);
     *reinterpret_cast<uint4*>(&sdO[h * VS + col]) = v;
   }
   if (tid < kHC) {
@@ -216,8 +223,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
         uint4 v = make_uint4(0, 0, 0, 0);
         if (k0 + r < cnt) {
           const int code = sRows[k0 + r];
-          const bf16* src = (code & kCmpFlag) ? p.cmp + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * DQK
-                                              : Kbase + ((size_t)code * p.Hkv + g) * DQK;
+          const E* src = (code & kCmpFlag) ? Cg + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * DQK
+                                           : Kbase + ((size_t)code * p.Hkv + g) * DQK;
           v = *reinterpret_cast<const uint4*>(src + col);
         }
         *reinterpret_cast<uint4*>(&sK[r * QS + col]) = v;
@@ -242,20 +249,20 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
         if (wv < 2) {
 #pragma unroll 2
           for (int kk = 0; kk < DQK / 32; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[l16 * QS + kk * 32 + lq * 8]);
-            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sK[(kb * 16 + l16) * QS + kk * 32 + lq * 8]);
-            acc = mfma16x16x32(a, b, acc);
+            const V8 a = *reinterpret_cast<const V8*>(&sQ[l16 * QS + kk * 32 + lq * 8]);
+            const V8 b = *reinterpret_cast<const V8*>(&sK[(kb * 16 + l16) * QS + kk * 32 + lq * 8]);
+            acc = Elem<E>::mma32(a, b, acc);
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) sS[(lq * 4 + i) * kNT + kb * 16 + l16] = acc[i];
         } else {
-          const bf16* vt = SHARED ? sK : sV;
+          const E* vt = SHARED ? sK : sV;
           constexpr int VT = SHARED ? QS : VS;
 #pragma unroll 2
           for (int kk = 0; kk < DV / 32; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sdO[l16 * VS + kk * 32 + lq * 8]);
-            const bf16x8 b = *reinterpret_cast<const bf16x8*>(&vt[(kb * 16 + l16) * VT + kk * 32 + lq * 8]);
-            acc = mfma16x16x32(a, b, acc);
+            const V8 a = *reinterpret_cast<const V8*>(&sdO[l16 * VS + kk * 32 + lq * 8]);
+            const V8 b = *reinterpret_cast<const V8*>(&vt[(kb * 16 + l16) * VT + kk * 32 + lq * 8]);
+            acc = Elem<E>::mma32(a, b, acc);
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) sdP[(lq * 4 + i) * kNT + kb * 16 + l16] = acc[i];
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
         float pv = 0.f;
         if (k0 + j < cnt && l > -INFINITY) pv = __expf(sS[e] * p.scale - l);
         const float ds = pv * (sdP[e] - sD[h]);
-        const bf16 pb = (bf16)pv, db = (bf16)ds;
+        const E pb = (E)pv, db = (E)ds;
         sP[h * PS + j] = pb;
         sdS[h * PS + j] = db;
         if (!w.dq_only) {
@@ -294,15 +301,15 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
 
       // ---- dQ += dS K (column blocks split over the 4 waves) ----------------
       {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sdS[l16 * PS + lq * 8]);
+        const V8 a = *reinterpret_cast<const V8*>(&sdS[l16 * PS + lq * 8]);
 #pragma unroll
         for (int i = 0; i < NQB_W; ++i) {
           const int cb = wv + 4 * i;
           if (cb < NQB) {
-            bf16x8 b;
+            V8 b;
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) b[jj] = sK[(lq * 8 + jj) * QS + cb * 16 + l16];
-            accQ[i] = mfma16x16x32(a, b, accQ[i]);
+            accQ[i] = Elem<E>::mma32(a, b, accQ[i]);
           }
         }
       }
@@ -317,19 +324,19 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
           if (is_v) cb -= NQB;
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           if (!is_v) {
-            const i16x4 a = *reinterpret_cast<const i16x4*>(&sdSt[(kb * 16 + l16) * TS + lq * 4]);
-            i16x4 b;
+            const V4 a = *reinterpret_cast<const V4*>(&sdSt[(kb * 16 + l16) * TS + lq * 4]);
+            V4 b;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) b[jj] = bf16_bits(sQ[(lq * 4 + jj) * QS + cb * 16 + l16]);
-            acc = mfma16x16x16(a, b, acc);
+            for (int jj = 0; jj < 4; ++jj) b[jj] = sQ[(lq * 4 + jj) * QS + cb * 16 + l16];
+            acc = Elem<E>::mma16(a, b, acc);
             acc *= p.scale;
           }
           if (is_v || (SHARED && cb < NVB)) {
-            const i16x4 a = *reinterpret_cast<const i16x4*>(&sPt[(kb * 16 + l16) * TS + lq * 4]);
-            i16x4 b;
+            const V4 a = *reinterpret_cast<const V4*>(&sPt[(kb * 16 + l16) * TS + lq * 4]);
+            V4 b;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) b[jj] = bf16_bits(sdO[(lq * 4 + jj) * VS + cb * 16 + l16]);
-            acc = mfma16x16x16(a, b, acc);
+            for (int jj = 0; jj < 4; ++jj) b[jj] = sdO[(lq * 4 + jj) * VS + cb * 16 + l16];
+            acc = Elem<E>::mma16(a, b, acc);
           }
           if (w.det) {
             // one partial row per (head chunk, token row, position)
@@ -365,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
     }
   }
 
-  // ---- dQ out (bf16) ---------------------------------------------------------
+  // ---- dQ out ------------------------------------------------------------------
 #pragma unroll
   for (int i = 0; i < NQB_W; ++i) {
     const int cb = wv + 4 * i;
@@ -373,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = lq * 4 + r;
-        if (h < Gc) w.dq[((size_t)t * p.Hq + h0 + h) * DQK + cb * 16 + l16] = (bf16)(accQ[i][r] * p.scale);
+        if (h < Gc) dQg[((size_t)t * p.Hq + h0 + h) * DQK + cb * 16 + l16] = (E)(accQ[i][r] * p.scale);
       }
     }
   }
@@ -382,7 +389,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(Params p, BwdBuffers
 template <int DQK, int DV, bool SHARED>
 hipError_t launch_rows_t(const Params& p, const BwdBuffers& w, hipStream_t s) {
   dim3 grid((unsigned)(w.Tc * p.Hkv), (unsigned)((p.G + kHC - 1) / kHC));
-  hipLaunchKernelGGL((bwd_rows_kernel<DQK, DV, SHARED>), grid, dim3(kThreads), 0, s, p, w);
+  if (p.fp16) hipLaunchKernelGGL((bwd_rows_kernel<DQK, DV, SHARED, f16>), grid, dim3(kThreads), 0, s, p, w);
+  else hipLaunchKernelGGL((bwd_rows_kernel<DQK, DV, SHARED, bf16>), grid, dim3(kThreads), 0, s, p, w);
   return hipGetLastError();
 }
 
@@ -401,16 +409,24 @@ hipError_t launch_bwd_rows(const Params& p, const BwdBuffers& w, hipStream_t s) 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_preprocess(const Params& p, const BwdBuffers& w, hipStream_t s) {
+template <typename E>
+void launch_preprocess_t(const Params& p, const BwdBuffers& w, hipStream_t s) {
   const int rows = p.T * p.Hq;
   const int cpr = p.dv / 8;   // 16-byte chunks per row
   if (cpr >= 64) {
-    hipLaunchKernelGGL(preprocess_kernel<64>, dim3((rows + 3) / 4), dim3(kThreads), 0, s, p, w.D, w.sink_term);
+    hipLaunchKernelGGL((preprocess_kernel<64, E>), dim3((rows + 3) / 4), dim3(kThreads), 0, s, p, w.D, w.sink_term);
   } else if (cpr >= 16) {
-    hipLaunchKernelGGL(preprocess_kernel<16>, dim3((rows + 15) / 16), dim3(kThreads), 0, s, p, w.D, w.sink_term);
+    hipLaunchKernelGGL((preprocess_kernel<16, E>), dim3((rows + 15) / 16), dim3(kThreads), 0, s, p, w.D,
+                       w.sink_term);
   } else {
-    hipLaunchKernelGGL(preprocess_kernel<8>, dim3((rows + 31) / 32), dim3(kThreads), 0, s, p, w.D, w.sink_term);
+    hipLaunchKernelGGL((preprocess_kernel<8, E>), dim3((rows + 31) / 32), dim3(kThreads), 0, s, p, w.D,
+                       w.sink_term);
   }
+}
+
+hipError_t launch_preprocess(const Params& p, const BwdBuffers& w, hipStream_t s) {
+  if (p.fp16) launch_preprocess_t<f16>(p, w, s);
+  else launch_preprocess_t<bf16>(p, w, s);
   return hipGetLastError();
 }
 
@@ -438,10 +454,11 @@ hipError_t launch_dsinks(const Params& p, const BwdBuffers& w, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_cast_bf16(const float* src, bf16* dst, size_t n, hipStream_t s) {
+hipError_t launch_cast(const float* src, void* dst, size_t n, int fp16, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 16384);
-  hipLaunchKernelGGL(cast_bf16_kernel, dim3(blocks), dim3(256), 0, s, src, dst, n);
+  if (fp16) hipLaunchKernelGGL(cast_kernel<f16>, dim3(blocks), dim3(256), 0, s, src, static_cast<f16*>(dst), n);
+  else hipLaunchKernelGGL(cast_kernel<bf16>, dim3(blocks), dim3(256), 0, s, src, static_cast<bf16*>(dst), n);
   return hipGetLastError();
 }
 

@@ -7,6 +7,10 @@
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -29,6 +33,7 @@ constexpr int kCmpFlag = 1 << 30;
 struct Params {
   int T, Hq, Hkv, G, dqk, dv, topk, bs, select, causal, win_left, win_right, cmp_ratio;
   int has_sinks, shared, layout, B, Sq, Skv;
+  int fp16;            // 1: the 16-bit tensors (q, k, v, cmp, o, dO, gradients) are fp16, else bf16
   float scale;
   const bf16* q;
   const bf16* k;      // K rows, or the shared KV rows
@@ -242,6 +247,36 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
 }
 
 __device__ __forceinline__ short bf16_bits(bf16 x) { return __builtin_bit_cast(short, x); }
+
+// The two 16-bit input formats: 8- and 4-element operand vectors and the
+// 16x16x32 / 16x16x16 MFMA products (fp32 accumulate) on each.
+template <typename E>
+struct Elem;
+
+template <>
+struct Elem<bf16> {
+  typedef bf16x8 V8;
+  typedef bf16x4 V4;
+  __device__ static f32x4 mma32(const V8& a, const V8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static f32x4 mma16(const V4& a, const V4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
+                                                      0, 0, 0);
+  }
+};
+
+template <>
+struct Elem<f16> {
+  typedef f16x8 V8;
+  typedef f16x4 V4;
+  __device__ static f32x4 mma32(const V8& a, const V8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static f32x4 mma16(const V4& a, const V4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+};
 
 // Sum over each row of 16 lanes, the result in all 16 (DPP: swap
 // neighbours, swap pairs, mirror within 8, mirror within 16).  Every lane

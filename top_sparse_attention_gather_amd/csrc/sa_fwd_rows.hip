@@ -4,7 +4,7 @@
 //
 // One workgroup of 4 waves owns one (token, kv head) row and up to 16 of its
 // query heads, compacts the row's selected rows into LDS and walks them in
-// tiles of 32 keys with an online softmax: S = Q K^T on bf16 MFMA, running
+// tiles of 32 keys with an online softmax: S = Q K^T on MFMA (bf16 or fp16), running
 // max / sum per head in LDS, O += P V on MFMA with the fp32 accumulator in
 // registers.  A sink logit enters as the initial running max with sum 1.
 #include "sa_launch.h"
@@ -18,8 +18,8 @@ constexpr int kNT = 32;
 constexpr int kHC = 16;
 constexpr int kMaxPos = 2048;
 
-template <int DQK, int DV, bool SHARED>
-__global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __restrict__ out_o,
+template <int DQK, int DV, bool SHARED, typename E>
+__global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restrict__ out_o,
                                                             float* __restrict__ out_lse) {
   constexpr int QS = DQK + 8;
   constexpr int VS = DV + 8;
@@ -28,11 +28,12 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __re
   constexpr int NVB_W = (NVB + 3) / 4;
   static_assert(DQK % 32 == 0 && DV % 32 == 0 && DV <= DQK, "head dims");
 
-  __shared__ __attribute__((aligned(16))) bf16 sQ[kHC * QS];
-  __shared__ __attribute__((aligned(16))) bf16 sK[kNT * QS];
-  __shared__ __attribute__((aligned(16))) bf16 sV[SHARED ? 8 : kNT * VS];
+  typedef typename Elem<E>::V8 V8;
+  __shared__ __attribute__((aligned(16))) E sQ[kHC * QS];
+  __shared__ __attribute__((aligned(16))) E sK[kNT * QS];
+  __shared__ __attribute__((aligned(16))) E sV[SHARED ? 8 : kNT * VS];
   __shared__ float sS[kHC * kNT];
-  __shared__ __attribute__((aligned(16))) bf16 sP[kHC * PS];
+  __shared__ __attribute__((aligned(16))) E sP[kHC * PS];
   __shared__ float sM[kHC], sL[kHC], sAlpha[kHC];
   __shared__ int sRows[kMaxPos];
   __shared__ int sWave[4];
@@ -45,12 +46,15 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __re
   const int Gc = min(kHC, p.G - blockIdx.y * kHC);
   const SeqPos s = seq_pos(p, t);
   const int* irow = p.idx + (size_t)row * p.topk;
-  const bf16* Vbase = SHARED ? p.k : p.v;
+  const E* Qg = reinterpret_cast<const E*>(p.q);
+  const E* Kg = reinterpret_cast<const E*>(p.k);
+  const E* Cg = reinterpret_cast<const E*>(p.cmp);
+  const E* Vbase = reinterpret_cast<const E*>(SHARED ? p.k : p.v);
 
   for (int c = tid; c < kHC * (DQK / 8); c += kThreads) {
     const int h = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (h < Gc) v = *reinterpret_cast<const uint4*>(p.q + ((size_t)t * p.Hq + h0 + h) * DQK + col);
+    if (h < Gc) v = *reinterpret_cast<const uint4*>(Qg + ((size_t)t * p.Hq + h0 + h) * DQK + col);
     *reinterpret_cast<uint4*>(&sQ[h * QS + col]) = v;
   }
   if (tid < kHC) {
@@ -75,8 +79,8 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __re
         uint4 v = make_uint4(0, 0, 0, 0);
         if (k0 + r < cnt) {
           const int code = sRows[k0 + r];
-          const bf16* src = (code & kCmpFlag) ? p.cmp + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * DQK
-                                              : p.k + ((size_t)code * p.Hkv + g) * DQK;
+          const E* src = (code & kCmpFlag) ? Cg + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * DQK
+                                           : Kg + ((size_t)code * p.Hkv + g) * DQK;
           v = *reinterpret_cast<const uint4*>(src + col);
         }
         *reinterpret_cast<uint4*>(&sK[r * QS + col]) = v;
@@ -99,9 +103,9 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __re
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
         for (int kk = 0; kk < DQK / 32; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[l16 * QS + kk * 32 + lq * 8]);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sK[(kb * 16 + l16) * QS + kk * 32 + lq * 8]);
-          acc = mfma16x16x32(a, b, acc);
+          const V8 a = *reinterpret_cast<const V8*>(&sQ[l16 * QS + kk * 32 + lq * 8]);
+          const V8 b = *reinterpret_cast<const V8*>(&sK[(kb * 16 + l16) * QS + kk * 32 + lq * 8]);
+          acc = Elem<E>::mma32(a, b, acc);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) sS[(lq * 4 + i) * kNT + kb * 16 + l16] = acc[i];
@@ -124,8 +128,8 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __re
         float sum = p0 + p1;
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
-        sP[h * PS + part * 2] = (bf16)p0;
-        sP[h * PS + part * 2 + 1] = (bf16)p1;
+        sP[h * PS + part * 2] = (E)p0;
+        sP[h * PS + part * 2 + 1] = (E)p1;
         __syncthreads();   // every thread has read sM[h] before it changes
         if (part == 0) {
           const float alpha = __expf(m_old - base);
@@ -137,9 +141,9 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __re
       __syncthreads();
 
       {
-        const bf16* vt = SHARED ? sK : sV;
+        const E* vt = SHARED ? sK : sV;
         constexpr int VT = SHARED ? QS : VS;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sP[l16 * PS + lq * 8]);
+        const V8 a = *reinterpret_cast<const V8*>(&sP[l16 * PS + lq * 8]);
         f32x4 al;
 #pragma unroll
         for (int r = 0; r < 4; ++r) al[r] = sAlpha[lq * 4 + r];
@@ -147,10 +151,10 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __re
         for (int i = 0; i < NVB_W; ++i) {
           const int cb = wv + 4 * i;
           if (cb < NVB) {
-            bf16x8 b;
+            V8 b;
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) b[jj] = vt[(lq * 8 + jj) * VT + cb * 16 + l16];
-            accO[i] = mfma16x16x32(a, b, accO[i] * al);
+            accO[i] = Elem<E>::mma32(a, b, accO[i] * al);
           }
         }
       }
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __re
         if (h < Gc) {
           const float l = sL[h];
           const float o = l > 0.f ? accO[i][r] / l : 0.f;
-          out_o[((size_t)t * p.Hq + h0 + h) * DV + cb * 16 + l16] = (bf16)o;
+          out_o[((size_t)t * p.Hq + h0 + h) * DV + cb * 16 + l16] = (E)o;
         }
       }
     }
@@ -180,9 +184,13 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, bf16* __re
 }
 
 template <int DQK, int DV, bool SHARED>
-hipError_t launch_t(const Params& p, bf16* o, float* lse, hipStream_t s) {
+hipError_t launch_t(const Params& p, void* o, float* lse, hipStream_t s) {
   dim3 grid((unsigned)(p.T * p.Hkv), (unsigned)((p.G + kHC - 1) / kHC));
-  hipLaunchKernelGGL((fwd_rows_kernel<DQK, DV, SHARED>), grid, dim3(kThreads), 0, s, p, o, lse);
+  if (p.fp16)
+    hipLaunchKernelGGL((fwd_rows_kernel<DQK, DV, SHARED, f16>), grid, dim3(kThreads), 0, s, p, static_cast<f16*>(o), lse);
+  else
+    hipLaunchKernelGGL((fwd_rows_kernel<DQK, DV, SHARED, bf16>), grid, dim3(kThreads), 0, s, p, static_cast<bf16*>(o),
+                       lse);
   return hipGetLastError();
 }
 
@@ -192,7 +200,7 @@ bool fwd_rows_supported(int dqk, int dv, int shared) {
   return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 576 && dv == 512);
 }
 
-hipError_t launch_fwd_rows(const Params& p, bf16* o, float* lse, hipStream_t s) {
+hipError_t launch_fwd_rows(const Params& p, void* o, float* lse, hipStream_t s) {
   if (p.dqk == 64 && p.dv == 64) return p.shared ? launch_t<64, 64, true>(p, o, lse, s) : launch_t<64, 64, false>(p, o, lse, s);
   if (p.dqk == 128 && p.dv == 128) return p.shared ? launch_t<128, 128, true>(p, o, lse, s) : launch_t<128, 128, false>(p, o, lse, s);
   if (p.dqk == 576 && p.dv == 512) return p.shared ? launch_t<576, 512, true>(p, o, lse, s) : launch_t<576, 512, false>(p, o, lse, s);

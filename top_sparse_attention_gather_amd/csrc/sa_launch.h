@@ -54,11 +54,12 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 hipError_t launch_preprocess(const Params& p, const BwdBuffers& w, hipStream_t s);
 hipError_t launch_bwd_rows(const Params& p, const BwdBuffers& w, hipStream_t s);
 hipError_t launch_dsinks(const Params& p, const BwdBuffers& w, hipStream_t s);
-hipError_t launch_cast_bf16(const float* src, bf16* dst, size_t n, hipStream_t s);
+// fp32 -> bf16 (fp16 = 0) or fp16 (fp16 = 1), round to nearest even
+hipError_t launch_cast(const float* src, void* dst, size_t n, int fp16, hipStream_t s);
 bool bwd_rows_supported(int dqk, int dv, int shared);
 int bwd_rows_head_chunks(const Params& p);
 
-hipError_t launch_fwd_rows(const Params& p, bf16* o, float* lse, hipStream_t s);
+hipError_t launch_fwd_rows(const Params& p, void* o, float* lse, hipStream_t s);
 bool fwd_rows_supported(int dqk, int dv, int shared);
 
 // CSR transpose of the index lists of tokens [t0, t1): row_ptr[n_keys + 1]
@@ -69,7 +70,8 @@ hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_key
                                 int* row_ptr, int* entries, void* ws, hipStream_t s);
 
 hipError_t launch_reduce(const Params& p, const ReduceArgs& r, hipStream_t s);
-hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk, bf16* a, bf16* b, hipStream_t s);
+hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk, void* a, void* b, int fp16,
+                             hipStream_t s);
 
 // Softmax L1-norm outputs from the head-chunk sums `l1` ([n_hg][T * Hkv]
 // [npos]): per (token, kv head) row, the chunk sums of every used position

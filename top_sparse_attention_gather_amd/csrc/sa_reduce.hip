@@ -187,14 +187,15 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
 
 // fp32 accumulator rows [n][RW] -> bf16 outputs: first dqk columns to
 // `a`, the next dv columns (separate K/V) to `b`.
-__global__ void split_cast_kernel(const float* __restrict__ acc, long long n, int RW, int dqk, bf16* __restrict__ a,
-                                  bf16* __restrict__ b) {
+template <typename E>
+__global__ void split_cast_kernel(const float* __restrict__ acc, long long n, int RW, int dqk, E* __restrict__ a,
+                                  E* __restrict__ b) {
   const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
   if (i >= n * RW) return;
   const long long row = i / RW;
   const int c = (int)(i - row * RW);
-  if (c < dqk) a[row * dqk + c] = (bf16)acc[i];
-  else b[row * (RW - dqk) + (c - dqk)] = (bf16)acc[i];
+  if (c < dqk) a[row * dqk + c] = (E)acc[i];
+  else b[row * (RW - dqk) + (c - dqk)] = (E)acc[i];
 }
 
 }  // namespace
@@ -213,11 +214,17 @@ hipError_t launch_reduce(const Params& p, const ReduceArgs& r, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk, bf16* a, bf16* b, hipStream_t s) {
+hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk, void* a, void* b, int fp16,
+                             hipStream_t s) {
   const long long n = n_rows * RW;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(split_cast_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, acc, n_rows, RW, dqk, a,
-                     b);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (fp16)
+    hipLaunchKernelGGL(split_cast_kernel<f16>, grid, dim3(256), 0, s, acc, n_rows, RW, dqk, static_cast<f16*>(a),
+                       static_cast<f16*>(b));
+  else
+    hipLaunchKernelGGL(split_cast_kernel<bf16>, grid, dim3(256), 0, s, acc, n_rows, RW, dqk, static_cast<bf16*>(a),
+                       static_cast<bf16*>(b));
   return hipGetLastError();
 }
 

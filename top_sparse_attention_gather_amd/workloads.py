@@ -70,6 +70,7 @@ class Workload:
     cmp_noise_std: float = 0.1
     seed: int = 0
     kv_seqlens: tuple = ()           # per-sequence kv lengths when they differ from the query's
+    dtype: str = "bf16"              # format of the 16-bit tensors: "bf16" or "fp16"
     mask_causal: int = 1             # 1: key <= query position (top-left); 2: aligned at the ends (bottom-right)
 
     # -- derived sizes -------------------------------------------------
@@ -218,9 +219,11 @@ def _normal_f32(ss: np.random.SeedSequence, shape: Sequence[int], std: float = 1
     return out.reshape(shape)
 
 
-def _to_bf16(a: np.ndarray) -> torch.Tensor:
-    """Round-to-nearest-even fp32 -> bf16 (torch's conversion)."""
-    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16)
+def _to_bf16(a: np.ndarray, dtype: str = "bf16") -> torch.Tensor:
+    """Round-to-nearest-even fp32 -> bf16 (or fp16 with dtype="fp16"),
+    torch's conversion."""
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(torch.float16 if dtype == "fp16" else torch.bfloat16)
 
 
 def _rows_self_plus_uniform(rng, t: int, k: int) -> np.ndarray:
@@ -314,16 +317,16 @@ def make_inputs(wl: Workload, with_indices: bool = True, threads: int = 8) -> Di
     st = _streams(wl.seed)
     T, Hq, Hkv = wl.total_q, wl.n_q_heads, wl.n_kv_heads
     out: Dict[str, object] = {"workload": wl}
-    out["q"] = _to_bf16(_normal_f32(st["q"], (T, Hq, wl.d_qk), threads=threads))
+    out["q"] = _to_bf16(_normal_f32(st["q"], (T, Hq, wl.d_qk), threads=threads), wl.dtype)
     if wl.kv_shared:
         kv32 = _normal_f32(st["kv"], (wl.total_kv, Hkv, wl.d_qk), std=wl.kv_std, threads=threads)
-        out["kv"] = _to_bf16(kv32)
+        out["kv"] = _to_bf16(kv32, wl.dtype)
     else:
         out["k"] = _to_bf16(_normal_f32(st["kv"], (wl.total_kv, Hkv, wl.d_qk), std=wl.kv_std,
-                                        threads=threads))
+                                        threads=threads), wl.dtype)
         out["v"] = _to_bf16(_normal_f32(st["v"], (wl.total_kv, Hkv, wl.d_v), std=wl.kv_std,
-                                        threads=threads))
-    out["d_o"] = _to_bf16(_normal_f32(st["do"], (T, Hq, wl.d_v), threads=threads))
+                                        threads=threads), wl.dtype)
+    out["d_o"] = _to_bf16(_normal_f32(st["do"], (T, Hq, wl.d_v), threads=threads), wl.dtype)
     if wl.select == SEL_WINDOW_CMP:
         # cmp_kv row j of a sequence = mean of its ori rows [r*j, r*j + r), taken
         # in fp32 over the bf16 values, plus N(0, noise_std^2) noise, rounded to bf16.
@@ -338,7 +341,7 @@ def make_inputs(wl: Workload, with_indices: bool = True, threads: int = 8) -> Di
             seg = ori[cu[b]:cu[b] + n * r].reshape(n, r, Hkv, wl.d_qk)
             cmp[cuc[b]:cuc[b + 1]] = seg.mean(axis=1, dtype=np.float32)
         cmp += noise
-        out["cmp_kv"] = _to_bf16(cmp)
+        out["cmp_kv"] = _to_bf16(cmp, wl.dtype)
     if wl.has_sinks:
         g = np.random.Generator(np.random.PCG64(st["sinks"]))
         out["sinks"] = torch.from_numpy(g.standard_normal(Hq, dtype=np.float32))
