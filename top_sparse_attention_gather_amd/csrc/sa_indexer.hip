@@ -31,8 +31,11 @@ constexpr int kThreads = 256;
 constexpr int kD = 128;          // indexer head dim
 constexpr int kHeads = 64;       // indexer heads per workgroup (zero-padded)
 constexpr int kNT = 32;          // selected rows per tile
+constexpr int kNKB = kNT / 16;   // 16-row blocks per tile
+constexpr int kLPW = kNT / 16;   // direct 1 KiB loads per wave per tile (4 rows each)
 constexpr int kMaxPos = 2048;    // slots per token
 constexpr int kXS = kHeads + 8;  // exchange row stride (elements)
+static_assert(kNT % 16 == 0 && kNT <= 64, "tile rows: whole 16-row blocks, one wave sums them");
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -95,15 +98,15 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
   __syncthreads();
 
   const int ntiles = (cnt + kNT - 1) / kNT;
-  // direct loads of tile `it` into buffer `buf`: 8 loads of 4 rows x 256 B,
-  // wave w issues loads 2w, 2w + 1; lane: row 4n + lane / 16, chunk slot
-  // lane % 16 <- chunk (lane % 16) ^ (row % 16).  Rows past the list reload
-  // the tile's first row (never used).
+  // direct loads of tile `it` into buffer `buf`: kNT / 4 loads of 4 rows x
+  // 256 B, wave w issues loads kLPW w .. kLPW w + kLPW - 1; lane: row
+  // 4n + lane / 16, chunk slot lane % 16 <- chunk (lane % 16) ^ (row % 16).
+  // Rows past the list reload the tile's first row (never used).
   auto gather = [&](int it, int buf) {
     const int k0 = it * kNT;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int n = wv * 2 + u;
+    for (int u = 0; u < kLPW; ++u) {
+      const int n = wv * kLPW + u;
       const int r = n * 4 + (lane >> 4);
       const int row = sm.rows[(k0 + r < cnt) ? k0 + r : k0];
       const int ch = (lane & 15) ^ (r & 15);
@@ -112,9 +115,9 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
     }
   };
   // S~^T of the tile for the wave's heads: lane (head hl, rows 16kb + 4lq + i)
-  auto scores = [&](const bf16* kt, f32x4 (&S)[2]) {
+  auto scores = [&](const bf16* kt, f32x4 (&S)[kNKB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < kNKB; ++kb) {
       S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < kD / 32; ++kk) {
@@ -130,11 +133,11 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
     const int buf = it & 1;
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     gather(it + 1 < ntiles ? it + 1 : 0, buf ^ 1);   // next tile, or pass 2's first
-    f32x4 S[2];
+    f32x4 S[kNKB];
     scores(sm.k[buf], S);
     const int i = l16 & 3;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < kNKB; ++kb) {
       float hs[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) hs[r] = row16_sum(wh * fmaxf(S[kb][r], 0.f));
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
       sm.ip[wv][kb * 16 + lq * 4 + i] = i == 0 ? hs[0] : i == 1 ? hs[1] : i == 2 ? hs[2] : hs[3];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (tid < kNT && it * kNT + tid < cnt)
+    if (tid < kNT && it * kNT + tid < cnt)   // kNT <= 64: one wave
       sm.ival[it * kNT + tid] = sm.ip[0][tid] + sm.ip[1][tid] + sm.ip[2][tid] + sm.ip[3][tid];
   }
   __syncthreads();
@@ -189,11 +192,11 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     if (it + 1 < ntiles) gather(it + 1, buf ^ 1);
     const bf16* kt = sm.k[buf];
-    f32x4 S[2];
+    f32x4 S[kNKB];
     scores(kt, S);
-    i16x4 dSa[2];
+    i16x4 dSa[kNKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < kNKB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = kb * 16 + lq * 4 + r;
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
 #pragma unroll
     for (int c = 0; c < kD / 16; ++c) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kNKB; ++kb) {
         const int rt = kb * 16 + lq * 4 + (l16 >> 2);
         const int ch = c * 2 + (tq >> 1);
         const i16x4 kf = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // dK~^T[32wv + 16cb + 4lq + i][row 16kb + l16] over all 64 heads
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < kNKB; ++kb) {
       const int key = kb * 16 + l16;
       const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(&sm.x[key * kXS + lq * 8]);
       const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&sm.x[key * kXS + 32 + lq * 8]);
