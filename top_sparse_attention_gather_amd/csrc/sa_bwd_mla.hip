@@ -275,15 +275,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     // no branch
     const int k0 = itb * kNT;
     const bool kvalid = live && krow < cnt - k0;
-    h.row = kvalid ? part_row0 + (size_t)sm.vpos[kvalid ? k0 + krow : 0] * kDQK : dump;
+    // 0 <= index < kMaxPos always (k0 = -32 for the tile before the first,
+    // a stale position past the list), so the load needs no branch; the
+    // select picks the dump row
+    const int vp = sm.vpos[max(k0 + krow, 0)];
+    bf16* const rowp = part_row0 + (size_t)vp * kDQK;
+    h.row = kvalid ? rowp : dump;
     return h;
   };
-  auto b_chain = [&](const BHalf& h, int cc) {
+  // dO^T operand block ks of column block cc < 8 (the first kDotLds from LDS)
+  auto dot_op = [&](int cc, int ks) -> bf16x8 {
+    const int c = cc < 8 ? cc : 0;
+    return c < kDotLds ? sm.dot[wv][c < kDotLds ? c : 0][ks][lane] : dOT[c][ks];
+  };
+  // one column-block chain: Q^T (scale dS) + dO^T P (no dO part for the
+  // rope columns, cc = 8); o0 / o1 are its dO^T operands
+  auto b_chain = [&](const BHalf& h, int cc, const bf16x8& o0, const bf16x8& o1) {
     f32x4 acc = mfma16x16x32(QT[cc][0], h.d0, f32x4{0.f, 0.f, 0.f, 0.f});
     acc = mfma16x16x32(QT[cc][1], h.d1, acc);
     if (cc < 8) {
-      const bf16x8 o0 = cc < kDotLds ? sm.dot[wv][cc < kDotLds ? cc : 0][0][lane] : dOT[cc][0];
-      const bf16x8 o1 = cc < kDotLds ? sm.dot[wv][cc < kDotLds ? cc : 0][1][lane] : dOT[cc][1];
       acc = mfma16x16x32(o0, h.p0, acc);
       acc = mfma16x16x32(o1, h.p1, acc);
     }
@@ -366,17 +376,26 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
       // products run on stale exchange data and go to the dump row)
       const BHalf hb = b_setup(it - 1, b, it > 0);
       f32x4 br[9];
+      // the dO^T operands of each chain are read one chain ahead (and the
+      // KV fragments kPF steps ahead): the scheduling barriers keep those
+      // LDS reads in front of the MFMAs that do not need them yet
+      bf16x8 od0 = dot_op(0, 0), od1 = dot_op(0, 1);
 #pragma unroll
       for (int kk = 0; kk < 18; ++kk) {
         if ((kk & 1) == 0) {
           const int cc = kk >> 1;
-          br[cc] = b_chain(hb, cc);
+          br[cc] = b_chain(hb, cc, cc < kDotLds ? od0 : dot_op(cc, 0), cc < kDotLds ? od1 : dot_op(cc, 1));
+          if (cc + 1 < kDotLds) {
+            od0 = dot_op(cc + 1, 0);
+            od1 = dot_op(cc + 1, 1);
+          }
           if (cc >= 2 && (cc & 1) == 0) b_put_pair(hb, cc - 2, br[cc - 2], br[cc - 1]);
         }
         if (kk + kPF < 18) {
           const int k2 = kk + kPF;
           f[k2 % (kPF + 1)] = *reinterpret_cast<const bf16x8*>(&kvb[off + (k2 >> 1) * kSegElems + (k2 & 1) * 32]);
         }
+        __builtin_amdgcn_sched_barrier(0);
         if (b == 0 && (kk & 1) == 0) {
           // next tile's rows: one direct load every other step (for the
           // last tile a harmless reload into the free buffer)
@@ -429,6 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
         if (c + kPF < 9) {
           fa[(c + kPF) % (kPF + 1)] = kvt(kvb, col_block(c + kPF) >> 4);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) dQ[c * 4 + hb] = mfma16x16x32(fa[c % (kPF + 1)], bt[hb], dQ[c * 4 + hb]);
       }
@@ -448,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
       f32x4 br[9];
 #pragma unroll
       for (int cc = 0; cc < 9; ++cc) {
-        br[cc] = b_chain(h, cc);
+        br[cc] = b_chain(h, cc, dot_op(cc, 0), dot_op(cc, 1));
         if (cc >= 2 && (cc & 1) == 0) b_put_pair(h, cc - 2, br[cc - 2], br[cc - 1]);
       }
       b_put_single(h, 8, br[8]);
