@@ -43,8 +43,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     ("mla_token_8k", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
-        "sha256": "8457a79e756ce2646dd19e8a9aec14aa82e336b5ea847db9d70e2cceaf36cc33",
-        "fetch_bytes": 9525765037, "write_bytes": 17519397696,
+        "sha256": "129212d9a27da5e761e6d9dfe5e165d5a6e11782d3bd72be4be7da774820529d",
+        "fetch_bytes": 8192461958, "write_bytes": 17519394688,
     },
 }
 
