@@ -106,6 +106,21 @@ __device__ __forceinline__ const bf16* row_ptr(const Params& p, int code, int g)
                            : p.k + ((size_t)code * p.Hkv + g) * kDQK;
 }
 
+// Direct global->LDS load, 16 bytes per lane, to the wave-uniform LDS
+// address `lds` (+ 16 x lane).  Inline asm instead of the builtin: the
+// compiler models the builtin as a FLAT access that may touch LDS, and while
+// one is outstanding it turns every LDS wait into a full drain
+// (lgkmcnt(0)), which cancels the read-ahead of the MFMA operands.  The
+// wait-count insertion does not see these loads, so the kernel waits for
+// them itself: vmcnt(0) before the barrier that hands a filled tile buffer
+// to its readers, and before the workgroup ends.  No register receives data
+// (it goes to LDS), so nothing else can depend on a load in flight.  M0
+// (the LDS base) is an input operand, so the compiler sets it.
+__device__ __forceinline__ void load_lds16(const bf16* src, bf16* lds) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void*)lds);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
+}
+
 // Gather the tile's rows (positions k0 .. k0+31 of the compacted list) into
 // `dst` with direct global->LDS loads; wave w loads row group w, one
 // segment per load.
@@ -117,7 +132,7 @@ __device__ __forceinline__ void gather_tile(const Params& p, const MlaSmem& sm, 
   bf16* d = dst + group_base(wv);
 #pragma unroll
   for (int sg = 0; sg < 9; ++sg)
-    __builtin_amdgcn_global_load_lds((gbl_void*)(src + sg * 64), (lds_void*)(d + sg * kSegElems), 16, 0, 0);
+    load_lds16(src + sg * 64, d + sg * kSegElems);
 }
 
 // L1: also write the head sums of P behind the softmax L1-norm outputs
@@ -400,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
           // next tile's rows: one direct load every other step (for the
           // last tile a harmless reload into the free buffer)
           const int sg = kk >> 1;
-          __builtin_amdgcn_global_load_lds((gbl_void*)(gsrc + sg * 64), (lds_void*)(gdst + sg * kSegElems), 16, 0, 0);
+          load_lds16(gsrc + sg * 64, gdst + sg * kSegElems);
         }
         const bf16x8 a = f[kk % (kPF + 1)];
         S = mfma16x16x32(a, QA[kk], S);

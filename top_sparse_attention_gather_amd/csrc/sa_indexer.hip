@@ -20,6 +20,7 @@
 //     transposing reads of the K~ tile) -- and into an LDS exchange
 //     [row][head]; dK~^T of the wave's 32 columns = q~^T dS~ over all 64
 //     heads (16x16x32), written as one bf16 partial row per (token, slot)
+//     (64 contiguous bytes of a row per 16-byte lane store)
 //     for the deterministic key-major sum over the CSR transpose.
 #include "sa_launch.h"
 
@@ -55,6 +56,18 @@ struct __attribute__((aligned(16))) IdxSmem {
 // element offset of 16-byte chunk `chunk` of tile row r
 __device__ __forceinline__ int koff(int r, int chunk) { return r * kD + ((chunk ^ (r & 15)) * 8); }
 
+// Direct global->LDS load, 16 bytes per lane, to the wave-uniform LDS
+// address `lds` (+ 16 x lane), as inline asm: the compiler models the
+// builtin as a FLAT access that may touch LDS and, while one is
+// outstanding, turns every LDS wait into a full drain.  The wait-count
+// insertion does not see these loads; the kernel waits for them itself
+// (vmcnt(0) before each tile's barrier and before the workgroup ends).  M0
+// (the LDS base) is an input operand, so the compiler sets it.
+__device__ __forceinline__ void load_lds16(const bf16* src, bf16* lds) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void*)lds);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -74,6 +87,9 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
   // ---- the token's used slots, compacted ---------------------------------
   const int cnt = compact_positions_batched<kMaxPos / 256>(p, s, irow, p.topk, sm.rows, sm.wave, sm.vpos);
 
+  const int hl = wv * 16 + l16;   // this lane's head in the S~^T layout
+  const float wh = hl < H ? a.w[(size_t)t * H + hl] : 0.f;
+
   // ---- q~ of the 64 heads via LDS into both operand layouts --------------
   bf16* qs = &sm.k[0][0];
   for (int c = tid; c < kHeads * kD / 8; c += kThreads) {
@@ -83,7 +99,6 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
     *reinterpret_cast<uint4*>(qs + h * kD + col) = v;
   }
   __syncthreads();
-  const int hl = wv * 16 + l16;   // this lane's head in the S~^T layout
   bf16x8 QB[kD / 32];             // B operand: head hl, dims 32kk + 8lq .. +8
 #pragma unroll
   for (int kk = 0; kk < kD / 32; ++kk) QB[kk] = *reinterpret_cast<const bf16x8*>(qs + hl * kD + kk * 32 + lq * 8);
@@ -94,7 +109,9 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) AT[cb][ks][j] = qs[(32 * ks + 8 * lq + j) * kD + 32 * wv + 16 * cb + l16];
-  const float wh = hl < H ? a.w[(size_t)t * H + hl] : 0.f;
+  // consume wh here: its load must not stay outstanding into the tile loops,
+  // where the wait for it would also wait for the tile loads in flight
+  asm volatile("" ::"v"(wh));
   __syncthreads();
 
   const int ntiles = (cnt + kNT - 1) / kNT;
@@ -110,8 +127,7 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
       const int r = n * 4 + (lane >> 4);
       const int row = sm.rows[(k0 + r < cnt) ? k0 + r : k0];
       const int ch = (lane & 15) ^ (r & 15);
-      __builtin_amdgcn_global_load_lds((gbl_void*)(a.k + (size_t)row * kD + ch * 8),
-                                       (lds_void*)(&sm.k[buf][n * 4 * kD]), 16, 0, 0);
+      load_lds16(a.k + (size_t)row * kD + ch * 8, &sm.k[buf][n * 4 * kD]);
     }
   };
   // S~^T of the tile for the wave's heads: lane (head hl, rows 16kb + 4lq + i)
@@ -232,13 +248,21 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
       const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(&sm.x[key * kXS + 32 + lq * 8]);
       const bool v = k0 + key < cnt;
       bf16* rowp = v ? part_tok + (size_t)sm.vpos[v ? k0 + key : 0] * kD : a.dump;
+      f32x4 acc[2];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        f32x4 acc = mfma16x16x32(AT[cb][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
-        acc = mfma16x16x32(AT[cb][1], b1, acc);
-        const uint2 o = {pk2(acc[0], acc[1]), pk2(acc[2], acc[3])};
-        *reinterpret_cast<uint2*>(rowp + 32 * wv + 16 * cb + 4 * lq) = o;
+        acc[cb] = mfma16x16x32(AT[cb][0], b0, f32x4{0.f, 0.f, 0.f, 0.f});
+        acc[cb] = mfma16x16x32(AT[cb][1], b1, acc[cb]);
       }
+      // lane (key l16, lq) holds columns 16cb + 4lq .. +3 of both blocks;
+      // after swapping halves with the neighbouring 16-lane row it holds 8
+      // contiguous columns (lq even: block 0 from 4lq, lq odd: block 1 from
+      // 4(lq - 1)), so one 16-byte store per lane writes 64 contiguous bytes
+      // of each row
+      const auto s0 = __builtin_amdgcn_permlane16_swap(pk2(acc[0][0], acc[0][1]), pk2(acc[1][0], acc[1][1]), false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(pk2(acc[0][2], acc[0][3]), pk2(acc[1][2], acc[1][3]), false, false);
+      const uint4 o = {s0[0], s1[0], s0[1], s1[1]};
+      *reinterpret_cast<uint4*>(rowp + 32 * wv + (lq & 1) * 16 + (lq >> 1) * 8) = o;
     }
   }
   // no direct load may still be writing this workgroup's LDS when it ends
