@@ -63,6 +63,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def device_info():
+    """Compute units and peak engine clock of device 0 as HIP reports them
+    (hipDeviceGetAttribute: hipDeviceAttributeMultiprocessorCount = 63,
+    hipDeviceAttributeClockRate = 5, in kHz), and the dense bf16 MFMA peak
+    they imply at 4 SIMDs per CU and 1024 FLOP per clock per SIMD."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(cus), 63, 0) or hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0):
+            return None
+    except OSError:
+        return None
+    return {"compute_units": cus.value, "max_sclk_mhz": khz.value / 1000.0,
+            "bf16_peak_at_max_sclk_tflops": round(cus.value * 4 * 1024 * khz.value * 1e3 / 1e12, 1)}
+
+
+def percentiles(ms):
+    q = np.percentile(np.asarray(ms), [10, 50, 90])
+    return {"p10": round(float(q[0]), 4), "median": round(float(q[1]), 4), "p90": round(float(q[2]), 4)}
+
+
 def valid_pairs(wl: W.Workload, idx: np.ndarray) -> int:
     """Valid (token, kv head, key row) pairs from the generated indices,
     counted from the index lists (any negative slot is unused)."""
@@ -194,14 +216,21 @@ def bench_indexer(args):
     stream = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evict = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if args.evict_cache else None
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
+        if evict is not None:
+            evict.fill_(float(i))
+        calls[i][0].record(stream)
         B.sparse_attn_indexer_grad_kl(desc, dev, outputs, ws, stream=stream, events=ev.pairs[i])
+        calls[i][1].record(stream)
     t_stop.record(stream)
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_stop) / args.steps
+    call_ms = [a.elapsed_time(b) for a, b in calls]
+    ms = float(np.mean(call_ms)) if evict is not None else t_start.elapsed_time(t_stop) / args.steps
     kern_ms = float(np.mean([ev.elapsed_ms(i) for i in range(args.steps)]))
     ev.close()
     for k, v in outputs.items():
@@ -227,6 +256,9 @@ def bench_indexer(args):
         "config": {"workload": f"{wl.name}: B={wl.batch} S={wl.seqlens[0]} indexer heads={H} d={d} top-{K}",
                    "valid_pairs": pairs, "selected_row_tflop": round(flop / 1e12, 4),
                    "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "parallelism": "single GPU"},
+        "timing": {"call_ms": percentiles(call_ms), "cache_evicted_between_calls": evict is not None,
+                   "step_time_from": "per-call events" if evict is not None else "bracketed region / steps",
+                   "device": device_info()},
         "roofline": {"kernel": "idx_grad_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
                      "mfma_tflops": round(ktf, 2), "traffic": None, "kernel_ms": round(kern_ms, 4)},
@@ -247,6 +279,9 @@ def main():
     ap.add_argument("--softmax-l1", action="store_true",
                     help="also produce the softmax L1-norm side outputs in every timed call")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--evict-cache", action="store_true",
+                    help="write 1 GiB before every timed call (evicts the 256 MB Infinity Cache); the step time "
+                         "is then the mean of the per-call events")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB): the known-size kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -294,15 +329,25 @@ def main():
     stream = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
+    # one event pair around every call, on the stream the library launches on
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evict = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if args.evict_cache else None
+    log(f"[bench] timing {args.steps} steps" + (" (Infinity Cache evicted before each call)" if evict is not None else ""))
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
+        if evict is not None:
+            evict.fill_(float(i))            # 1 GiB written between calls, outside the per-call events
+        calls[i][0].record(stream)
         B.sparse_attn_bwd(desc, dev, outputs, ws, stream=stream, events=ev.pairs[i])
+        calls[i][1].record(stream)
     t_stop.record(stream)
     torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in calls]
     total_ms = t_start.elapsed_time(t_stop)
-    ms = total_ms / args.steps
+    # with eviction the bracketed region also holds the eviction writes, so
+    # the step time is the mean of the per-call events
+    ms = float(np.mean(call_ms)) if evict is not None else total_ms / args.steps
     kern_ms = float(np.mean([ev.elapsed_ms(i) for i in range(args.steps)]))
     ev.close()
     for k, v in outputs.items():
@@ -344,6 +389,9 @@ def main():
             "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
             "parallelism": "single GPU",
         },
+        "timing": {"call_ms": percentiles(call_ms), "cache_evicted_between_calls": evict is not None,
+                   "step_time_from": "per-call events" if evict is not None else "bracketed region / steps",
+                   "device": device_info()},
         "roofline": dict(main_kernel_roofline(wl, args.dkv_mode, idx, flop, kern_ms), **{
             # the stored counter readings are of the kernel without the L1-norm sums
             "traffic": None if args.softmax_l1 else measured_traffic(wl.name, args.dkv_mode),
