@@ -71,7 +71,9 @@ design notes):
       (slot, block row, window offset) with 0 where nothing is selected;
   R19 the indexer's S~ is the raw product q~ K~^T (no scale); its softmax and
       loss run over the selected rows; the target p is given per slot and
-      only used slots count; dI = softmax(I) - p as printed.
+      only used slots count; dI = softmax(I) - p as printed;
+  R23 the cmp residual (the remainder of the ori length by cmp_ratio) follows
+      from R6's blocks and the lengths, so no residual input exists.
 """
 from __future__ import annotations
 
