@@ -43,8 +43,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     ("mla_token_8k", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
-        "sha256": "129212d9a27da5e761e6d9dfe5e165d5a6e11782d3bd72be4be7da774820529d",
-        "fetch_bytes": 8192461958, "write_bytes": 17519394688,
+        "sha256": "eccdc5ca9b2fbd900a260cedc62b4b8eedc9d6d28c1cb467012b25b8d155ba93",
+        "fetch_bytes": 8369911936, "write_bytes": 17519300960,
     },
 }
 
