@@ -49,8 +49,14 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
   constexpr int kPer = Vec8<PT>::kPer;
   const int tpr = r.RW / kPer;
   const int sub = threadIdx.x % tpr;
-  const long long orow = (long long)blockIdx.x * (blockDim.x / tpr) + threadIdx.x / tpr;
-  if (orow >= r.n_out_rows || threadIdx.x / tpr >= blockDim.x / tpr) return;
+  const long long lin = (long long)blockIdx.x * (blockDim.x / tpr) + threadIdx.x / tpr;
+  if (lin >= r.n_out_rows || threadIdx.x / tpr >= blockDim.x / tpr) return;
+  // Heavy rows first: the cmp rows (each named by the cmp slots of many
+  // queries) are scheduled before the window rows (at most win_left + 1 +
+  // win_right partials each), so the long sums do not form the grid's tail.
+  // A bijection on the output rows; each row's summation order is unchanged.
+  const long long n_cmp_out = r.n_out_rows - r.n_kv_out;
+  const long long orow = lin < n_cmp_out ? r.n_kv_out + lin : lin - n_cmp_out;
   const int col = sub * kPer;
   const PT* part = static_cast<const PT*>(r.partial);
   float acc[kPer];
