@@ -64,3 +64,11 @@ def test_csr_shuffled_duplicates_out_of_range():
 def test_csr_bit_exact_full_size(name):
     wl = W.WORKLOADS[name]
     _check(wl, W.make_index_inputs(wl))
+
+
+def test_csr_three_radix_passes():
+    """70 000 kv rows, so more than 2^16 keys: the sort takes three 8-bit
+    passes, the middle one reading and writing (key, slot) pairs."""
+    wl = W.Workload(name="csr_70k_keys", select=W.SEL_TOKEN, layout=W.LAYOUT_BSND, seqlens=(70000,), n_q_heads=2,
+                    n_kv_heads=1, d_qk=64, d_v=64, kv_shared=False, topk=4, seed=17)
+    _check(wl, W.make_index_inputs(wl))

@@ -7,7 +7,9 @@
 // produced by a stable LSD radix sort (8-bit digits) of (key, p) pairs in
 // p order: per pass a digit histogram per 4096-element tile, one
 // exclusive scan over the digit-major table, and a stable scatter that
-// ranks equal digits inside a tile with wave ballots.  Per-key counts come
+// ranks equal digits inside a tile with wave ballots.  Between passes a
+// pair travels as one 8-byte (key, p) element, so each scattered write is
+// one store; the last pass writes only p (the entries).  Per-key counts come
 // from an integer histogram and the same scan, giving row_ptr.  Everything
 // is integer work, so the result is bit-exact and run-to-run identical.
 #include "sa_launch.h"
@@ -180,15 +182,17 @@ __global__ __launch_bounds__(kThreads) void slot_keys_hist_kernel(Params p, long
 // ---------------------------------------------------------------------------
 // LSD radix sort passes.
 
-__global__ __launch_bounds__(kThreads) void radix_hist_kernel(const int* __restrict__ keys, long long n, int shift,
-                                                              int nb, int* __restrict__ hist) {
+// keys: element i's key at keys[i * kstride] (1: the key array, 2: the
+// (key, p) pair array)
+__global__ __launch_bounds__(kThreads) void radix_hist_kernel(const int* __restrict__ keys, int kstride, long long n,
+                                                              int shift, int nb, int* __restrict__ hist) {
   __shared__ int h[256];
   h[threadIdx.x] = 0;
   __syncthreads();
   const long long base = (long long)blockIdx.x * kTile;
   for (int r = 0; r < kItems; ++r) {
     const long long i = base + r * kThreads + threadIdx.x;
-    if (i < n) atomicAdd(&h[(keys[i] >> shift) & 255], 1);
+    if (i < n) atomicAdd(&h[(keys[i * kstride] >> shift) & 255], 1);
   }
   __syncthreads();
   hist[(long long)threadIdx.x * nb + blockIdx.x] = h[threadIdx.x];
@@ -196,11 +200,14 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(const int* __restr
 
 // Stable scatter: element e = base + r * 256 + tid is ranked after every
 // element of an earlier round or a lower thread with the same digit.
+// FIRST: the input is the key array and p = val0 + e; otherwise (key, p)
+// pairs.  LAST: only p is written (to vals_out); otherwise (key, p) pairs.
+template <bool FIRST, bool LAST>
 __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(const int* __restrict__ keys_in,
-                                                                 const int* __restrict__ vals_in,
+                                                                 const int2* __restrict__ pairs_in,
                                                                  long long val0, long long n, int shift, int nb,
                                                                  const int* __restrict__ offs,
-                                                                 int* __restrict__ keys_out,
+                                                                 int2* __restrict__ pairs_out,
                                                                  int* __restrict__ vals_out) {
   __shared__ int cnt[256];
   __shared__ int wcnt[4][256];
@@ -213,8 +220,17 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(const int* __re
   for (int r = 0; r < kItems; ++r) {
     const long long i = base + r * kThreads + tid;
     const bool ok = i < n;
-    const int key = ok ? keys_in[i] : 0;
-    const int val = ok ? (vals_in ? vals_in[i] : (int)(val0 + i)) : 0;
+    int key = 0, val = 0;
+    if (ok) {
+      if (FIRST) {
+        key = keys_in[i];
+        val = (int)(val0 + i);
+      } else {
+        const int2 kv = pairs_in[i];
+        key = kv.x;
+        val = kv.y;
+      }
+    }
     const int d = (key >> shift) & 255;
     // lanes of this wave holding the same digit
     unsigned long long peers = __ballot(ok);
@@ -228,8 +244,8 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(const int* __re
     if (ok) {
       int rank = cnt[d] + __popcll(peers & lt);
       for (int ww = 0; ww < w; ++ww) rank += wcnt[ww][d];
-      keys_out[rank] = key;
-      vals_out[rank] = val;
+      if (LAST) vals_out[rank] = val;
+      else pairs_out[rank] = make_int2(key, val);
     }
     __syncthreads();
     cnt[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
@@ -240,8 +256,21 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(const int* __re
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+int csr_sentinel_bits(long long n_keys) {
+  int bits = 1;
+  while ((1LL << bits) <= n_keys) ++bits;
+  return bits;
+}
+
+// 8-bit LSD passes that cover every key and the sentinel (n_keys)
+int csr_passes(long long n_keys) { return (csr_sentinel_bits(n_keys) + 7) / 8; }
+
+// Workspace: the slot keys, one (key, p) pair buffer (two from the third
+// pass on), the per-key counts, the digit histograms and the scan sums.
 struct CsrWs {
-  int *keys_a, *keys_b, *vals_a, *counts, *hist, *bsum;
+  int* keys;
+  int2 *pairs_a, *pairs_b;
+  int *counts, *hist, *bsum;
   long long nb_tiles, nb_scan;
 };
 
@@ -252,9 +281,13 @@ CsrWs carve(void* ws, long long n, long long n_keys) {
   const long long hist_n = 256 * c.nb_tiles;
   const long long scan_n = std::max(hist_n, n_keys + 1);
   c.nb_scan = (scan_n + kScanChunk - 1) / kScanChunk;
-  c.keys_a = reinterpret_cast<int*>(p); p += align256(n * 4);
-  c.keys_b = reinterpret_cast<int*>(p); p += align256(n * 4);
-  c.vals_a = reinterpret_cast<int*>(p); p += align256(n * 4);
+  c.keys = reinterpret_cast<int*>(p); p += align256(n * 4);
+  c.pairs_a = reinterpret_cast<int2*>(p); p += align256(n * 8);
+  c.pairs_b = nullptr;
+  if (csr_passes(n_keys) > 2) {
+    c.pairs_b = reinterpret_cast<int2*>(p);
+    p += align256(n * 8);
+  }
   c.counts = reinterpret_cast<int*>(p); p += align256((n_keys + 1) * 4);
   c.hist = reinterpret_cast<int*>(p); p += align256(hist_n * 4);
   c.bsum = reinterpret_cast<int*>(p); p += align256(c.nb_scan * 4);
@@ -282,19 +315,13 @@ size_t csr_workspace_bytes(long long n, long long n_keys, int batch) {
   const long long hist_n = 256 * nb_tiles;
   const long long scan_n = std::max(hist_n, n_keys + 1);
   const long long nb_scan = (scan_n + kScanChunk - 1) / kScanChunk;
-  return align256(n * 4) * 3 + align256((n_keys + 1) * 4) + align256(hist_n * 4) + align256(nb_scan * 4) +
-         align256((size_t)(batch + 1) * 4);
+  return align256(n * 4) + align256(n * 8) * (csr_passes(n_keys) > 2 ? 2 : 1) + align256((n_keys + 1) * 4) +
+         align256(hist_n * 4) + align256(nb_scan * 4) + align256((size_t)(batch + 1) * 4);
 }
 
 hipError_t launch_block_base(const Params& p, int* blk_base, hipStream_t s) {
   hipLaunchKernelGGL(block_base_kernel, dim3(1), dim3(64), 0, s, p, blk_base);
   return hipGetLastError();
-}
-
-int csr_sentinel_bits(long long n_keys) {
-  int bits = 1;
-  while ((1LL << bits) <= n_keys) ++bits;
-  return bits;
 }
 
 hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_keys, const int* blk_base,
@@ -310,28 +337,39 @@ hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_key
     const long long per = std::max<long long>(kThreads, (n + 511) / 512);
     const unsigned nb = (unsigned)((n + per - 1) / per);
     hipLaunchKernelGGL(slot_keys_hist_kernel, dim3(nb), dim3(kThreads), 0, s, p, slot0, n, per, (int)n_keys, blk_base,
-                       sentinel, c.keys_a, c.counts);
+                       sentinel, c.keys, c.counts);
   } else if (n > 0) {
     hipLaunchKernelGGL(slot_keys_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, p,
-                       slot0, n, blk_base, sentinel, c.keys_a, c.counts);
+                       slot0, n, blk_base, sentinel, c.keys, c.counts);
   }
   if ((e = scan_excl(c.counts, n_keys, row_ptr, n_keys + 1, c.bsum, s)) != hipSuccess) return e;
   if (n == 0) return hipGetLastError();
-  const int bits = csr_sentinel_bits(n_keys);
-  const int passes = (bits + 7) / 8;
+  const int passes = csr_passes(n_keys);
   const int nb = (int)c.nb_tiles;
-  int* kin = c.keys_a;
-  int* kout = c.keys_b;
-  int* vin = nullptr;            // first pass: values are the slot ids
+  // pass 0 reads the key array; later passes read the pair buffer the
+  // previous pass wrote (pairs_a, pairs_b alternating); the last pass
+  // writes only the slot ids, into `entries`
+  const int2* pin = nullptr;
   for (int pass = 0; pass < passes; ++pass) {
-    // value buffers alternate so that the last pass lands in `entries`
-    int* vout = ((passes - 1 - pass) % 2 == 0) ? entries : c.vals_a;
-    hipLaunchKernelGGL(radix_hist_kernel, dim3(nb), dim3(kThreads), 0, s, kin, n, pass * 8, nb, c.hist);
+    const bool first = pass == 0, last = pass == passes - 1;
+    int2* pout = (pass % 2 == 0) ? c.pairs_a : c.pairs_b;
+    const int* hkeys = first ? c.keys : reinterpret_cast<const int*>(pin);
+    hipLaunchKernelGGL(radix_hist_kernel, dim3(nb), dim3(kThreads), 0, s, hkeys, first ? 1 : 2, n, pass * 8, nb,
+                       c.hist);
     if ((e = scan_excl(c.hist, 256LL * nb, c.hist, 256LL * nb, c.bsum, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(radix_scatter_kernel, dim3(nb), dim3(kThreads), 0, s, kin, vin, slot0, n, pass * 8, nb,
-                       c.hist, kout, vout);
-    std::swap(kin, kout);
-    vin = vout;
+    if (first && last)
+      hipLaunchKernelGGL((radix_scatter_kernel<true, true>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, slot0, n,
+                         pass * 8, nb, c.hist, pout, entries);
+    else if (first)
+      hipLaunchKernelGGL((radix_scatter_kernel<true, false>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, slot0, n,
+                         pass * 8, nb, c.hist, pout, entries);
+    else if (last)
+      hipLaunchKernelGGL((radix_scatter_kernel<false, true>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, slot0, n,
+                         pass * 8, nb, c.hist, pout, entries);
+    else
+      hipLaunchKernelGGL((radix_scatter_kernel<false, false>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, slot0, n,
+                         pass * 8, nb, c.hist, pout, entries);
+    pin = pout;
   }
   return hipGetLastError();
 }
