@@ -57,11 +57,16 @@ constexpr int kTileElems = 4 * kGroupStride;         // 18560 (36.25 KiB)
 constexpr int kStageElems = kHeads * kKS;            // LDS of the KV tiles and of the Q / dO staging
 static_assert(2 * kTileElems <= kStageElems, "two tiles fit the staging region");
 
-__device__ __forceinline__ int group_base(int rg) { return rg * kGroupStride; }
+// dO (512 columns) is staged in the same layout with 8 segments per group.
+constexpr int kDoGroupStride = 8 * kSegElems + 32;
+constexpr int kDoTileElems = 4 * kDoGroupStride;     // 32 heads of dO (33 KiB)
 
-__device__ __forceinline__ int tile_off(int row, int chunk) {
+__device__ __forceinline__ int group_base(int rg, int gstride = kGroupStride) { return rg * gstride; }
+
+__device__ __forceinline__ int tile_off(int row, int chunk, int gstride = kGroupStride) {
   const int rr = row & 7;
-  return group_base(row >> 3) + (chunk >> 3) * kSegElems + rr * 64 + ((chunk & 4) | ((chunk & 3) ^ (rr >> 1))) * 8;
+  return group_base(row >> 3, gstride) + (chunk >> 3) * kSegElems + rr * 64 +
+         ((chunk & 4) | ((chunk & 3) ^ (rr >> 1))) * 8;
 }
 
 // The chunk (within its segment) that lane `lane` of a wave-wide segment
@@ -77,15 +82,23 @@ __device__ __forceinline__ int seg_chunk(int lane) {
 constexpr int kDotLds = 6;
 
 struct __attribute__((aligned(16))) MlaSmem {
-  bf16 kv[kStageElems];            // KV tiles at 0 and kTileElems; Q / dO staging at token start
-  bf16 xds[2][kNT * kXS];          // scale * dS  [key][head], tiles alternate
-  bf16 xp[2][kNT * kXS];           // P           [key][head]
-  bf16x8 dot[4][kDotLds][2][64];   // phase-B dO^T operand blocks 0..kDotLds-1, register layout per lane
+  bf16 kv[kStageElems];            // KV tiles at 0 and kTileElems; Q staging at token start
+  union {
+    struct {
+      bf16 xds[2][kNT * kXS];          // scale * dS  [key][head], tiles alternate
+      bf16 xp[2][kNT * kXS];           // P           [key][head]
+      bf16x8 dot[4][kDotLds][2][64];   // phase-B dO^T operand blocks 0..kDotLds-1, register layout per lane
+    };
+    bf16 dost[2 * kDoTileElems];       // dO staging at token start (free until the tile loop)
+  };
   int rows[kMaxPos];
   int vpos[kMaxPos];
   int wave[4];
   float l1s[4][kNT];               // softmax L1-norm: P summed over each wave's 16 heads, per key
 };
+
+static_assert(2 * kDoTileElems * 2 <= 2 * (2 * kNT * kXS * 2) + 4 * kDotLds * 2 * 64 * 16,
+              "the dO staging fits the exchange and dO^T-block area");
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -168,6 +181,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   const bool row_live = lse > -INFINITY;
 
   // ---- Q and dO into registers, via LDS, in both operand layouts ---------
+  // Q goes to the two KV tile buffers and dO to the exchange / dO^T-block
+  // area (both free until the tile loop), with all the loads in flight
+  // together; one wait, then both are read out.
   bf16x8 QA[18], dOA[16];          // phase A: [head 16wv + l16][32kk + 8lq .. +8]
   bf16x8 QT[9][2], dOT[8][2];      // phase B: [col][heads 32ks + 8lq .. +8]
   {
@@ -175,63 +191,54 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     // both buffers (heads 32hb + 8w + lane / 8)
     const int hr = wv * 8 + (lane >> 3);
     const int sc = seg_chunk(lane) * 8;
-    // QA: head 16wv + l16 = buffer wv / 2, local row 16 (wv % 2) + l16
-    const bf16* qa = sm.kv + (wv >> 1) * kTileElems;
-    const int qrow = (wv & 1) * 16 + l16;
     {
       const bf16* src = p.q + ((size_t)t * p.Hq + h0 + hr) * kDQK + sc;
+      const bf16* srcd = p.dO + ((size_t)t * p.Hq + h0 + hr) * kDV + sc;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+      for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
         for (int sg = 0; sg < 9; ++sg)
-          __builtin_amdgcn_global_load_lds((gbl_void*)(src + (size_t)hb * 32 * kDQK + sg * 64),
-                                           (lds_void*)(sm.kv + hb * kTileElems + group_base(wv) + sg * kSegElems),
-                                           16, 0, 0);
+          load_lds16(src + (size_t)hb * 32 * kDQK + sg * 64, sm.kv + hb * kTileElems + group_base(wv) + sg * kSegElems);
+#pragma unroll
+        for (int sg = 0; sg < 8; ++sg)
+          load_lds16(srcd + (size_t)hb * 32 * kDV + sg * 64,
+                     sm.dost + hb * kDoTileElems + group_base(wv, kDoGroupStride) + sg * kSegElems);
+      }
     }
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    // QA / dOA: head 16wv + l16 = buffer wv / 2, local row 16 (wv % 2) + l16
+    const int qrow = (wv & 1) * 16 + l16;
+    const bf16* qa = sm.kv + (wv >> 1) * kTileElems;
+    const bf16* da = sm.dost + (wv >> 1) * kDoTileElems;
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) QA[kk] = *reinterpret_cast<const bf16x8*>(&qa[tile_off(qrow, 4 * kk + lq)]);
 #pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      dOA[kk] = *reinterpret_cast<const bf16x8*>(&da[tile_off(qrow, 4 * kk + lq, kDoGroupStride)]);
+    const int r0 = lq * 8 + (l16 >> 2);
+    const int sub = (l16 & 1) * 4;
+#pragma unroll
     for (int c = 0; c < 9; ++c) {
       const int col0 = c < 8 ? wv * 128 + c * 16 : 512 + wv * 16;
+      const int ch = (col0 >> 3) + ((l16 & 3) >> 1);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16* b = sm.kv + ks * kTileElems;
-        const int r0 = lq * 8 + (l16 >> 2);
-        const int ch = (col0 >> 3) + ((l16 & 3) >> 1);
-        const int sub = (l16 & 1) * 4;
         QT[c][ks] = join(tr_read(&b[tile_off(r0, ch) + sub]), tr_read(&b[tile_off(r0 + 4, ch) + sub]));
+        if (c < 8) {
+          const bf16* bd = sm.dost + ks * kDoTileElems;
+          dOT[c][ks] = join(tr_read(&bd[tile_off(r0, ch, kDoGroupStride) + sub]),
+                            tr_read(&bd[tile_off(r0 + 4, ch, kDoGroupStride) + sub]));
+        }
       }
     }
-    __syncthreads();
-    {
-      const bf16* src = p.dO + ((size_t)t * p.Hq + h0 + hr) * kDV + sc;
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int sg = 0; sg < 8; ++sg)
-          __builtin_amdgcn_global_load_lds((gbl_void*)(src + (size_t)hb * 32 * kDV + sg * 64),
-                                           (lds_void*)(sm.kv + hb * kTileElems + group_base(wv) + sg * kSegElems),
-                                           16, 0, 0);
-    }
+    // every wave has read the staged Q and dO before the dO^T blocks (which
+    // overlay the dO staging) are written and the first KV tile is gathered
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) dOA[kk] = *reinterpret_cast<const bf16x8*>(&qa[tile_off(qrow, 4 * kk + lq)]);
+    for (int c = 0; c < kDotLds; ++c)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int col0 = wv * 128 + c * 16;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16* b = sm.kv + ks * kTileElems;
-        const int r0 = lq * 8 + (l16 >> 2);
-        const int ch = (col0 >> 3) + ((l16 & 3) >> 1);
-        const int sub = (l16 & 1) * 4;
-        const bf16x8 v = join(tr_read(&b[tile_off(r0, ch) + sub]), tr_read(&b[tile_off(r0 + 4, ch) + sub]));
-        if (c < kDotLds) sm.dot[wv][c][ks][lane] = v;
-        else dOT[c][ks] = v;
-      }
-    }
-    __syncthreads();
+      for (int ks = 0; ks < 2; ++ks) sm.dot[wv][c][ks][lane] = dOT[c][ks];
   }
 
   f32x4 dQ[36];
