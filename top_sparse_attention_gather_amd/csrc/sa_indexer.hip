@@ -79,7 +79,9 @@ __global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lq = lane >> 4;
-  const int t = a.t0 + blockIdx.x;
+  // tokens in descending order: with causal selection the late tokens use
+  // the most slots, so the short rows come last and fill the grid's tail
+  const int t = a.t0 + (a.Tc - 1 - (int)blockIdx.x);
   const int H = a.H;
   const SeqPos s = seq_pos(p, t);
   const int* irow = p.idx + (size_t)t * p.topk;
