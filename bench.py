@@ -43,8 +43,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     ("mla_token_8k", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
-        "sha256": "eccdc5ca9b2fbd900a260cedc62b4b8eedc9d6d28c1cb467012b25b8d155ba93",
-        "fetch_bytes": 8369911936, "write_bytes": 17519300960,
+        "sha256": "486eeabb0c779130caf2b2d6c0f5d13f4451a8daf243d5b263493a2a9ebefc50",
+        "fetch_bytes": 8352420891, "write_bytes": 17519313280,
     },
 }
 
