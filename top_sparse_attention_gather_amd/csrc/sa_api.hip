@@ -486,8 +486,17 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   };
 
   const size_t Hkv = (size_t)desc->n_kv_heads;
-  SA_TRY_HIP(sa::launch_preprocess(p, w, s));
-  if (desc->has_sinks) SA_TRY_HIP(sa::launch_dsinks(p, w, s));
+  // With short rows (at most 1024 positions, e.g. window + cmp) the MLA
+  // kernel (deterministic mode) forms D and the dSinks terms from its own
+  // staged dO and O: the separate pass would re-read dO and O of many tokens
+  // per unit of main-kernel work.  Every other call takes them from the
+  // preprocess.
+  const bool fused_d = desc->dkv_mode == SA_DKV_DETERMINISTIC && L.fast && n_positions_host(desc) <= 1024;
+  w.fuse_d = fused_d ? 1 : 0;
+  if (!fused_d) {
+    SA_TRY_HIP(sa::launch_preprocess(p, w, s));
+    if (desc->has_sinks) SA_TRY_HIP(sa::launch_dsinks(p, w, s));
+  }
 
   if (desc->dkv_mode == SA_DKV_ATOMIC) {
     w.acc_k = reinterpret_cast<float*>(ws + L.acc_k);
@@ -585,6 +594,7 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     SA_TRY_HIP(sa::launch_reduce(p, r, s));
     first = false;
   }
+  if (fused_d && desc->has_sinks) SA_TRY_HIP(sa::launch_dsinks(p, w, s));
   SA_TRY_HIP(l1_norm());
   bf16* out_a = static_cast<bf16*>(desc->kv_shared ? a->dkv : a->dk);
   bf16* out_b = desc->kv_shared ? nullptr : static_cast<bf16*>(a->dv);

@@ -171,10 +171,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   const int cnt =
       compact_positions_batched<kMaxPos / 256>(p, s, irow, npos, sm.rows, sm.wave, sm.vpos, row_len(p, row));
 
-  // ---- lse / D of the wave's heads (phase-A layout: head = 16 wv + l16) ---
+  // ---- lse / D of the wave's heads (phase-A layout: head = 16 wv + l16);
+  // with fuse_d, D follows from the staged dO and O below -------------------
   const int hA = h0 + wv * 16 + l16;
   const float lse = p.lse[(size_t)t * p.Hq + hA];
-  const float Dv = w.D[(size_t)t * p.Hq + hA];
+  float Dv = w.fuse_d ? 0.f : w.D[(size_t)t * p.Hq + hA];
   const float kLog2e = 1.4426950408889634f;
   const float lse2 = lse * kLog2e;
   const float sl2 = p.scale * kLog2e;
@@ -183,7 +184,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   // ---- Q and dO into registers, via LDS, in both operand layouts ---------
   // Q goes to the two KV tile buffers and dO to the exchange / dO^T-block
   // area (both free until the tile loop), with all the loads in flight
-  // together; one wait, then both are read out.
+  // together (with fuse_d, so do the O rows of the wave's 16 heads, into
+  // registers); one wait, then (fuse_d) D = rowsum(dO o O) (SparseFlashMlaGrad
+  // README, Stage 2) and the operand layouts are read out.
   bf16x8 QA[18], dOA[16];          // phase A: [head 16wv + l16][32kk + 8lq .. +8]
   bf16x8 QT[9][2], dOT[8][2];      // phase B: [col][heads 32ks + 8lq .. +8]
   {
@@ -205,7 +208,33 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
                      sm.dost + hb * kDoTileElems + group_base(wv, kDoGroupStride) + sg * kSegElems);
       }
     }
+    uint4 orow[16];   // O of head 16wv + i, columns 8 lane .. 8 lane + 7
+    if (w.fuse_d) {
+      const bf16* ob = p.o + ((size_t)t * p.Hq + h0 + wv * 16) * kDV + lane * 8;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) orow[i] = *reinterpret_cast<const uint4*>(ob + (size_t)i * kDV);
+    }
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    // D of head 16wv + i: the lane's 8 products with chunk `lane` of the
+    // staged dO row, summed over the 64 lanes; lane l16 keeps head l16's
+    if (w.fuse_d) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hh = wv * 16 + i;
+        const bf16x8 dv = *reinterpret_cast<const bf16x8*>(
+            &sm.dost[(hh >> 5) * kDoTileElems + tile_off(hh & 31, lane, kDoGroupStride)]);
+        const bf16x8 ov = __builtin_bit_cast(bf16x8, orow[i]);
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a += (float)ov[j] * (float)dv[j];
+        a = wave_sum(a);
+        Dv = l16 == i ? a : Dv;
+      }
+      // the dSinks term of each (token, head) row (SparseFlashMlaGrad
+      // README, Stage 3), summed over the tokens after the kernel
+      if (p.has_sinks && lq == 0)
+        w.sink_term[(size_t)t * p.Hq + hA] = lse > -INFINITY ? -__expf(p.sinks[hA] - lse) * Dv : 0.f;
+    }
     // QA / dOA: head 16wv + l16 = buffer wv / 2, local row 16 (wv % 2) + l16
     const int qrow = (wv & 1) * 16 + l16;
     const bf16* qa = sm.kv + (wv >> 1) * kTileElems;

@@ -16,6 +16,7 @@ namespace sa {
 struct BwdBuffers {
   float* D;          // [T][Hq] softmax-grad term
   float* sink_term;  // [T][Hq] per-row dSinks terms (sinks only)
+  int fuse_d;        // MLA kernel: form D (and the dSinks terms) itself instead of reading D
   float* acc_k;      // fp32 dK (or shared dKV) accumulator, rows x Hkv x dqk (atomic mode)
   float* acc_v;      // fp32 dV accumulator (separate V, atomic mode)
   float* acc_cmp;    // fp32 dCmpKV accumulator (window+cmp, atomic mode)
