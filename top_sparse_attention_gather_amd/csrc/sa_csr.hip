@@ -163,16 +163,33 @@ __global__ __launch_bounds__(kThreads) void slot_keys_hist_kernel(Params p, long
   __syncthreads();
   const long long i0 = blockIdx.x * per_block;
   const long long i1 = std::min(n, i0 + per_block);
-  for (long long i = i0 + threadIdx.x; i < i1; i += kThreads) {
-    const long long slot = slot0 + i;
-    const int row = (int)(slot / p.topk);
-    const int t = row / p.Hkv, g = row - t * p.Hkv;
-    const SeqPos s = seq_pos(p, t);
-    const int key = (int)(slot - (long long)row * p.topk) < row_len(p, row)
-                        ? slot_key(p, s, g, p.idx[slot], blk_base, sentinel)
-                        : sentinel;
-    keys[i] = key;
-    if (key != sentinel) atomicAdd(&hist[key], 1);
+  // The thread's slots are i0 + tid, i0 + tid + 256, ...: its (row, slot in
+  // row) pair advances by 256 slots per step, and the row's sequence data
+  // is recomputed only when the row changes.
+  long long i = i0 + threadIdx.x;
+  if (i < i1) {
+    int row = (int)((slot0 + i) / p.topk);
+    int sl = (int)(slot0 + i - (long long)row * p.topk);
+    int cur = -1, g = 0, len = 0;
+    SeqPos s;
+    for (; i < i1; i += kThreads) {
+      if (row != cur) {
+        cur = row;
+        const int t = row / p.Hkv;
+        g = row - t * p.Hkv;
+        s = seq_pos(p, t);
+        len = row_len(p, row);
+      }
+      const int key = sl < len ? slot_key(p, s, g, p.idx[slot0 + i], blk_base, sentinel) : sentinel;
+      keys[i] = key;
+      if (key != sentinel) atomicAdd(&hist[key], 1);
+      sl += kThreads;
+      if (sl >= p.topk) {
+        const int q = sl / p.topk;
+        row += q;
+        sl -= q * p.topk;
+      }
+    }
   }
   __syncthreads();
   for (int k = threadIdx.x; k < n_keys; k += kThreads)
