@@ -375,7 +375,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   // tile) are restrict-qualified: they never overlap, and the alias scopes
   // this gives every LDS access let the compiler skip waiting for the
   // in-flight loads before each LDS read.
-  auto step = [&](const bf16* __restrict__ kvb, bf16* __restrict__ kvn, int it) {
+  // PB: whether the tile before this one exists, i.e. whether its phase B
+  // runs here (not for the first tile)
+  auto step = [&](auto pb, const bf16* __restrict__ kvb, bf16* __restrict__ kvn, int it) {
+    constexpr bool PB = decltype(pb)::value;
     const int k0 = it * kNT;
     const int nvalid = min(kNT, cnt - k0);
     // every wave's loads of this tile are done and the previous tile's
@@ -423,17 +426,21 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
       for (int kk = 0; kk < kPF; ++kk)
         f[kk] = *reinterpret_cast<const bf16x8*>(&kvb[off + (kk >> 1) * kSegElems + (kk & 1) * 32]);
       f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = S;
-      // phase B of the previous tile, key half b (for the first tile the
-      // products run on stale exchange data and go to the dump row)
-      const BHalf hb = b_setup(it - 1, b, it > 0);
+      // phase B of the previous tile, key half b (none for the first tile)
+      BHalf hb;
+      if constexpr (PB) hb = b_setup(it - 1, b, true);
       f32x4 br[9];
       // the dO^T operands of each chain are read one chain ahead (and the
       // KV fragments kPF steps ahead): the scheduling barriers keep those
       // LDS reads in front of the MFMAs that do not need them yet
-      bf16x8 od0 = dot_op(0, 0), od1 = dot_op(0, 1);
+      bf16x8 od0, od1;
+      if constexpr (PB) {
+        od0 = dot_op(0, 0);
+        od1 = dot_op(0, 1);
+      }
 #pragma unroll
       for (int kk = 0; kk < 18; ++kk) {
-        if ((kk & 1) == 0) {
+        if (PB && (kk & 1) == 0) {
           const int cc = kk >> 1;
           br[cc] = b_chain(hb, cc, cc < kDotLds ? od0 : dot_op(cc, 0), cc < kDotLds ? od1 : dot_op(cc, 1));
           if (cc + 1 < kDotLds) {
@@ -458,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
         if (kk < 16) dP = mfma16x16x32(a, dOA[kk], dP);
         if (b == 1 && kk == 2) softmax_grad(0, Sh0, Ph0);
       }
-      b_put_single(hb, 8, br[8]);
+      if constexpr (PB) b_put_single(hb, 8, br[8]);
       if (b == 0) {
         Sh0 = S;
         Ph0 = dP;
@@ -505,10 +512,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
       }
     }
   };
-  for (int it = 0; it < ntiles; ++it) {
+  if (ntiles > 0) step(std::false_type{}, sm.kv, sm.kv + kTileElems, 0);
+  for (int it = 1; it < ntiles; ++it) {
     const bf16* b0 = sm.kv + (it & 1) * kTileElems;
     bf16* b1 = sm.kv + ((it + 1) & 1) * kTileElems;
-    step(b0, b1, it);
+    step(std::true_type{}, b0, b1, it);
   }
 
   // phase B of the last tile
