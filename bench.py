@@ -43,8 +43,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     ("mla_token_8k", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
-        "sha256": "486eeabb0c779130caf2b2d6c0f5d13f4451a8daf243d5b263493a2a9ebefc50",
-        "fetch_bytes": 8352420891, "write_bytes": 17519313280,
+        "sha256": "4315d1cee8178fd5dc0af23bd67533e6d8539708d1f65bb077fd87e75be20962",
+        "fetch_bytes": 8614558034, "write_bytes": 17522023584,
     },
 }
 
