@@ -20,10 +20,16 @@
 //     heads, with KV^T of the wave's columns only (transposing
 //     ds_read_b64_tr_b16 reads) -- every wave reads a quarter of the tile
 //     instead of all of it.
-//   The next KV tile is gathered with direct global->LDS loads during
-//   phase A, so the gather latency is off the MFMA path.
-// Partial rows go to the token-major buffer consumed by the key-major
-// reduce (deterministic sum in CSR order).
+//   Phase B of a tile runs during the next tile's phase A (its MFMA chains
+//   and stores interleaved with the phase-A steps); the first tile has none
+//   before it and the last tile's runs after the loop.  The next KV tile is
+//   gathered with direct global->LDS loads during phase A, so the gather
+//   latency is off the MFMA path.
+// D = rowsum(dO o O) comes from the preprocess pass, or, for rows of at
+// most 1024 positions, is formed at the workgroup's start from the staged
+// dO and the O rows (with the dSinks terms).  Partial rows go to the
+// token-major buffer consumed by the key-major reduce (deterministic sum in
+// CSR order).
 #include <type_traits>
 
 #include "sa_launch.h"
@@ -37,7 +43,7 @@ constexpr int kNT = 32;            // keys per tile
 constexpr int kDQK = 576;
 constexpr int kDV = 512;
 constexpr int kHeads = 64;         // heads per workgroup
-constexpr int kKS = kDQK + 8;      // LDS row stride (elements) of KV / Q / dO tiles: 1168 B
+constexpr int kKS = kDQK + 8;      // sizes the KV tile / Q staging region: 64 rows of 1168 B
 constexpr int kXS = kHeads + 8;    // exchange row stride: 144 B
 constexpr int kMaxPos = 2048;
 // KV tile layout in LDS (32 rows x 72 chunks of 16 bytes): the rows form 4
