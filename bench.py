@@ -43,8 +43,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     ("mla_token_8k", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
-        "sha256": "4315d1cee8178fd5dc0af23bd67533e6d8539708d1f65bb077fd87e75be20962",
-        "fetch_bytes": 8614558034, "write_bytes": 17522023584,
+        "sha256": "bd5fe81f12724817e0ff7ba51034c3534d3a9cf92527330caa06f3e7d4d3dd34",
+        "fetch_bytes": 8163138173, "write_bytes": 17521873056,
     },
 }
 
