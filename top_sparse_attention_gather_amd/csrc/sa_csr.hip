@@ -216,9 +216,15 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(const int* __restr
 }
 
 // Stable scatter: element e = base + r * 256 + tid is ranked after every
-// element of an earlier round or a lower thread with the same digit.
+// element of an earlier round or a lower thread with the same digit.  The
+// ranks are tile-local and digit-major: the tile is first ordered in LDS
+// and then written out, so the elements of one digit go to consecutive
+// addresses (runs of ~kTile / 256) instead of one scattered store each.
 // FIRST: the input is the key array and p = val0 + e; otherwise (key, p)
 // pairs.  LAST: only p is written (to vals_out); otherwise (key, p) pairs.
+// offs: the exclusively scanned digit-major histogram, 256 * nb + 1 entries
+// (the last one the total), so a tile's count of digit d is the difference
+// of two neighbouring entries.
 template <bool FIRST, bool LAST>
 __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(const int* __restrict__ keys_in,
                                                                  const int2* __restrict__ pairs_in,
@@ -226,10 +232,18 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(const int* __re
                                                                  const int* __restrict__ offs,
                                                                  int2* __restrict__ pairs_out,
                                                                  int* __restrict__ vals_out) {
-  __shared__ int cnt[256];
+  __shared__ int cnt[256];     // next tile-local position of each digit
+  __shared__ int goff[256];    // global position of the digit's run minus its tile-local start
   __shared__ int wcnt[4][256];
+  __shared__ int sWave[4];
+  __shared__ int2 stage[kTile];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  cnt[tid] = offs[(long long)tid * nb + blockIdx.x];
+  const long long tix = (long long)tid * nb + blockIdx.x;
+  const int o = offs[tix];
+  int loc;
+  block_excl_scan(offs[tix + 1] - o, &loc, sWave);
+  cnt[tid] = loc;
+  goff[tid] = o - loc;
   for (int i = 0; i < 4; ++i) wcnt[i][tid] = 0;
   __syncthreads();
   const long long base = (long long)blockIdx.x * kTile;
@@ -261,13 +275,20 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(const int* __re
     if (ok) {
       int rank = cnt[d] + __popcll(peers & lt);
       for (int ww = 0; ww < w; ++ww) rank += wcnt[ww][d];
-      if (LAST) vals_out[rank] = val;
-      else pairs_out[rank] = make_int2(key, val);
+      stage[rank] = make_int2(key, val);
     }
     __syncthreads();
     cnt[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
     wcnt[0][tid] = wcnt[1][tid] = wcnt[2][tid] = wcnt[3][tid] = 0;
     __syncthreads();
+  }
+  // the tile in digit-major order: element j of digit d goes to goff[d] + j
+  const int m = (int)std::min<long long>(kTile, n - base);
+  for (int j = tid; j < m; j += kThreads) {
+    const int2 kv = stage[j];
+    const int pos = goff[(kv.x >> shift) & 255] + j;
+    if (LAST) vals_out[pos] = kv.y;
+    else pairs_out[pos] = kv;
   }
 }
 
@@ -295,7 +316,7 @@ CsrWs carve(void* ws, long long n, long long n_keys) {
   CsrWs c;
   char* p = static_cast<char*>(ws);
   c.nb_tiles = (n + kTile - 1) / kTile;
-  const long long hist_n = 256 * c.nb_tiles;
+  const long long hist_n = 256 * c.nb_tiles + 1;   // + the total
   const long long scan_n = std::max(hist_n, n_keys + 1);
   c.nb_scan = (scan_n + kScanChunk - 1) / kScanChunk;
   c.keys = reinterpret_cast<int*>(p); p += align256(n * 4);
@@ -329,7 +350,7 @@ long long scan_bsum_ints(long long n) { return (n + kScanChunk - 1) / kScanChunk
 
 size_t csr_workspace_bytes(long long n, long long n_keys, int batch) {
   const long long nb_tiles = (n + kTile - 1) / kTile;
-  const long long hist_n = 256 * nb_tiles;
+  const long long hist_n = 256 * nb_tiles + 1;
   const long long scan_n = std::max(hist_n, n_keys + 1);
   const long long nb_scan = (scan_n + kScanChunk - 1) / kScanChunk;
   return align256(n * 4) + align256(n * 8) * (csr_passes(n_keys) > 2 ? 2 : 1) + align256((n_keys + 1) * 4) +
@@ -373,7 +394,7 @@ hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_key
     const int* hkeys = first ? c.keys : reinterpret_cast<const int*>(pin);
     hipLaunchKernelGGL(radix_hist_kernel, dim3(nb), dim3(kThreads), 0, s, hkeys, first ? 1 : 2, n, pass * 8, nb,
                        c.hist);
-    if ((e = scan_excl(c.hist, 256LL * nb, c.hist, 256LL * nb, c.bsum, s)) != hipSuccess) return e;
+    if ((e = scan_excl(c.hist, 256LL * nb, c.hist, 256LL * nb + 1, c.bsum, s)) != hipSuccess) return e;
     if (first && last)
       hipLaunchKernelGGL((radix_scatter_kernel<true, true>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, slot0, n,
                          pass * 8, nb, c.hist, pout, entries);
