@@ -180,6 +180,29 @@ def test_fwd_parity_small(name):
     np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
 
 
+# rows with more selected positions than one compaction pass holds (2048):
+# 2300 slots per row over 2400 tokens, so the late tokens are compacted in
+# two passes by the row kernels
+LONG_ROWS = _wl(name="long_rows", seqlens=(2400,), n_q_heads=2, n_kv_heads=1, topk=2300, seed=78)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_rows_longer_than_one_compaction_pass(mode):
+    U.say(f"[long rows] {mode}")
+    res, got, ref = U.run_full_case(LONG_ROWS, dkv_mode=MODES[mode], l1=True)
+    assert int((W.make_index_inputs(LONG_ROWS)["idx"].numpy()[-1] >= 0).sum()) > 2048
+
+
+def test_fwd_rows_longer_than_one_compaction_pass():
+    inp = W.make_inputs(LONG_ROWS)
+    U.say("[long rows] fwd")
+    out_ref, lse_ref = O.sparse_fwd(O.Problem(inp))
+    o, lse = B.sparse_attn_fwd(B.make_desc(LONG_ROWS), B.device_tensors(inp))
+    torch.cuda.synchronize()
+    check_close("long_rows:o", o.float().cpu().numpy(), out_ref)
+    np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
+
+
 def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINISTIC, l1=False):
     """Full-size run where only the compared rows need the oracle: GPU
     forward supplies O/lse for all tokens, the oracle's own O/lse replace
@@ -260,6 +283,16 @@ def test_softmax_l1_full_size_sampled(name):
     configuration (MLA kernel, block dQ kernel, window + cmp), sampled
     token rows, with the gradients of the same call."""
     _tail_splice_case(W.WORKLOADS[name], dkv_mode=B.DKV_DETERMINISTIC, l1=True)
+
+
+@pytest.mark.parametrize("mode", ["det", "atomic"])
+def test_bwd_mla_rows_longer_than_the_mla_kernel_takes(mode):
+    """Shared-KV 576/512 with 64 heads and 2100 positions per row: past the
+    64-head MLA kernel's 2048, so the generic row kernel (two compaction
+    passes) runs; the last tokens against the oracle."""
+    wl = W.Workload(name="mla_long_rows", select=W.SEL_TOKEN, layout=W.LAYOUT_BSND, seqlens=(2200,), n_q_heads=64,
+                    n_kv_heads=1, d_qk=576, d_v=512, kv_shared=True, topk=2100, kv_std=0.5, seed=79)
+    _tail_splice_case(wl, n_tail=8, n_early=2, dkv_mode=B.DKV_DETERMINISTIC if mode == "det" else B.DKV_ATOMIC)
 
 
 def test_bwd_parity_mla_32k_full_size_sampled():
