@@ -180,6 +180,18 @@ def test_fwd_parity_small(name):
     np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
 
 
+@pytest.mark.parametrize("bs", [8, 20, 128])
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_block_sizes_off_the_block_dq_kernel(mode, bs):
+    """Block sizes the block dQ kernel does not take (not a multiple of 16:
+    dQ from the row kernel, dK/dV key-major; above 64: the row kernel with
+    partial rows), ragged last block, both dK/dV modes."""
+    wl = _wl(name=f"block_bs{bs}", select=W.SEL_BLOCK, seqlens=(300,), n_q_heads=4, n_kv_heads=1, topk=4,
+             block_size=bs, index_policy="own_block_plus_uniform", seed=80 + bs)
+    U.say(f"[block bs={bs}] {mode}")
+    U.run_full_case(wl, dkv_mode=MODES[mode], l1=True)
+
+
 # rows with more selected positions than one compaction pass holds (2048):
 # 2300 slots per row over 2400 tokens, so the late tokens are compacted in
 # two passes by the row kernels
