@@ -192,6 +192,18 @@ def test_bwd_block_sizes_off_the_block_dq_kernel(mode, bs):
     U.run_full_case(wl, dkv_mode=MODES[mode], l1=True)
 
 
+@pytest.mark.parametrize("heads", [1, 20])
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_mla_head_counts_off_the_mla_kernel(mode, heads):
+    """Shared-KV 576/512 with a head count that is not a multiple of 64 (the
+    pages allow 1 to 128): the generic row kernel, with a ragged head chunk
+    for 20 heads, both dK/dV modes."""
+    wl = _wl(name=f"mla_{heads}h", seqlens=(200,), n_q_heads=heads, d_qk=576, d_v=512, kv_shared=True, topk=80,
+             kv_std=0.5, seed=90 + heads)
+    U.say(f"[mla heads={heads}] {mode}")
+    U.run_full_case(wl, dkv_mode=MODES[mode], l1=True)
+
+
 # rows with more selected positions than one compaction pass holds (2048):
 # 2300 slots per row over 2400 tokens, so the late tokens are compacted in
 # two passes by the row kernels
