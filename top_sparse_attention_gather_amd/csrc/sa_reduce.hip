@@ -14,6 +14,9 @@ namespace sa {
 
 namespace {
 
+// Every partial row is read exactly once, so the loads are non-temporal:
+// the rows stream past the caches instead of evicting lines that are still
+// in use (measured on the 8192-token shared-KV shape: 5.9 -> 6.6 TB/s).
 template <typename PT>
 struct Vec8;
 
@@ -21,7 +24,11 @@ template <>
 struct Vec8<float> {
   static constexpr int kPer = 4;   // columns per thread-step
   typedef float4 T;
-  __device__ static T load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static T load(const float* p) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+  }
   __device__ static void add(const T& v, float* acc) {
     acc[0] += v.x;
     acc[1] += v.y;
@@ -34,7 +41,7 @@ template <>
 struct Vec8<bf16> {
   static constexpr int kPer = 8;
   typedef bf16x8 T;
-  __device__ static T load(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  __device__ static T load(const bf16* p) { return __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p)); }
   __device__ static void add(const T& v, float* acc) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += (float)v[i];
@@ -154,9 +161,9 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           ok[u] = e + u < ee;
-          const long long slot = r.entries[ok[u] ? e + u : eb];
-          const long long prow = slot / p.topk;
-          const int s = (int)(slot - prow * p.topk);
+          const int slot = r.entries[ok[u] ? e + u : eb];
+          const int prow = (int)((unsigned)slot / (unsigned)p.topk);   // slot ids are int32
+          const int s = slot - prow * p.topk;
           if (ok[u] && p.causal) {
             const SeqPos sp = seq_pos(p, (int)(prow / p.Hkv));
             ok[u] = jl <= sp.tl;     // row masked inside the selected block
@@ -167,15 +174,20 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
       }
     } else {
       const int eb = r.row_ptr[kcsr], ee = r.row_ptr[kcsr + 1];
+      // Flat slot id (row * topk + s) -> partial row (row - row0) * npos +
+      // nwin + s.  Here npos = nwin + topk, so that is slot + (row + 1) *
+      // nwin - row0 * npos: no division unless there are window positions
+      // (slot ids are int32, so a 32-bit one then).
+      const long long pos0 = -row0 * npos;
       for (int e = eb; e < ee; e += kBatch) {
         long long offs[kBatch];
         bool ok[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           ok[u] = e + u < ee;
-          const long long slot = r.entries[ok[u] ? e + u : eb];
-          const long long prow = slot / p.topk;
-          offs[u] = offset_of(prow, nwin + (int)(slot - prow * p.topk));
+          const int slot = r.entries[ok[u] ? e + u : eb];
+          const int prow = nwin ? (int)((unsigned)slot / (unsigned)p.topk) : 0;
+          offs[u] = ((long long)slot + (long long)(prow + 1) * nwin + pos0) * r.RW + col;
         }
         add_batch(offs, ok);
       }
