@@ -51,13 +51,23 @@ struct Vec8<bf16> {
 constexpr int kBatch = 16;  // partial rows whose loads are in flight together
 
 // One group of TPR threads per output row; each thread owns kPer columns.
-template <typename PT>
+// SPLIT (token selection only, TPR a divisor of 64 below 64): one wave per
+// output row, whose 64 / TPR sub-groups take the row's CSR list in
+// interleaved batches (sub-group q: batches q, q + 64 / TPR, ...); their sums
+// are then added in sub-group order.  Short rows (few columns) otherwise
+// leave most of the GPU idle while the longest list is walked one batch
+// after another, each batch waiting for its entries and then its rows.
+template <typename PT, bool SPLIT>
 __global__ void reduce_kernel(Params p, ReduceArgs r) {
   constexpr int kPer = Vec8<PT>::kPer;
   const int tpr = r.RW / kPer;
+  const int grp = SPLIT ? 64 : tpr;                      // threads per output row
+  const int nsg = SPLIT ? 64 / tpr : 1;                  // sub-groups per output row
+  const int sg = SPLIT ? (int)(threadIdx.x & 63) / tpr : 0;
   const int sub = threadIdx.x % tpr;
-  const long long lin = (long long)blockIdx.x * (blockDim.x / tpr) + threadIdx.x / tpr;
-  if (lin >= r.n_out_rows || threadIdx.x / tpr >= blockDim.x / tpr) return;
+  const long long lin = (long long)blockIdx.x * (blockDim.x / grp) + threadIdx.x / grp;
+  // SPLIT: lin is uniform over the wave, so whole waves leave here
+  if (lin >= r.n_out_rows || threadIdx.x / grp >= blockDim.x / grp) return;
   // Heavy rows first: the cmp rows (each named by the cmp slots of many
   // queries) are scheduled before the window rows (at most win_left + 1 +
   // win_right partials each), so the long sums do not form the grid's tail.
@@ -179,7 +189,7 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
       // nwin - row0 * npos: no division unless there are window positions
       // (slot ids are int32, so a 32-bit one then).
       const long long pos0 = -row0 * npos;
-      for (int e = eb; e < ee; e += kBatch) {
+      for (int e = eb + sg * kBatch; e < ee; e += nsg * kBatch) {
         long long offs[kBatch];
         bool ok[kBatch];
 #pragma unroll
@@ -192,6 +202,16 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
         add_batch(offs, ok);
       }
     }
+  }
+  if constexpr (SPLIT) {
+    // sub-group sums in sub-group order (lane sub + q * tpr: sub-group q)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      float t = __shfl(acc[i], sub);
+      for (int q = 1; q < nsg; ++q) t += __shfl(acc[i], sub + q * tpr);
+      acc[i] = t;
+    }
+    if (sg != 0) return;
   }
   float* dst = r.acc + orow * (long long)r.RW + col;
   if (r.accumulate) {
@@ -222,13 +242,20 @@ hipError_t launch_reduce(const Params& p, const ReduceArgs& r, hipStream_t s) {
   if (r.n_out_rows == 0) return hipSuccess;
   const int kPer = r.partial_bf16 ? 8 : 4;
   const int tpr = r.RW / kPer;
-  const int rpw = std::max(1, 512 / tpr);
-  const int threads = tpr * rpw;
+  // token selection: every output row takes the CSR branch, which is the
+  // one that splits its list
+  const bool split = p.select == kSelToken && tpr < 64 && 64 % tpr == 0;
+  const int grp = split ? 64 : tpr;
+  const int rpw = std::max(1, 512 / grp);
+  const int threads = grp * rpw;
   const unsigned blocks = (unsigned)((r.n_out_rows + rpw - 1) / rpw);
-  if (r.partial_bf16)
-    hipLaunchKernelGGL(reduce_kernel<bf16>, dim3(blocks), dim3(threads), 0, s, p, r);
-  else
-    hipLaunchKernelGGL(reduce_kernel<float>, dim3(blocks), dim3(threads), 0, s, p, r);
+  if (r.partial_bf16) {
+    if (split) hipLaunchKernelGGL((reduce_kernel<bf16, true>), dim3(blocks), dim3(threads), 0, s, p, r);
+    else hipLaunchKernelGGL((reduce_kernel<bf16, false>), dim3(blocks), dim3(threads), 0, s, p, r);
+  } else {
+    if (split) hipLaunchKernelGGL((reduce_kernel<float, true>), dim3(blocks), dim3(threads), 0, s, p, r);
+    else hipLaunchKernelGGL((reduce_kernel<float, false>), dim3(blocks), dim3(threads), 0, s, p, r);
+  }
   return hipGetLastError();
 }
 
