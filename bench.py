@@ -267,6 +267,89 @@ def bench_indexer(args):
     print(json.dumps(line), flush=True)
 
 
+def fwd_flops_per_pair(wl: W.Workload) -> int:
+    """S = q K^T and O = P V: 2 (d_qk + d_v) per head and selected row."""
+    return wl.group * 2 * (wl.d_qk + wl.d_v)
+
+
+def bench_forward(args):
+    """Selected-attention forward (O and lse), the step before the backward:
+    one step = one sparse_attn_fwd call, a single kernel launch, so the
+    per-call events time that kernel."""
+    wl = W.WORKLOADS[args.workload]
+    log(f"[bench] workload {wl.name} (forward): generating inputs")
+    inputs = W.make_inputs(wl, threads=16)
+    idx = inputs["idx"].numpy()
+    pairs = valid_pairs(wl, idx)
+    flop = pairs * fwd_flops_per_pair(wl)
+    dev = B.device_tensors(inputs)
+    desc = B.make_desc(wl)
+    stream = torch.cuda.current_stream()
+    o, lse = B.sparse_attn_fwd(desc, dev, stream=stream)
+    for _ in range(args.warmup):
+        B.sparse_attn_fwd(desc, dev, o, lse, stream=stream)
+    torch.cuda.synchronize()
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} forward steps")
+    t_start.record(stream)
+    for i in range(args.steps):
+        calls[i][0].record(stream)
+        B.sparse_attn_fwd(desc, dev, o, lse, stream=stream)
+        calls[i][1].record(stream)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in calls]
+    ms = t_start.elapsed_time(t_stop) / args.steps
+    kern_ms = float(np.mean(call_ms))
+    if not torch.isfinite(o.float()).all():
+        raise RuntimeError("non-finite values in o")
+    tflops = flop / (ms * 1e-3) / 1e12
+    kern_tflops = flop / (kern_ms * 1e-3) / 1e12
+    log(f"[bench] forward {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import sparse_attn_oracle as O   # the oracle is only timed here
+        try:
+            import threadpoolctl
+            threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        pb = O.Problem(inputs)
+        T = wl.total_q
+        done, fl, spent, chunk = 0, 0, 0.0, 8
+        while spent < args.cpu_budget and done < T:
+            toks = list(range(T - done - chunk, T - done))
+            t0 = time.perf_counter()
+            O.sparse_fwd(pb, toks)
+            spent += time.perf_counter() - t0
+            fl += sum(pb.selection(t, g)[1].size for t in toks for g in range(wl.n_kv_heads)) * fwd_flops_per_pair(wl)
+            done += chunk
+            chunk = min(2 * chunk, 64)
+        cpu = {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"fp64 numpy oracle sparse_fwd on the last {done} of {T} query tokens of {wl.name} "
+                         f"({fl / 1e12:.3f} TFLOP in {spent:.1f} s)"}
+    kernel = "fwd_mla_kernel" if (wl.d_qk, wl.d_v, wl.kv_shared) == (576, 512, True) and wl.group % 64 == 0 \
+        else "fwd_rows_kernel"
+    line = {
+        "metric": "sparse-attn fwd TFLOP/s (selected-KV FLOPs), 1 GPU",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name} forward: B={wl.batch} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} "
+                               f"d_qk={wl.d_qk} d_v={wl.d_v} top-{wl.topk}",
+                   "valid_pairs": pairs, "selected_kv_tflop": round(flop / 1e12, 4),
+                   "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "parallelism": "single GPU"},
+        "timing": {"call_ms": percentiles(call_ms), "step_time_from": "bracketed region / steps",
+                   "device": device_info()},
+        "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(kern_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel_ms": round(kern_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +357,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mla_token_8k",
                     choices=W.WORKLOAD_ORDER + list(W.INDEXER_WORKLOADS))
+    ap.add_argument("--op", default="bwd", choices=["bwd", "fwd"],
+                    help="bwd: the backward (the default line); fwd: the selected-attention forward alone")
     ap.add_argument("--dkv-mode", default="deterministic", choices=["atomic", "deterministic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--softmax-l1", action="store_true",
@@ -304,6 +389,9 @@ def main():
 
     if args.workload in W.INDEXER_WORKLOADS:
         bench_indexer(args)
+        return
+    if args.op == "fwd":
+        bench_forward(args)
         return
     wl = W.WORKLOADS[args.workload]
     mode = B.DKV_ATOMIC if args.dkv_mode == "atomic" else B.DKV_DETERMINISTIC

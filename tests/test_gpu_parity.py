@@ -309,14 +309,34 @@ def test_softmax_l1_full_size_sampled(name):
     _tail_splice_case(W.WORKLOADS[name], dkv_mode=B.DKV_DETERMINISTIC, l1=True)
 
 
+MLA_LONG_ROWS = W.Workload(name="mla_long_rows", select=W.SEL_TOKEN, layout=W.LAYOUT_BSND, seqlens=(2200,),
+                           n_q_heads=64, n_kv_heads=1, d_qk=576, d_v=512, kv_shared=True, topk=2100, kv_std=0.5,
+                           seed=79)
+
+
 @pytest.mark.parametrize("mode", ["det", "atomic"])
 def test_bwd_mla_rows_longer_than_the_mla_kernel_takes(mode):
     """Shared-KV 576/512 with 64 heads and 2100 positions per row: past the
     64-head MLA kernel's 2048, so the generic row kernel (two compaction
     passes) runs; the last tokens against the oracle."""
-    wl = W.Workload(name="mla_long_rows", select=W.SEL_TOKEN, layout=W.LAYOUT_BSND, seqlens=(2200,), n_q_heads=64,
-                    n_kv_heads=1, d_qk=576, d_v=512, kv_shared=True, topk=2100, kv_std=0.5, seed=79)
-    _tail_splice_case(wl, n_tail=8, n_early=2, dkv_mode=B.DKV_DETERMINISTIC if mode == "det" else B.DKV_ATOMIC)
+    _tail_splice_case(MLA_LONG_ROWS, n_tail=8, n_early=2,
+                      dkv_mode=B.DKV_DETERMINISTIC if mode == "det" else B.DKV_ATOMIC)
+
+
+def test_fwd_mla_64_heads_rows_over_several_compaction_passes():
+    """Shared-KV 576/512 forward with 64 heads (the 64-head forward kernel)
+    and up to 2100 positions per row, i.e. three compaction passes of 1024
+    positions for the last tokens: sampled tokens against the oracle."""
+    inp = W.make_inputs(MLA_LONG_ROWS)
+    U.say("[mla long rows] fwd")
+    o, lse = B.sparse_attn_fwd(B.make_desc(MLA_LONG_ROWS), B.device_tensors(inp))
+    torch.cuda.synchronize()
+    T = MLA_LONG_ROWS.total_q
+    toks = [0, 1, 31, 32, 700, 1023, 1024, 1500, 2047, 2048] + list(range(T - 12, T))
+    out_ref, lse_ref = O.sparse_fwd(O.Problem(inp), toks)
+    sel = torch.tensor(toks, device=o.device)
+    check_close("mla_long_rows:o", o[sel].float().cpu().numpy(), out_ref)
+    np.testing.assert_allclose(lse[sel].cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
 
 
 def test_bwd_parity_mla_32k_full_size_sampled():

@@ -183,6 +183,183 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
   }
 }
 
+
+// Shared-KV 576/512 forward with 64 query heads per workgroup: the selected
+// rows of one (token, kv head) are gathered once for all 64 heads (the
+// generic kernel above gathers them once per 16-head chunk).
+//
+// Wave w owns heads 16w..16w+15.  Per tile of 32 rows it forms S^T = K Q^T
+// (16x16x32 MFMA, K from LDS, Q resident in registers), so that each lane
+// holds one head's logits for 4 consecutive rows: the layout of the A
+// operand of the 16x16x16 MFMA, so P = exp(S - m) feeds O += P V straight
+// from registers.  V is the first 512 columns of the same LDS rows, read
+// as B operands by transposing LDS reads.  The running max and sum of a
+// head live in the 4 lanes of its column (log2 domain); a sink logit
+// starts them at (sink, 1).  Tiles are double-buffered: the next tile's
+// rows are loaded into registers while the current one is computed.
+namespace mla_fwd {
+constexpr int kD = 576, kDV = 512;
+constexpr int kKS = kD + 8;        // LDS row stride (elements)
+constexpr int kRows = 32;            // rows per tile
+constexpr int kHeads = 64;         // query heads per workgroup
+constexpr int kCompact = 1024;      // positions compacted at a time
+constexpr int kChunks = kRows * kD / 8 / kThreads;   // 16-byte loads per thread and tile
+static_assert(kRows * kD / 8 == kChunks * kThreads, "tile load split");
+}  // namespace mla_fwd
+
+typedef __attribute__((address_space(3))) i16x4 fwd_lds_i16x4;
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restrict__ out_o,
+                                                           float* __restrict__ out_lse) {
+  using namespace mla_fwd;
+  typedef typename Elem<E>::V8 V8;
+  typedef typename Elem<E>::V4 V4;
+  __shared__ __attribute__((aligned(16))) E sK[2][kRows * kKS];
+  __shared__ int sRows[kCompact];
+  __shared__ int sWave[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int row = blockIdx.x;
+  const int t = row / p.Hkv, g = row - t * p.Hkv;
+  const int h0 = g * p.G + blockIdx.y * kHeads + wv * 16;   // the wave's first head
+  const SeqPos s = seq_pos(p, t);
+  const int* irow = p.idx + (size_t)row * p.topk;
+  const E* Kg = reinterpret_cast<const E*>(p.k);
+  const E* Cg = reinterpret_cast<const E*>(p.cmp);
+  const float sl2 = p.scale * 1.4426950408889634f;   // scale * log2(e)
+
+  // Q of head h0 + l16, columns 32kk + 8lq .. +7 (B operand of S^T)
+  V8 q[kD / 32];
+  {
+    const E* qrow = reinterpret_cast<const E*>(p.q) + ((size_t)t * p.Hq + h0 + l16) * kD + lq * 8;
+#pragma unroll
+    for (int kk = 0; kk < kD / 32; ++kk) q[kk] = *reinterpret_cast<const V8*>(qrow + kk * 32);
+  }
+  // running max (log2 units) and sum of head h0 + l16
+  const bool sk = p.has_sinks;
+  float m_run = sk ? p.sinks[h0 + l16] * 1.4426950408889634f : -INFINITY;
+  float l_run = sk ? 1.f : 0.f;
+  f32x4 acc[kDV / 16];
+#pragma unroll
+  for (int c = 0; c < kDV / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto src_of = [&](int code) -> const E* {
+    return (code & kCmpFlag) ? Cg + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * kD : Kg + ((size_t)code * p.Hkv + g) * kD;
+  };
+  // tile rows k0 .. k0 + 31 into registers (rows past cnt: zeros)
+  auto load_tile = [&](uint4* v, int k0, int cnt) {
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      const int c = tid + j * kThreads, r = c / (kD / 8), ch = c - r * (kD / 8);
+      v[j] = make_uint4(0, 0, 0, 0);
+      if (k0 + r < cnt) v[j] = *reinterpret_cast<const uint4*>(src_of(sRows[k0 + r]) + ch * 8);
+    }
+  };
+  auto store_tile = [&](const uint4* v, E* dst) {
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      const int c = tid + j * kThreads, r = c / (kD / 8), ch = c - r * (kD / 8);
+      *reinterpret_cast<uint4*>(dst + r * kKS + ch * 8) = v[j];
+    }
+  };
+
+  const int npos = n_positions(p);
+  for (int pos0 = 0; pos0 < npos; pos0 += kCompact) {
+    __syncthreads();   // the previous chunk's rows and tiles are no longer read
+    const int cnt =
+        compact_positions(p, s, irow, pos0, min(kCompact, npos - pos0), sRows, sWave, nullptr, row_len(p, row));
+    const int ntiles = (cnt + kRows - 1) / kRows;
+    if (ntiles == 0) continue;
+    uint4 pf[kChunks];
+    load_tile(pf, 0, cnt);
+    store_tile(pf, sK[0]);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int k0 = it * kRows;
+      const E* kb = sK[it & 1];
+      const bool more = it + 1 < ntiles;
+      if (more) load_tile(pf, k0 + kRows, cnt);
+
+      // S^T for rows k0 + 16b + 4lq + i (i < 4), head h0 + l16
+      float sv[2][4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        f32x4 st = {0.f, 0.f, 0.f, 0.f};
+        const E* arow = kb + (b * 16 + l16) * kKS + lq * 8;
+#pragma unroll
+        for (int kk = 0; kk < kD / 32; ++kk)
+          st = Elem<E>::mma32(*reinterpret_cast<const V8*>(arow + kk * 32), q[kk], st);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[b][i] = (k0 + b * 16 + lq * 4 + i < cnt) ? st[i] * sl2 : -INFINITY;
+      }
+      // online softmax over the tile's 32 rows (the 4 lanes of head l16)
+      float mx = sv[0][0];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[b][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float base = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - base);
+      float pr[2][4];
+      float sum = 0.f;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[b][i] = __builtin_amdgcn_exp2f(sv[b][i] - base);
+          sum += pr[b][i];
+        }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      l_run = l_run * alpha + sum;
+      m_run = m_new;
+      // O rows are heads 4lq + i: their rescale factors from lanes 4lq + i
+      f32x4 al;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, lq * 4 + i);
+#pragma unroll
+      for (int c = 0; c < kDV / 16; ++c) acc[c] = acc[c] * al;
+      // O += P V: A = P (head l16, rows 16b + 4lq + i), B = V^T by transposing
+      // reads of rows 16b + 4lq + l16/4, columns 16c + 4(l16 % 4)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        V4 pa;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pa[i] = (E)pr[b][i];
+        const E* vrow = kb + (b * 16 + lq * 4 + (l16 >> 2)) * kKS + (l16 & 3) * 4;
+#pragma unroll
+        for (int c = 0; c < kDV / 16; ++c) {
+          const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fwd_lds_i16x4*)(vrow + c * 16));
+          acc[c] = Elem<E>::mma16(pa, __builtin_bit_cast(V4, vb), acc[c]);
+        }
+      }
+      if (more) store_tile(pf, sK[(it + 1) & 1]);
+      __syncthreads();
+    }
+  }
+
+  // O = acc / l for heads h0 + 4lq + i; lse of head h0 + l16
+  float linv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float l = __shfl(l_run, lq * 4 + i);
+    linv[i] = l > 0.f ? 1.f / l : 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < kDV / 16; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out_o[((size_t)t * p.Hq + h0 + lq * 4 + i) * kDV + c * 16 + l16] = (E)(acc[c][i] * linv[i]);
+  if (lq == 0)
+    out_lse[(size_t)t * p.Hq + h0 + l16] =
+        l_run > 0.f ? m_run * 0.6931471805599453f + __logf(l_run) : -INFINITY;
+}
+
 template <int DQK, int DV, bool SHARED>
 hipError_t launch_t(const Params& p, void* o, float* lse, hipStream_t s) {
   dim3 grid((unsigned)(p.T * p.Hkv), (unsigned)((p.G + kHC - 1) / kHC));
@@ -201,6 +378,14 @@ bool fwd_rows_supported(int dqk, int dv, int shared) {
 }
 
 hipError_t launch_fwd_rows(const Params& p, void* o, float* lse, hipStream_t s) {
+  if (p.dqk == 576 && p.dv == 512 && p.shared && p.G % mla_fwd::kHeads == 0) {
+    const dim3 grid((unsigned)(p.T * p.Hkv), (unsigned)(p.G / mla_fwd::kHeads));
+    if (p.fp16)
+      hipLaunchKernelGGL(fwd_mla_kernel<f16>, grid, dim3(kThreads), 0, s, p, static_cast<f16*>(o), lse);
+    else
+      hipLaunchKernelGGL(fwd_mla_kernel<bf16>, grid, dim3(kThreads), 0, s, p, static_cast<bf16*>(o), lse);
+    return hipGetLastError();
+  }
   if (p.dqk == 64 && p.dv == 64) return p.shared ? launch_t<64, 64, true>(p, o, lse, s) : launch_t<64, 64, false>(p, o, lse, s);
   if (p.dqk == 128 && p.dv == 128) return p.shared ? launch_t<128, 128, true>(p, o, lse, s) : launch_t<128, 128, false>(p, o, lse, s);
   if (p.dqk == 576 && p.dv == 512) return p.shared ? launch_t<576, 512, true>(p, o, lse, s) : launch_t<576, 512, false>(p, o, lse, s);
