@@ -190,24 +190,43 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
 //
 // Wave w owns heads 16w..16w+15.  Per tile of 32 rows it forms S^T = K Q^T
 // (16x16x32 MFMA, K from LDS, Q resident in registers), so that each lane
-// holds one head's logits for 4 consecutive rows: the layout of the A
-// operand of the 16x16x16 MFMA, so P = exp(S - m) feeds O += P V straight
-// from registers.  V is the first 512 columns of the same LDS rows, read
+// holds one head's logits for 4 consecutive rows of each 16-row half: with
+// the two halves side by side that is an A operand of the 16x16x32 MFMA,
+// so P = exp(S - m) feeds O += P V straight from registers.  V is the first 512 columns of the same LDS rows, read
 // as B operands by transposing LDS reads.  The running max and sum of a
 // head live in the 4 lanes of its column (log2 domain); a sink logit
-// starts them at (sink, 1).  Tiles are double-buffered: the next tile's
-// rows are loaded into registers while the current one is computed.
+// starts them at (sink, 1).  Tiles come by direct global->LDS loads, the
+// next one issued while the current one is computed (two buffers: on the
+// 8192-token top-2048 shape, three or four buffers measured no faster).
 namespace mla_fwd {
 constexpr int kD = 576, kDV = 512;
 constexpr int kKS = kD + 8;        // LDS row stride (elements)
 constexpr int kRows = 32;            // rows per tile
 constexpr int kHeads = 64;         // query heads per workgroup
 constexpr int kCompact = 1024;      // positions compacted at a time
-constexpr int kChunks = kRows * kD / 8 / kThreads;   // 16-byte loads per thread and tile
-static_assert(kRows * kD / 8 == kChunks * kThreads, "tile load split");
+constexpr int kRowChunks = kKS / 8;                 // 16-byte chunks per LDS row (the last one padding)
+constexpr int kTileChunks = kRows * kRowChunks;
+constexpr int kBufs = 2;                             // tile it and kBufs - 1 tiles issued ahead
+// direct loads per wave and tile: wave w issues instruction j when chunk
+// (4j + w) * 64 is inside the tile
+constexpr int loads_of_wave(int w) { return (kTileChunks - 1 - w * 64) / 256 + 1; }
+static_assert(loads_of_wave(0) == 10 && loads_of_wave(1) == 9 && loads_of_wave(2) == 9 && loads_of_wave(3) == 9,
+              "the per-wave wait counts below");
+static_assert(kBufs >= 2 && kBufs <= 4, "wait counts cover up to two tiles in flight");
 }  // namespace mla_fwd
 
 typedef __attribute__((address_space(3))) i16x4 fwd_lds_i16x4;
+typedef __attribute__((address_space(3))) void fwd_lds_void;
+
+// Direct global->LDS load of 16 bytes per lane to the wave-uniform LDS
+// address `lds` + 16 x lane.  Written as inline asm because the compiler
+// treats the builtin as a FLAT access that may touch LDS and would then
+// drain every LDS wait; the kernel waits for these loads itself (vmcnt).
+__device__ __forceinline__ void fwd_load_lds16(const void* src, void* lds) {
+  const unsigned base = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(fwd_lds_void*)lds);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
+}
+typedef short fwd_i16x8 __attribute__((ext_vector_type(8)));
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restrict__ out_o,
@@ -215,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
   using namespace mla_fwd;
   typedef typename Elem<E>::V8 V8;
   typedef typename Elem<E>::V4 V4;
-  __shared__ __attribute__((aligned(16))) E sK[2][kRows * kKS];
+  __shared__ __attribute__((aligned(16))) E sK[kBufs][kRows * kKS];
   __shared__ int sRows[kCompact];
   __shared__ int sWave[4];
 
@@ -236,6 +255,10 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
     const E* qrow = reinterpret_cast<const E*>(p.q) + ((size_t)t * p.Hq + h0 + l16) * kD + lq * 8;
 #pragma unroll
     for (int kk = 0; kk < kD / 32; ++kk) q[kk] = *reinterpret_cast<const V8*>(qrow + kk * 32);
+    // wait for Q here: the compiler does not count the direct loads below,
+    // so a wait for Q inside the tile loop would not be one it could place
+#pragma unroll
+    for (int kk = 0; kk < kD / 32; ++kk) asm volatile("" ::"v"(q[kk]));
   }
   // running max (log2 units) and sum of head h0 + l16
   const bool sk = p.has_sinks;
@@ -248,21 +271,32 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
   auto src_of = [&](int code) -> const E* {
     return (code & kCmpFlag) ? Cg + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * kD : Kg + ((size_t)code * p.Hkv + g) * kD;
   };
-  // tile rows k0 .. k0 + 31 into registers (rows past cnt: zeros)
-  auto load_tile = [&](uint4* v, int k0, int cnt) {
+  // rows k0 .. k0 + 31 of the compacted list into `buf` by direct loads;
+  // rows past cnt repeat row cnt - 1 (finite values, masked out of S), the
+  // padding chunk of each LDS row repeats its first chunk
+  auto issue_tile = [&](int k0, int cnt, E* buf) {
 #pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const int c = tid + j * kThreads, r = c / (kD / 8), ch = c - r * (kD / 8);
-      v[j] = make_uint4(0, 0, 0, 0);
-      if (k0 + r < cnt) v[j] = *reinterpret_cast<const uint4*>(src_of(sRows[k0 + r]) + ch * 8);
+    for (int j = 0; j < (kTileChunks + kThreads - 1) / kThreads; ++j) {
+      const int c0 = (j * 4 + wv) * 64;
+      if (c0 < kTileChunks) {
+        const int c = c0 + lane;
+        if (c < kTileChunks) {
+          const int r = c / kRowChunks, ch = c - r * kRowChunks;
+          const E* src = src_of(sRows[min(k0 + r, cnt - 1)]) + (ch < kD / 8 ? ch : 0) * 8;
+          fwd_load_lds16(src, buf + c0 * 8);
+        }
+      }
     }
   };
-  auto store_tile = [&](const uint4* v, E* dst) {
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const int c = tid + j * kThreads, r = c / (kD / 8), ch = c - r * (kD / 8);
-      *reinterpret_cast<uint4*>(dst + r * kKS + ch * 8) = v[j];
-    }
+  // this wave's loads of tile it are done (those of the `later` tiles
+  // issued after it may still be in flight), then every wave's: the tile
+  // is complete and tile it - 1 is no longer read
+  auto wait_tile = [&](int later) {   // tiles issued after tile it (0 .. kBufs - 2)
+    if (later == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (later == 1 && wv == 0) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (wv == 0) asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
   const int npos = n_positions(p);
@@ -272,15 +306,12 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
         compact_positions(p, s, irow, pos0, min(kCompact, npos - pos0), sRows, sWave, nullptr, row_len(p, row));
     const int ntiles = (cnt + kRows - 1) / kRows;
     if (ntiles == 0) continue;
-    uint4 pf[kChunks];
-    load_tile(pf, 0, cnt);
-    store_tile(pf, sK[0]);
-    __syncthreads();
+    for (int a = 0; a < kBufs - 1 && a < ntiles; ++a) issue_tile(a * kRows, cnt, sK[a]);
     for (int it = 0; it < ntiles; ++it) {
       const int k0 = it * kRows;
-      const E* kb = sK[it & 1];
-      const bool more = it + 1 < ntiles;
-      if (more) load_tile(pf, k0 + kRows, cnt);
+      const E* kb = sK[it % kBufs];
+      wait_tile(min(kBufs - 2, ntiles - 1 - it));
+      if (it + kBufs - 1 < ntiles) issue_tile(k0 + (kBufs - 1) * kRows, cnt, sK[(it + kBufs - 1) % kBufs]);
 
       // S^T for rows k0 + 16b + 4lq + i (i < 4), head h0 + l16
       float sv[2][4];
@@ -319,27 +350,32 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
       l_run = l_run * alpha + sum;
       m_run = m_new;
       // O rows are heads 4lq + i: their rescale factors from lanes 4lq + i
-      f32x4 al;
+      // (skipped when no head's max moved: the factors are then exactly 1)
+      if (__ballot(alpha != 1.f)) {
+        f32x4 al;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, lq * 4 + i);
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, lq * 4 + i);
 #pragma unroll
-      for (int c = 0; c < kDV / 16; ++c) acc[c] = acc[c] * al;
-      // O += P V: A = P (head l16, rows 16b + 4lq + i), B = V^T by transposing
-      // reads of rows 16b + 4lq + l16/4, columns 16c + 4(l16 % 4)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        V4 pa;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pa[i] = (E)pr[b][i];
-        const E* vrow = kb + (b * 16 + lq * 4 + (l16 >> 2)) * kKS + (l16 & 3) * 4;
-#pragma unroll
-        for (int c = 0; c < kDV / 16; ++c) {
-          const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fwd_lds_i16x4*)(vrow + c * 16));
-          acc[c] = Elem<E>::mma16(pa, __builtin_bit_cast(V4, vb), acc[c]);
-        }
+        for (int c = 0; c < kDV / 16; ++c) acc[c] = acc[c] * al;
       }
-      if (more) store_tile(pf, sK[(it + 1) & 1]);
-      __syncthreads();
+      // O += P V, one 16x16x32 MFMA per 16 columns: k-slot 8lq + j stands
+      // for row 4lq + j of the tile's first half (j < 4) or row 12 + 4lq + j
+      // of its second, in A (P of head l16) and in B alike; B = V^T from two
+      // transposing reads (rows 16b + 4lq + l16/4, columns 16c + 4(l16 % 4))
+      V8 pa;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pa[i] = (E)pr[0][i];
+        pa[4 + i] = (E)pr[1][i];
+      }
+      const E* vrow = kb + (lq * 4 + (l16 >> 2)) * kKS + (l16 & 3) * 4;
+#pragma unroll
+      for (int c = 0; c < kDV / 16; ++c) {
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fwd_lds_i16x4*)(vrow + c * 16));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fwd_lds_i16x4*)(vrow + 16 * kKS + c * 16));
+        const fwd_i16x8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[c] = Elem<E>::mma32(pa, __builtin_bit_cast(V8, vb), acc[c]);
+      }
     }
   }
 
