@@ -197,22 +197,18 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
 // head live in the 4 lanes of its column (log2 domain); a sink logit
 // starts them at (sink, 1).  Tiles come by direct global->LDS loads, the
 // next one issued while the current one is computed (two buffers: on the
-// 8192-token top-2048 shape, three or four buffers measured no faster).
+// 8192-token top-2048 shape, loads issued two or three tiles ahead measured
+// no faster).
 namespace mla_fwd {
 constexpr int kD = 576, kDV = 512;
-constexpr int kKS = kD + 8;        // LDS row stride (elements)
-constexpr int kRows = 32;            // rows per tile
-constexpr int kHeads = 64;         // query heads per workgroup
-constexpr int kCompact = 1024;      // positions compacted at a time
-constexpr int kRowChunks = kKS / 8;                 // 16-byte chunks per LDS row (the last one padding)
+constexpr int kKS = kD + 8;                    // LDS row stride (elements)
+constexpr int kRows = 32;                      // rows per tile (a multiple of 32)
+constexpr int kNB = kRows / 16;                // 16-row blocks per tile
+constexpr int kHeads = 64;                     // query heads per workgroup
+constexpr int kCompact = 1024;                 // positions compacted at a time
+constexpr int kRowChunks = kKS / 8;            // 16-byte chunks per LDS row (the last one padding)
 constexpr int kTileChunks = kRows * kRowChunks;
-constexpr int kBufs = 2;                             // tile it and kBufs - 1 tiles issued ahead
-// direct loads per wave and tile: wave w issues instruction j when chunk
-// (4j + w) * 64 is inside the tile
-constexpr int loads_of_wave(int w) { return (kTileChunks - 1 - w * 64) / 256 + 1; }
-static_assert(loads_of_wave(0) == 10 && loads_of_wave(1) == 9 && loads_of_wave(2) == 9 && loads_of_wave(3) == 9,
-              "the per-wave wait counts below");
-static_assert(kBufs >= 2 && kBufs <= 4, "wait counts cover up to two tiles in flight");
+static_assert(kRows % 32 == 0 && kCompact % kRows == 0, "tile shape");
 }  // namespace mla_fwd
 
 typedef __attribute__((address_space(3))) i16x4 fwd_lds_i16x4;
@@ -234,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
   using namespace mla_fwd;
   typedef typename Elem<E>::V8 V8;
   typedef typename Elem<E>::V4 V4;
-  __shared__ __attribute__((aligned(16))) E sK[kBufs][kRows * kKS];
+  __shared__ __attribute__((aligned(16))) E sK[2][kRows * kKS];
   __shared__ int sRows[kCompact];
   __shared__ int sWave[4];
 
@@ -288,16 +284,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
       }
     }
   };
-  // this wave's loads of tile it are done (those of the `later` tiles
-  // issued after it may still be in flight), then every wave's: the tile
-  // is complete and tile it - 1 is no longer read
-  auto wait_tile = [&](int later) {   // tiles issued after tile it (0 .. kBufs - 2)
-    if (later == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if (later == 1 && wv == 0) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if (wv == 0) asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
+  // every wave's loads of tile it are done (the tile is complete) and tile
+  // it - 1 is no longer read, so its buffer takes tile it + 1
+  auto wait_tile = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   const int npos = n_positions(p);
   for (int pos0 = 0; pos0 < npos; pos0 += kCompact) {
@@ -306,17 +295,17 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
         compact_positions(p, s, irow, pos0, min(kCompact, npos - pos0), sRows, sWave, nullptr, row_len(p, row));
     const int ntiles = (cnt + kRows - 1) / kRows;
     if (ntiles == 0) continue;
-    for (int a = 0; a < kBufs - 1 && a < ntiles; ++a) issue_tile(a * kRows, cnt, sK[a]);
+    issue_tile(0, cnt, sK[0]);
     for (int it = 0; it < ntiles; ++it) {
       const int k0 = it * kRows;
-      const E* kb = sK[it % kBufs];
-      wait_tile(min(kBufs - 2, ntiles - 1 - it));
-      if (it + kBufs - 1 < ntiles) issue_tile(k0 + (kBufs - 1) * kRows, cnt, sK[(it + kBufs - 1) % kBufs]);
+      const E* kb = sK[it & 1];
+      wait_tile();
+      if (it + 1 < ntiles) issue_tile(k0 + kRows, cnt, sK[(it + 1) & 1]);
 
       // S^T for rows k0 + 16b + 4lq + i (i < 4), head h0 + l16
-      float sv[2][4];
+      float sv[kNB][4];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < kNB; ++b) {
         f32x4 st = {0.f, 0.f, 0.f, 0.f};
         const E* arow = kb + (b * 16 + l16) * kKS + lq * 8;
 #pragma unroll
@@ -328,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
       // online softmax over the tile's 32 rows (the 4 lanes of head l16)
       float mx = sv[0][0];
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < kNB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[b][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -336,10 +325,10 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
       const float m_new = fmaxf(m_run, mx);
       const float base = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-      float pr[2][4];
+      float pr[kNB][4];
       float sum = 0.f;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < kNB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           pr[b][i] = __builtin_amdgcn_exp2f(sv[b][i] - base);
@@ -358,23 +347,27 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
 #pragma unroll
         for (int c = 0; c < kDV / 16; ++c) acc[c] = acc[c] * al;
       }
-      // O += P V, one 16x16x32 MFMA per 16 columns: k-slot 8lq + j stands
-      // for row 4lq + j of the tile's first half (j < 4) or row 12 + 4lq + j
-      // of its second, in A (P of head l16) and in B alike; B = V^T from two
-      // transposing reads (rows 16b + 4lq + l16/4, columns 16c + 4(l16 % 4))
-      V8 pa;
+      // O += P V, one 16x16x32 MFMA per 16 columns and 32 rows: k-slot
+      // 8lq + j stands for row 4lq + j of the step's first 16-row block
+      // (j < 4) or row 12 + 4lq + j of its second, in A (P of head l16) and
+      // in B alike; B = V^T from two transposing reads (rows 16b + 4lq +
+      // l16/4, columns 16c + 4(l16 % 4))
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pa[i] = (E)pr[0][i];
-        pa[4 + i] = (E)pr[1][i];
-      }
-      const E* vrow = kb + (lq * 4 + (l16 >> 2)) * kKS + (l16 & 3) * 4;
+      for (int ks = 0; ks < kNB / 2; ++ks) {   // 32 rows (two 16-row blocks) per MFMA
+        V8 pa;
 #pragma unroll
-      for (int c = 0; c < kDV / 16; ++c) {
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fwd_lds_i16x4*)(vrow + c * 16));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fwd_lds_i16x4*)(vrow + 16 * kKS + c * 16));
-        const fwd_i16x8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[c] = Elem<E>::mma32(pa, __builtin_bit_cast(V8, vb), acc[c]);
+        for (int i = 0; i < 4; ++i) {
+          pa[i] = (E)pr[2 * ks][i];
+          pa[4 + i] = (E)pr[2 * ks + 1][i];
+        }
+        const E* vrow = kb + (32 * ks + lq * 4 + (l16 >> 2)) * kKS + (l16 & 3) * 4;
+#pragma unroll
+        for (int c = 0; c < kDV / 16; ++c) {
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fwd_lds_i16x4*)(vrow + c * 16));
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fwd_lds_i16x4*)(vrow + 16 * kKS + c * 16));
+          const fwd_i16x8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[c] = Elem<E>::mma32(pa, __builtin_bit_cast(V8, vb), acc[c]);
+        }
       }
     }
   }
