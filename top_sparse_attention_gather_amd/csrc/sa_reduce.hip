@@ -184,22 +184,37 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
       }
     } else {
       const int eb = r.row_ptr[kcsr], ee = r.row_ptr[kcsr + 1];
-      // Flat slot id (row * topk + s) -> partial row (row - row0) * npos +
-      // nwin + s.  Here npos = nwin + topk, so that is slot + (row + 1) *
-      // nwin - row0 * npos: no division unless there are window positions
-      // (slot ids are int32, so a 32-bit one then).
-      const long long pos0 = -row0 * npos;
-      for (int e = eb + sg * kBatch; e < ee; e += nsg * kBatch) {
-        long long offs[kBatch];
-        bool ok[kBatch];
+      if (nwin == 0) {
+        // Flat slot id (row * topk + s) -> partial row (row - row0) * npos
+        // + s, and npos = topk here: slot - row0 * topk, no division.
+        const long long pos0 = -row0 * npos;
+        for (int e = eb + sg * kBatch; e < ee; e += nsg * kBatch) {
+          long long offs[kBatch];
+          bool ok[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          ok[u] = e + u < ee;
-          const int slot = r.entries[ok[u] ? e + u : eb];
-          const int prow = nwin ? (int)((unsigned)slot / (unsigned)p.topk) : 0;
-          offs[u] = ((long long)slot + (long long)(prow + 1) * nwin + pos0) * r.RW + col;
+          for (int u = 0; u < kBatch; ++u) {
+            ok[u] = e + u < ee;
+            offs[u] = ((long long)r.entries[ok[u] ? e + u : eb] + pos0) * r.RW + col;
+          }
+          add_batch(offs, ok);
         }
-        add_batch(offs, ok);
+      } else {
+        // cmp slots follow the nwin window positions of their row.  (A
+        // division-free form of this offset, slot + (row + 1) nwin - row0
+        // npos, measured slower here: 4.1 against 3.3 ms on the window+cmp
+        // varlen shape.)
+        for (int e = eb; e < ee; e += kBatch) {
+          long long offs[kBatch];
+          bool ok[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            ok[u] = e + u < ee;
+            const long long slot = r.entries[ok[u] ? e + u : eb];
+            const long long prow = slot / p.topk;
+            offs[u] = offset_of(prow, nwin + (int)(slot - prow * p.topk));
+          }
+          add_batch(offs, ok);
+        }
       }
     }
   }
