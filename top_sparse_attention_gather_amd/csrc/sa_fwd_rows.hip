@@ -188,12 +188,13 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
 // rows of one (token, kv head) are gathered once for all 64 heads (the
 // generic kernel above gathers them once per 16-head chunk).
 //
-// Wave w owns heads 16w..16w+15.  Per tile of 32 rows it forms S^T = K Q^T
-// (16x16x32 MFMA, K from LDS, Q resident in registers), so that each lane
-// holds one head's logits for 4 consecutive rows of each 16-row half: with
-// the two halves side by side that is an A operand of the 16x16x32 MFMA,
-// so P = exp(S - m) feeds O += P V straight from registers.  V is the first 512 columns of the same LDS rows, read
-// as B operands by transposing LDS reads.  The running max and sum of a
+// Wave w owns heads 16w..16w+15.  Per tile of kRows rows it forms S^T =
+// K Q^T (16x16x32 MFMA, K from LDS, Q resident in registers), so that each
+// lane holds one head's logits for 4 consecutive rows of each 16-row block:
+// with two blocks side by side that is an A operand of the 16x16x32 MFMA,
+// so P = exp(S - m) feeds O += P V straight from registers.  V is the first
+// 512 columns of the same LDS rows, read as B operands by transposing LDS
+// reads.  The running max and sum of a
 // head live in the 4 lanes of its column (log2 domain); a sink logit
 // starts them at (sink, 1).  Tiles come by direct global->LDS loads, the
 // next one issued while the current one is computed (two buffers: on the
@@ -229,7 +230,6 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
                                                            float* __restrict__ out_lse) {
   using namespace mla_fwd;
   typedef typename Elem<E>::V8 V8;
-  typedef typename Elem<E>::V4 V4;
   __shared__ __attribute__((aligned(16))) E sK[2][kRows * kKS];
   __shared__ int sRows[kCompact];
   __shared__ int sWave[4];
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
   auto src_of = [&](int code) -> const E* {
     return (code & kCmpFlag) ? Cg + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * kD : Kg + ((size_t)code * p.Hkv + g) * kD;
   };
-  // rows k0 .. k0 + 31 of the compacted list into `buf` by direct loads;
+  // rows k0 .. k0 + kRows - 1 of the compacted list into `buf` by direct loads;
   // rows past cnt repeat row cnt - 1 (finite values, masked out of S), the
   // padding chunk of each LDS row repeats its first chunk
   auto issue_tile = [&](int k0, int cnt, E* buf) {
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[b][i] = (k0 + b * 16 + lq * 4 + i < cnt) ? st[i] * sl2 : -INFINITY;
       }
-      // online softmax over the tile's 32 rows (the 4 lanes of head l16)
+      // online softmax over the tile's rows (the 4 lanes of head l16)
       float mx = sv[0][0];
 #pragma unroll
       for (int b = 0; b < kNB; ++b)
