@@ -225,6 +225,27 @@ __device__ __forceinline__ void fwd_load_lds16(const void* src, void* lds) {
 }
 typedef short fwd_i16x8 __attribute__((ext_vector_type(8)));
 
+// x and its value in lane ^ 16 (resp. lane ^ 32), as a pair, by swapping a
+// register with itself across 16-lane rows (resp. 32-lane halves): a VALU
+// exchange instead of an LDS-routed lane shuffle.  Every lane then combines
+// the same two operands (in either order).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename E>
 __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restrict__ out_o,
                                                            float* __restrict__ out_lse) {
@@ -320,8 +341,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
       for (int b = 0; b < kNB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[b][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       const float m_new = fmaxf(m_run, mx);
       const float base = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - base);
@@ -334,8 +354,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
           pr[b][i] = __builtin_amdgcn_exp2f(sv[b][i] - base);
           sum += pr[b][i];
         }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
+      sum = add_xor32(add_xor16(sum));
       l_run = l_run * alpha + sum;
       m_run = m_new;
       // O rows are heads 4lq + i: their rescale factors from lanes 4lq + i
