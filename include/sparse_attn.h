@@ -252,8 +252,8 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* ar
 
 /* Selected-attention forward (aclnnNsaSelectedAttentionInfer, "Formula";
  * the forward whose o and lse the backward consumes): enqueues on
- * `stream`, writes o (bf16) and lse (fp32; -inf for a row with no visible
- * key and no sink).  No workspace. */
+ * `stream`, writes o (in the inputs' 16-bit type, desc->dtype) and lse
+ * (fp32; -inf for a row with no visible key and no sink).  No workspace. */
 sa_status_t sparse_attn_fwd(const sa_desc_t* desc, const sa_fwd_args_t* args, void* stream);
 
 /* Number of CSR keys for `desc`: token mode n_kv_rows * n_kv_heads, block
