@@ -151,3 +151,26 @@ def test_indexer_phase1_validation_codes():
     e = B.make_indexer_desc(W.small_workload("tiny_token_gqa", seqlens=(0,)), n_heads=4, d=128, topk=16)
     a = B.SaIndexerArgs()
     assert lib.sparse_attn_indexer_grad_kl(ctypes.byref(e), ctypes.byref(a), None, 0, None) == 0
+
+
+def test_deterministic_workspace_holds_one_chunk_of_partial_rows():
+    """Deterministic MLA: the workspace holds the bf16 partial rows of one
+    token chunk (one 1152-byte row per (head group, token, position)) plus
+    the fp32 dKV accumulator; tokens are chunked so that the partial rows
+    stay under 24 GiB (the 32K-token, 128-head shape needs 154 GB of them in
+    all).  Atomic mode needs only the accumulators."""
+    cap = 24 << 30
+    for name, groups in (("mla_token_8k", 1), ("mla_token_32k_local", 2)):
+        wl = W.WORKLOADS[name]
+        T = wl.total_q
+        per_token = groups * wl.n_kv_heads * wl.topk * wl.d_qk * 2
+        tc = min(T, max(1, cap // per_token))
+        acc = T * wl.n_kv_heads * wl.d_qk * 4
+        st, n = _ws(B.make_desc(wl, B.DKV_DETERMINISTIC))
+        assert st == 0
+        assert tc * per_token + acc <= n <= tc * per_token + acc + (2 << 30), (name, n)
+        if name == "mla_token_32k_local":
+            assert tc < T and tc * per_token <= cap      # chunked
+        st, na = _ws(B.make_desc(wl, B.DKV_ATOMIC))
+        assert st == 0
+        assert acc <= na < acc + (256 << 20), (name, na)
