@@ -3,10 +3,11 @@
 // The row kernels write one partial row per (head chunk, token, kv head,
 // selected position) into a token-major buffer; this kernel sums, for
 // every output row, the partials that name it in a fixed order -- by the
-// CSR transpose of the index lists (ascending slot id), or for window
-// keys by ascending query token -- and adds the sum into an fp32
-// accumulator.  The order never depends on scheduling, so results are
-// bitwise repeatable.  (aclnnSparseFlashAttentionGrad, "Formula": dK[u] and
+// CSR transpose of the index lists (ascending slot id; for rows narrower
+// than a wave, interleaved batches of the list per sub-group, the sub-group
+// sums then in sub-group order), or for window keys by ascending query
+// token -- and adds the sum into an fp32 accumulator.  The order never
+// depends on scheduling, so results are bitwise repeatable.  (aclnnSparseFlashAttentionGrad, "Formula": dK[u] and
 // dV[u] collect the contributions of every query that gathered row u.)
 #include "sa_launch.h"
 
