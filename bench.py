@@ -36,7 +36,8 @@ METRIC = "sparse-attn bwd TFLOP/s (selected-KV FLOPs) and % of bf16 MFMA peak, 1
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per launch of the dominant kernel on the MLA 8K workload, from
+# HBM bytes per launch of the dominant kernel on the MLA 8K workload (the
+# backward's main kernel in deterministic mode; "fwd": the forward), from
 # rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by the same counters on a
 # plain 1 GiB copy (`--copy-calibration`); valid only for the kernel source
 # they were taken on (its SHA-256), else reported as null.
@@ -45,6 +46,11 @@ MEASURED_TRAFFIC = {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
         "sha256": "bd5fe81f12724817e0ff7ba51034c3534d3a9cf92527330caa06f3e7d4d3dd34",
         "fetch_bytes": 8163138173, "write_bytes": 17521873056,
+    },
+    ("mla_token_8k", "fwd"): {
+        "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_fwd_rows.hip",
+        "sha256": "700634eaa3f72e5cb3688b1fb892ff7124fd67af5abae81062eb97f8f196528a",
+        "fetch_bytes": 5255923790, "write_bytes": 538968064,
     },
 }
 
@@ -343,7 +349,9 @@ def bench_forward(args):
         "timing": {"call_ms": percentiles(call_ms), "step_time_from": "bracketed region / steps",
                    "device": device_info()},
         "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(kern_tflops, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(wl.name, "fwd") if kernel == "fwd_mla_kernel" else None,
+                     "traffic_unit": "bytes per launch (HBM fetch + write, copy-calibrated rocprofv3 counters)",
                      "kernel_ms": round(kern_ms, 4)},
         "cpu_baseline": cpu,
     }
