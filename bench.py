@@ -37,7 +37,8 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per launch of the dominant kernel on the MLA 8K workload (the
-# backward's main kernel in deterministic mode; "fwd": the forward), from
+# backward's main kernel in deterministic mode; "fwd": the forward) and on
+# the 8K indexer workload ("idx": the per-token indexer kernel), from
 # rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by the same counters on a
 # plain 1 GiB copy (`--copy-calibration`); valid only for the kernel source
 # they were taken on (its SHA-256), else reported as null.
@@ -46,6 +47,11 @@ MEASURED_TRAFFIC = {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
         "sha256": "bd5fe81f12724817e0ff7ba51034c3534d3a9cf92527330caa06f3e7d4d3dd34",
         "fetch_bytes": 8163138173, "write_bytes": 17521873056,
+    },
+    ("indexer_8k", "idx"): {
+        "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_indexer.hip",
+        "sha256": "355a1e89c78e00580e8e919c47d6f142165ee5e76d448c9617cab9a8e0c05303",
+        "fetch_bytes": 660554130, "write_bytes": 3894948864,
     },
     ("mla_token_8k", "fwd"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_fwd_rows.hip",
@@ -267,7 +273,9 @@ def bench_indexer(args):
                    "device": device_info()},
         "roofline": {"kernel": "idx_grad_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
-                     "mfma_tflops": round(ktf, 2), "traffic": None, "kernel_ms": round(kern_ms, 4)},
+                     "mfma_tflops": round(ktf, 2), "traffic": measured_traffic(wl.name, "idx"),
+                     "traffic_unit": "bytes per launch (HBM fetch + write, copy-calibrated rocprofv3 counters)",
+                     "kernel_ms": round(kern_ms, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
