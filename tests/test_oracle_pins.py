@@ -327,6 +327,26 @@ def test_empty_row_has_no_gradient():
     assert all(np.isfinite(v).all() for v in g.values())
 
 
+def test_empty_row_with_a_sink_is_the_sink_alone():
+    """A row with no valid key but a sink: the softmax runs over the sink
+    logit alone, so lse = sink exactly, O = 0, and the row has no dQ."""
+    wl = tiny("token_sinks")
+    inp = W.make_inputs(wl)
+    idx = inp["idx"].numpy().copy()
+    idx[3] = -1
+    inp["idx"] = torch.from_numpy(idx)
+    pb = O.Problem(inp)
+    out, lse = O.sparse_fwd(pb)
+    sinks = inp["sinks"].to(torch.float64).numpy()
+    heads = slice(0, wl.n_q_heads)
+    np.testing.assert_array_equal(lse[3][heads], sinks)
+    assert np.all(out[3] == 0)
+    Ob, Lb = O.round_fwd_outputs(out, lse)
+    g = O.sparse_bwd(pb, Ob, Lb)
+    assert np.all(g["dq"][3] == 0)
+    assert all(np.isfinite(v).all() for v in g.values())
+
+
 @pytest.mark.parametrize("mode", ["token_gqa", "block_gqa", "wcmp_sinks"])
 def test_per_row_topk_lengths(mode):
     """Per-row top-k lengths: slots at or past a row's length are unused.
