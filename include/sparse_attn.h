@@ -220,12 +220,17 @@ typedef struct sa_fwd_args {
   const int32_t* seqused_cmp;
 } sa_fwd_args_t;
 
-/* Phase 1 of the backward: validates `desc` (host only, no HIP call) and
- * returns in *bytes the device workspace that sparse_attn_bwd needs for
- * it (fp32 accumulators, the softmax-grad term D, CSR buffers, and with
- * softmax_l1 the per-head-group sums behind the L1-norm outputs).
- * Errors: SA_ERR_NULL_PTR, SA_ERR_BAD_SHAPE, SA_ERR_BAD_ARG,
- * SA_ERR_UNSUPPORTED (e.g. a head dim the kernels are not built for). */
+/* Phase 1 of the backward (aclnnSparseFlashAttentionGrad, "Function
+ * prototype": the operator is called in two phases, the first of which
+ * checks the parameters and computes the workspace size the second needs):
+ * validates `desc` (host only, no HIP call) and returns in *bytes the
+ * device workspace that sparse_attn_bwd needs for it (fp32 accumulators,
+ * the softmax-grad term D, CSR buffers, and with softmax_l1 the
+ * per-head-group sums behind the L1-norm outputs).
+ * Errors: SA_ERR_NULL_PTR, SA_ERR_BAD_SHAPE (also when a key count times
+ * the kv heads, or the slots of one token, would not fit int32),
+ * SA_ERR_BAD_ARG, SA_ERR_UNSUPPORTED (e.g. a head dim the kernels are not
+ * built for). */
 sa_status_t sparse_attn_bwd_workspace_size(const sa_desc_t* desc, size_t* bytes);
 
 /* Phase 2 of the backward (aclnnSparseFlashAttentionGrad, "Formula";
@@ -260,7 +265,8 @@ sa_status_t sparse_attn_fwd(const sa_desc_t* desc, const sa_fwd_args_t* args, vo
  * mode (sum over sequences of ceil(len_kv / block_size)) * n_kv_heads,
  * window+cmp total_cmp * n_kv_heads; and the workspace the CSR build needs.
  * Requires the sequence lengths (BSND: from desc; TND: host copies of
- * cu_seqlens_kv, may be NULL for BSND). */
+ * cu_seqlens_kv, may be NULL for BSND).  SA_ERR_BAD_SHAPE when the key
+ * count or T * n_kv_heads * topk exceeds 2^31 - 1. */
 sa_status_t sparse_attn_csr_size(const sa_desc_t* desc, const int32_t* host_cu_seqlens_kv,
                                  int64_t* n_keys, size_t* workspace_bytes);
 
@@ -269,7 +275,9 @@ sa_status_t sparse_attn_csr_size(const sa_desc_t* desc, const int32_t* host_cu_s
  * p = (t * n_kv_heads + g) * topk + slot of the used slots naming it, in
  * increasing p.  row_ptr [n_keys + 1] gets the exclusive prefix sum of the
  * per-key counts (row_ptr[n_keys] = number of used slots); entries needs
- * room for T * n_kv_heads * topk ids.  Bit-exact and deterministic. */
+ * room for T * n_kv_heads * topk ids.  Bit-exact and deterministic.
+ * SA_ERR_BAD_SHAPE when T * n_kv_heads * topk exceeds 2^31 - 1 (the ids
+ * are int32; the backward itself transposes token chunks that fit). */
 sa_status_t sparse_attn_csr_transpose(const sa_desc_t* desc, const int32_t* topk_indices,
                                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
                                       int32_t* row_ptr, int32_t* entries, void* workspace,
@@ -340,7 +348,9 @@ sa_status_t sparse_attn_indexer_grad_kl_timed(const sa_indexer_desc_t* desc, con
                                               void* workspace, size_t workspace_bytes, void* stream,
                                               void* ev_main_start, void* ev_main_stop);
 
-/* Static string for a status code. */
+/* Static string for a status code (every call returns one, as the pages'
+ * operator API returns a status code: aclnnSparseFlashAttentionGrad,
+ * "Returns").  Unknown codes give "unknown sa_status_t"; never NULL. */
 const char* sparse_attn_status_string(sa_status_t status);
 
 /* Library version as major * 10000 + minor * 100 + patch. */

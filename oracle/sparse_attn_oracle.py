@@ -89,7 +89,31 @@ SEL_WINDOW_CMP = 2
 
 
 def _f64(t: torch.Tensor) -> np.ndarray:
-    return t.to(torch.float64).numpy()
+    """fp64 copy of a CPU tensor (exact for bf16, fp16 and fp32 values).
+
+    The 16-bit formats are widened in numpy from their bit patterns (a bf16
+    value is the top half of the fp32 with the same bits), which keeps
+    torch's intra-op thread pool out of the per-token loops: next to the
+    BLAS threads it made these small copies ~100x slower."""
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return _widen16(t.view(torch.int16).numpy(), t.dtype)
+    return t.numpy().astype(np.float64)
+
+
+def _widen16(bits: np.ndarray, dtype: torch.dtype) -> np.ndarray:
+    """fp64 values of 16-bit bf16 / fp16 bit patterns (an int16 array)."""
+    u = bits.view(np.uint16)
+    if dtype == torch.float16:
+        return u.view(np.float16).astype(np.float64)
+    return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _take_f64(t: torch.Tensor, rows: np.ndarray, g) -> np.ndarray:
+    """fp64 copy of t[rows, g] (rows: a numpy index array; g: an index or a
+    slice)."""
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return _widen16(t.view(torch.int16).numpy()[rows, g], t.dtype)
+    return t.numpy()[rows, g].astype(np.float64)
 
 
 class Problem:
@@ -229,15 +253,15 @@ class Problem:
         K = np.zeros((n, self.d_qk))
         m0 = srcs == 0
         if m0.any():
-            K[m0] = _f64(self.k[torch.from_numpy(rows[m0]), g])
+            K[m0] = _take_f64(self.k, rows[m0], g)
         if (~m0).any():
-            K[~m0] = _f64(self.cmp_kv[torch.from_numpy(rows[~m0]), g])
+            K[~m0] = _take_f64(self.cmp_kv, rows[~m0], g)
         if self.kv_shared:
             V = K[:, :self.d_v]
         else:
             V = np.zeros((n, self.d_v))
             if n:
-                V[:] = _f64(self.v[torch.from_numpy(rows), g])
+                V[:] = _take_f64(self.v, rows, g)
         return K, V
 
 
@@ -311,8 +335,8 @@ def sparse_bwd(pb: Problem, O: torch.Tensor, lse: torch.Tensor,
     for t in toks:
         q_t = _f64(pb.q[t])
         do_t = _f64(pb.d_o[t])
-        o_t = O[t].to(torch.float64).numpy() if isinstance(O, torch.Tensor) else np.asarray(O[t], np.float64)
-        l_t = lse[t].to(torch.float64).numpy() if isinstance(lse, torch.Tensor) else np.asarray(lse[t], np.float64)
+        o_t = _f64(O[t]) if isinstance(O, torch.Tensor) else np.asarray(O[t], np.float64)
+        l_t = _f64(lse[t]) if isinstance(lse, torch.Tensor) else np.asarray(lse[t], np.float64)
         for g in range(pb.Hkv):
             hs = slice(g * pb.G, (g + 1) * pb.G)
             Qg, dOg, Og, Lg = q_t[hs], do_t[hs], o_t[hs], l_t[hs]
@@ -389,7 +413,7 @@ def softmax_l1_norm(pb: Problem, lse: torch.Tensor,
     cmp = np.zeros((pb.T, pb.Hkv, pb.K)) if pb.select == SEL_WINDOW_CMP else None
     for t in toks:
         q_t = _f64(pb.q[t])
-        l_t = lse[t].to(torch.float64).numpy() if isinstance(lse, torch.Tensor) else np.asarray(lse[t], np.float64)
+        l_t = _f64(lse[t]) if isinstance(lse, torch.Tensor) else np.asarray(lse[t], np.float64)
         for g in range(pb.Hkv):
             hs = slice(g * pb.G, (g + 1) * pb.G)
             srcs, rows, pos = pb.selection_positions(t, g)
@@ -465,7 +489,7 @@ def indexer_grad_kl(inputs: Dict[str, object], tokens: Optional[Sequence[int]] =
         if rows.size == 0:
             continue
         qt = _f64(q[t])                                   # [H, d]
-        K = _f64(k[torch.from_numpy(rows)])               # [n, d]
+        K = _take_f64(k, rows, slice(None))               # [n, d]
         S = qt @ K.T                                      # [H, n]
         R = np.maximum(S, 0.0)
         I = W[t] @ R                                      # [n]
@@ -552,16 +576,3 @@ def csr_transpose(pb: Problem) -> Tuple[np.ndarray, np.ndarray]:
     row_ptr[1:] = np.cumsum(counts)
     order = np.argsort(keys[valid], kind="stable")        # ties keep p order
     return row_ptr, valid[order]
-
-
-# ----------------------------------------------------------------------------
-# work counting (selected-KV FLOPs)
-# ----------------------------------------------------------------------------
-
-def count_valid_pairs(pb: Problem) -> int:
-    """Number of valid (token, kv head, key row) pairs."""
-    n = 0
-    for t in range(pb.T):
-        for g in range(pb.Hkv):
-            n += pb.selection(t, g)[1].size
-    return n

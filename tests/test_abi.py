@@ -174,3 +174,29 @@ def test_deterministic_workspace_holds_one_chunk_of_partial_rows():
         st, na = _ws(B.make_desc(wl, B.DKV_ATOMIC))
         assert st == 0
         assert acc <= na < acc + (256 << 20), (name, na)
+
+
+def test_int32_slot_and_key_counts_are_checked():
+    """Slot ids and CSR keys are int32 on the device.  A key space (kv rows
+    times kv heads, plus the sentinel) past 2^31 - 1 is rejected; a
+    backward whose slots pass 2^31 in all still gets a workspace (tokens are
+    chunked so every chunk's slot ids fit); the standalone CSR transpose,
+    which writes the slot ids of every token, rejects it."""
+    wl = W.WORKLOADS["mla_token_8k"]
+    lib = B.load()
+    # 2^29 kv rows x 4 kv heads = 2^31 keys
+    big_keys = B.make_desc(wl, n_q_heads=4, n_kv_heads=4, seqlen_kv=1 << 29, seqlen_q=1 << 10)
+    assert _ws(big_keys)[0] == 2
+    # 2^20 tokens x 2048 slots = 2^31 slots: chunked backward is fine
+    many_slots = B.make_desc(wl, seqlen_q=1 << 20, seqlen_kv=1 << 20)
+    for mode in (B.DKV_ATOMIC, B.DKV_DETERMINISTIC):
+        st, n = _ws(B.make_desc(wl, mode, seqlen_q=1 << 20, seqlen_kv=1 << 20))
+        assert st == 0 and n > 0
+    nk, nws = ctypes.c_int64(0), ctypes.c_size_t(0)
+    assert lib.sparse_attn_csr_size(ctypes.byref(many_slots), None, ctypes.byref(nk), ctypes.byref(nws)) == 2
+    ok = B.make_desc(wl)
+    assert lib.sparse_attn_csr_size(ctypes.byref(ok), None, ctypes.byref(nk), ctypes.byref(nws)) == 0
+    assert nk.value == 8192
+    # the slots of one (token, kv head set) must fit one chunk
+    assert _ws(B.make_desc(wl, n_q_heads=1024, n_kv_heads=1024, topk=1 << 21, seqlen_kv=1 << 10,
+                           seqlen_q=1 << 10, d_qk=128, d_v=128, kv_shared=0))[0] == 2

@@ -30,6 +30,12 @@ long long rows_kv(const sa_desc_t* d) {
 
 long long rows_cmp(const sa_desc_t* d) { return d->select == SA_SEL_WINDOW_CMP ? (long long)d->total_cmp : 0; }
 
+long long csr_keys_bound(const sa_desc_t* d);
+
+// Largest int32 count: slot ids, CSR keys and their sentinel are int32 on
+// the device.
+constexpr long long kMaxI32 = (1LL << 31) - 1;
+
 // Phase-1 checks shared by every entry point.
 sa_status_t validate(const sa_desc_t* d) {
   if (!d) return SA_ERR_NULL_PTR;
@@ -69,8 +75,16 @@ sa_status_t validate(const sa_desc_t* d) {
                          : d->select == SA_SEL_TOKEN ? d->topk
                                                      : (long long)d->win_left + 1 + d->win_right + d->topk;
   if (npos >= (1LL << 30)) return SA_ERR_BAD_SHAPE;
+  // CSR keys (kv row, block or cmp row, times the kv heads) and the
+  // sentinel key past them must fit int32; the slots of one token fit one
+  // token chunk (chunks keep fewer than 2^31 slots)
+  if (csr_keys_bound(d) >= kMaxI32) return SA_ERR_BAD_SHAPE;
+  if ((long long)d->n_kv_heads * d->topk > kMaxI32) return SA_ERR_BAD_SHAPE;
   return SA_OK;
 }
+
+// Tokens per chunk whose slot ids (chunk-local, int32) all fit.
+long long max_chunk_tokens(long long Hkv, long long topk) { return topk > 0 ? kMaxI32 / (Hkv * topk) : kMaxI32; }
 
 // Partial-row buffer cap of the deterministic path; larger problems are
 // processed in token chunks whose partials fit under it.
@@ -141,9 +155,11 @@ BwdLayout bwd_layout(const sa_desc_t* d, const Params& p) {
   const size_t elem = L.fast ? 2 : 4;   // bf16 partials from the MLA kernel, fp32 otherwise
   // block selection with separate K/V: dK/dV from the key-major block
   // kernel, no partial rows, one pass over all tokens
-  L.blk_km = (!L.fast && sa::blk_dkv_supported(p)) ? 1 : 0;
+  // (one pass over every token: its slot ids must fit int32)
+  L.blk_km = (!L.fast && sa::blk_dkv_supported(p) && (long long)T * (long long)Hkv * d->topk <= kMaxI32) ? 1 : 0;
   const size_t per_token = L.blk_km ? 0 : (size_t)L.n_hc * Hkv * npos * L.RW * elem;
   size_t Tc = per_token ? std::max<size_t>(1, kPartialCap / per_token) : T;
+  Tc = std::min<size_t>(Tc, (size_t)max_chunk_tokens((long long)Hkv, d->topk));
   L.Tc = (int)std::min<size_t>(std::max<size_t>(T, 1), Tc);
   const long long nk = csr_keys_bound(d);
   if (L.blk_km) {
@@ -274,6 +290,7 @@ sa_status_t validate_idx(const sa_indexer_desc_t* d) {
   const long long T = idx_total_q(d);
   if (T > 0 && idx_rows_kv(d) < 1) return SA_ERR_BAD_SHAPE;
   if (idx_rows_kv(d) >= (1LL << 30) || T >= (1LL << 31)) return SA_ERR_BAD_SHAPE;
+  if (d->topk > (1 << 30)) return SA_ERR_BAD_SHAPE;
   if (!sa::idx_grad_supported(make_idx_params(d))) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
@@ -290,6 +307,7 @@ IdxLayout idx_layout(const sa_indexer_desc_t* d) {
   const long long nk = idx_rows_kv(d);
   const size_t per_token = K * D * sizeof(uint16_t);   // bf16 partial rows
   L.Tc = (int)std::min<size_t>(std::max<size_t>(T, 1), std::max<size_t>(1, kPartialCap / per_token));
+  L.Tc = (int)std::min<long long>(L.Tc, max_chunk_tokens(1, (long long)K));
   size_t off = 0;
   L.loss_tok = off;
   off += align_up(T * sizeof(float));
@@ -656,9 +674,10 @@ sa_status_t sparse_attn_csr_size(const sa_desc_t* desc, const int32_t* host_cu_s
   } else {
     nk = csr_keys_bound(desc);
   }
-  if (nk >= (1LL << 31) - 1) return SA_ERR_BAD_SHAPE;
+  if (nk >= kMaxI32) return SA_ERR_BAD_SHAPE;
   *n_keys = nk;
   const long long n_slots = total_q(desc) * desc->n_kv_heads * desc->topk;
+  if (n_slots > kMaxI32) return SA_ERR_BAD_SHAPE;   // entries are int32 slot ids
   *workspace_bytes = align_up((size_t)(desc->batch + 1) * 4) + sa::csr_workspace_bytes(n_slots, nk, desc->batch);
   return SA_OK;
 }
@@ -678,6 +697,7 @@ sa_status_t sparse_attn_csr_transpose(const sa_desc_t* desc, const int32_t* topk
   // TND block mode uses the bound, whose extra keys stay empty
   const long long nk = csr_keys_bound(desc);
   const long long n_slots = total_q(desc) * desc->n_kv_heads * desc->topk;
+  if (n_slots > kMaxI32) return SA_ERR_BAD_SHAPE;   // entries are int32 slot ids
   const size_t need = align_up((size_t)(desc->batch + 1) * 4) + sa::csr_workspace_bytes(n_slots, nk, desc->batch);
   if (workspace_bytes < need) return SA_ERR_WORKSPACE_TOO_SMALL;
   if (total_q(desc) == 0) return SA_OK;

@@ -1,5 +1,7 @@
 // CSR transpose of the top-k index lists on the GPU: for every key, the
-// flat slot ids p = (t * Hkv + g) * K + slot that name it, ascending.
+// flat slot ids p = (t * Hkv + g) * K + slot that name it, ascending,
+// counted from the first slot of the token range transposed (for a range
+// starting at token 0, the global ids).
 //
 // A slot's key follows the selection rules of the backward (token: the kv
 // row; block: the sequence's block; window+cmp: the cmp row) and unused or
@@ -395,17 +397,19 @@ hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_key
     hipLaunchKernelGGL(radix_hist_kernel, dim3(nb), dim3(kThreads), 0, s, hkeys, first ? 1 : 2, n, pass * 8, nb,
                        c.hist);
     if ((e = scan_excl(c.hist, 256LL * nb, c.hist, 256LL * nb + 1, c.bsum, s)) != hipSuccess) return e;
+    // entries are chunk-local slot ids (slot - slot0), so they fit int32
+    // whenever the chunk's slot count does
     if (first && last)
-      hipLaunchKernelGGL((radix_scatter_kernel<true, true>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, slot0, n,
+      hipLaunchKernelGGL((radix_scatter_kernel<true, true>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, 0LL, n,
                          pass * 8, nb, c.hist, pout, entries);
     else if (first)
-      hipLaunchKernelGGL((radix_scatter_kernel<true, false>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, slot0, n,
+      hipLaunchKernelGGL((radix_scatter_kernel<true, false>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, 0LL, n,
                          pass * 8, nb, c.hist, pout, entries);
     else if (last)
-      hipLaunchKernelGGL((radix_scatter_kernel<false, true>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, slot0, n,
+      hipLaunchKernelGGL((radix_scatter_kernel<false, true>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, 0LL, n,
                          pass * 8, nb, c.hist, pout, entries);
     else
-      hipLaunchKernelGGL((radix_scatter_kernel<false, false>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, slot0, n,
+      hipLaunchKernelGGL((radix_scatter_kernel<false, false>), dim3(nb), dim3(kThreads), 0, s, c.keys, pin, 0LL, n,
                          pass * 8, nb, c.hist, pout, entries);
     pin = pout;
   }

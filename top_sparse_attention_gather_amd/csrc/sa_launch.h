@@ -64,7 +64,8 @@ hipError_t launch_fwd_rows(const Params& p, void* o, float* lse, hipStream_t s);
 bool fwd_rows_supported(int dqk, int dv, int shared);
 
 // CSR transpose of the index lists of tokens [t0, t1): row_ptr[n_keys + 1]
-// and entries (flat slot ids, ascending per key).
+// and entries (flat slot ids minus t0 * Hkv * topk, ascending per key; the
+// range must hold fewer than 2^31 slots).
 size_t csr_workspace_bytes(long long n_slots, long long n_keys, int batch);
 hipError_t launch_block_base(const Params& p, int* blk_base, hipStream_t s);
 hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_keys, const int* blk_base,

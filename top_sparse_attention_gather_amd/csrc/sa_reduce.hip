@@ -97,9 +97,8 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
         if (ok[u]) Vec8<PT>::add(v[u], acc);
     }
   };
-  auto offset_of = [&](long long prow, int pos) -> long long {
-    return ((prow - row0) * npos + pos) * r.RW + col;
-  };
+  // partial row of position `pos` of chunk-local (token, kv head) row lrow
+  auto offset_of = [&](long long lrow, int pos) -> long long { return (lrow * npos + pos) * r.RW + col; };
 
   const bool is_cmp = orow >= r.n_kv_out;   // cmp rows follow the kv rows
   if (!is_cmp && p.select == kSelWindowCmp) {
@@ -137,7 +136,7 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
       for (int u = 0; u < kBatch; ++u) {
         ok[u] = tb + u <= tl_hi;
         const int tl = ok[u] ? tb + u : tl_lo;
-        off[u] = offset_of((long long)(L.q_base + tl) * p.Hkv + g, jl - (tl + L.off - p.win_left));
+        off[u] = offset_of((long long)(L.q_base + tl) * p.Hkv + g - row0, jl - (tl + L.off - p.win_left));
       }
       add_batch(off, ok);
     }
@@ -172,30 +171,30 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           ok[u] = e + u < ee;
+          // chunk-local slot id -> chunk-local row and slot
           const int slot = r.entries[ok[u] ? e + u : eb];
-          const int prow = (int)((unsigned)slot / (unsigned)p.topk);   // slot ids are int32
-          const int s = slot - prow * p.topk;
+          const int lrow = (int)((unsigned)slot / (unsigned)p.topk);
+          const int s = slot - lrow * p.topk;
           if (ok[u] && p.causal) {
-            const SeqPos sp = seq_pos(p, (int)(prow / p.Hkv));
+            const SeqPos sp = seq_pos(p, (int)((row0 + lrow) / p.Hkv));
             ok[u] = jl <= sp.tl;     // row masked inside the selected block
           }
-          offs[u] = offset_of(prow, s * p.bs + off);
+          offs[u] = offset_of(lrow, s * p.bs + off);
         }
         add_batch(offs, ok);
       }
     } else {
       const int eb = r.row_ptr[kcsr], ee = r.row_ptr[kcsr + 1];
       if (nwin == 0) {
-        // Flat slot id (row * topk + s) -> partial row (row - row0) * npos
-        // + s, and npos = topk here: slot - row0 * topk, no division.
-        const long long pos0 = -row0 * npos;
+        // Chunk-local slot id (lrow * topk + s) -> partial row lrow * npos
+        // + s, and npos = topk here: the slot id itself, no division.
         for (int e = eb + sg * kBatch; e < ee; e += nsg * kBatch) {
           long long offs[kBatch];
           bool ok[kBatch];
 #pragma unroll
           for (int u = 0; u < kBatch; ++u) {
             ok[u] = e + u < ee;
-            offs[u] = ((long long)r.entries[ok[u] ? e + u : eb] + pos0) * r.RW + col;
+            offs[u] = (long long)r.entries[ok[u] ? e + u : eb] * r.RW + col;
           }
           add_batch(offs, ok);
         }
@@ -211,8 +210,8 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
           for (int u = 0; u < kBatch; ++u) {
             ok[u] = e + u < ee;
             const long long slot = r.entries[ok[u] ? e + u : eb];
-            const long long prow = slot / p.topk;
-            offs[u] = offset_of(prow, nwin + (int)(slot - prow * p.topk));
+            const long long lrow = slot / p.topk;
+            offs[u] = offset_of(lrow, nwin + (int)(slot - lrow * p.topk));
           }
           add_batch(offs, ok);
         }

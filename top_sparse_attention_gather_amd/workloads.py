@@ -72,6 +72,7 @@ class Workload:
     kv_seqlens: tuple = ()           # per-sequence kv lengths when they differ from the query's
     dtype: str = "bf16"              # format of the 16-bit tensors: "bf16" or "fp16"
     mask_causal: int = 1             # 1: key <= query position (top-left); 2: aligned at the ends (bottom-right)
+    local_window: int = 4096         # "local_half": the window the first half of the indices comes from
 
     # -- derived sizes -------------------------------------------------
     @property
@@ -274,7 +275,7 @@ def make_indices(wl: Workload, rng: Optional[np.random.Generator] = None) -> np.
                 elif wl.index_policy == "uniform_causal":
                     rows = _rows_uniform(rng, t + 1, K)
                 elif wl.index_policy == "local_half":
-                    rows = _rows_local_half(rng, t, K, 4096)
+                    rows = _rows_local_half(rng, t, K, wl.local_window)
                 elif wl.index_policy == "own_block_plus_uniform":
                     own = t // wl.block_size
                     rows = np.sort(np.concatenate([_rows_uniform(rng, own, K - 1), [own]]))
