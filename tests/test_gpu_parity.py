@@ -227,22 +227,40 @@ def test_fwd_rows_longer_than_one_compaction_pass():
     np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
 
 
-def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINISTIC, l1=False):
-    """Full-size run where only the compared rows need the oracle: GPU
-    forward supplies O/lse for all tokens, the oracle's own O/lse replace
-    them for the last n_tail tokens (and a few early ones); compared are dq
-    of those tokens and dK/dKV rows >= T - n_tail, whose every contributing
-    token is in the replaced set."""
-    U.say(f"[full] {wl.name}: generating inputs")
-    inp = W.make_inputs(wl)
+_FULL_INPUTS = {}
+
+
+def _full_inputs(wl):
+    """Generated inputs of a full-size workload, kept for the other modes."""
+    if wl.name not in _FULL_INPUTS:
+        U.say(f"[full] {wl.name}: generating inputs")
+        _FULL_INPUTS.clear()
+        _FULL_INPUTS[wl.name] = W.make_inputs(wl)
+    return _FULL_INPUTS[wl.name]
+
+
+def _sampled_full_size_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINISTIC, l1=False):
+    """Full-size call in the benchmark's launch configuration, compared on
+    every output row.  dO is zero for every token outside a sampled set (the
+    last n_tail tokens and n_early others), so those tokens contribute
+    exactly nothing (dP = 0 and D = 0, hence dS = 0): the GPU's dq, every
+    dK/dV/dKV and cmp row and dSinks then equal the oracle's sums over the
+    sampled tokens alone.  O/lse of the sampled tokens come from the oracle's
+    forward; the other tokens' O/lse (from the GPU forward) feed only the
+    GPU call and multiply a zero dO.  The softmax L1-norm outputs do not
+    depend on dO and are compared on the sampled tokens."""
+    inp = dict(_full_inputs(wl))
     T = wl.total_q
+    rng = np.random.default_rng(seed)
+    early = np.sort(rng.choice(T - n_tail, size=n_early, replace=False))
+    toks = np.concatenate([early, np.arange(T - n_tail, T)])
+    keep = torch.zeros(T, dtype=torch.bool)
+    keep[torch.from_numpy(toks)] = True
+    inp["d_o"] = torch.where(keep[:, None, None], inp["d_o"], torch.zeros((), dtype=inp["d_o"].dtype))
     dev = B.device_tensors(inp)
     desc = B.make_desc(wl, dkv_mode, softmax_l1=int(l1))
     U.say(f"[full] {wl.name}: GPU forward")
     o, lse = B.sparse_attn_fwd(desc, dev)
-    rng = np.random.default_rng(seed)
-    early = np.sort(rng.choice(T - n_tail, size=n_early, replace=False))
-    toks = np.concatenate([early, np.arange(T - n_tail, T)])
     U.say(f"[full] {wl.name}: oracle forward on {toks.size} tokens")
     pb = O.Problem(inp)
     out_ref, lse_ref = O.sparse_fwd(pb, toks.tolist())
@@ -250,55 +268,54 @@ def _tail_splice_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DETERMINI
     o[torch.from_numpy(toks).cuda()] = Ob.cuda()
     lse[torch.from_numpy(toks).cuda()] = Lb.cuda()
     dev["o"], dev["lse"] = o, lse
-    U.say(f"[full] {wl.name}: GPU backward")
+    U.say(f"[full] {wl.name}: GPU backward (mode {dkv_mode})")
     out = B.sparse_attn_bwd(desc, dev)
     torch.cuda.synchronize()
     got = {k: v.float().cpu().numpy() for k, v in out.items()}
+    del o, lse, dev, out
     O_full = torch.zeros(T, wl.n_q_heads, wl.d_v, dtype=torch.bfloat16)
     L_full = torch.zeros(T, wl.n_q_heads, dtype=torch.float32)
     O_full[torch.from_numpy(toks)] = Ob
     L_full[torch.from_numpy(toks)] = Lb
     U.say(f"[full] {wl.name}: oracle backward on {toks.size} tokens")
     ref = O.sparse_bwd(pb, O_full, L_full, tokens=toks.tolist())
+    rows = {"dq": toks}
     if l1:
         U.say(f"[full] {wl.name}: oracle softmax L1-norm on {toks.size} tokens")
         ref.update({k + "_l1": v for k, v in O.softmax_l1_norm(pb, L_full, tokens=toks.tolist()).items()})
-    for k in got:
-        assert np.isfinite(got[k]).all(), k
-    key = "dkv" if wl.kv_shared else "dk"
-    rows = {"dq": toks, key: np.arange(T - n_tail, T)}
-    if not wl.kv_shared:
-        rows["dv"] = np.arange(T - n_tail, T)
-    if l1:
         rows["ori_softmax_l1"] = toks
         if wl.select == W.SEL_WINDOW_CMP:
             rows["cmp_softmax_l1"] = toks
-    if wl.select == W.SEL_WINDOW_CMP:
-        # cmp row c of the last sequence is visible only to tokens whose
-        # local position is >= cmp_ratio * c + cmp_ratio - 1
-        n_c = n_tail // wl.cmp_ratio
-        rows["d_cmp_kv"] = np.arange(wl.total_cmp - n_c, wl.total_cmp)
-    got = {k: v for k, v in got.items() if k in rows}
+    for k in got:
+        assert np.isfinite(got[k]).all(), k
+    # tokens outside the sample have exactly zero dq; every other output
+    # is compared on all of its rows
+    others = np.setdiff1d(np.arange(T), toks)
+    assert not got["dq"].reshape(T, -1)[others].any()
+    got["dq"] = got["dq"].reshape(ref["dq"].shape)
     return U.compare_all(got, ref, rows=rows, tag=wl.name)
 
 
 @pytest.mark.parametrize("mode", list(MODES))
 def test_bwd_parity_nsa_block_full_size_sampled(mode):
     """The NSA-style block-sparse GQA workload at its full size (B=2,
-    S=4096, 16:1 heads, d=128, 16 blocks of 64), sampled rows."""
-    _tail_splice_case(W.WORKLOADS["nsa_block_gqa"], dkv_mode=MODES[mode])
+    S=4096, 16:1 heads, d=128, 16 blocks of 64): sampled dq rows, every dK
+    and dV row."""
+    _sampled_full_size_case(W.WORKLOADS["nsa_block_gqa"], dkv_mode=MODES[mode])
 
 
 @pytest.mark.parametrize("mode", list(MODES))
 def test_bwd_parity_mla_cmp_sinks_varlen_full_size_sampled(mode):
     """Window + cmp with sinks, varlen {1024, 3000, 6000, 16000}, at full
-    size: sampled dq rows, the last dKV rows and the last cmp rows."""
-    _tail_splice_case(W.WORKLOADS["mla_cmp_sinks_varlen"], dkv_mode=MODES[mode])
+    size: sampled dq rows, every dKV and cmp row and the full dSinks (the
+    sum over all 26 024 tokens, of which only the sampled ones carry a
+    non-zero dO)."""
+    _sampled_full_size_case(W.WORKLOADS["mla_cmp_sinks_varlen"], dkv_mode=MODES[mode])
 
 
 @pytest.mark.parametrize("mode", list(MODES))
 def test_bwd_parity_mla_8k_full_size_sampled(mode):
-    _tail_splice_case(W.WORKLOADS["mla_token_8k"], dkv_mode=MODES[mode])
+    _sampled_full_size_case(W.WORKLOADS["mla_token_8k"], dkv_mode=MODES[mode])
 
 
 @pytest.mark.parametrize("name", ["mla_token_8k", "nsa_block_gqa", "mla_cmp_sinks_varlen"])
@@ -306,7 +323,7 @@ def test_softmax_l1_full_size_sampled(name):
     """Softmax L1-norm outputs at full size in the deterministic launch
     configuration (MLA kernel, block dQ kernel, window + cmp), sampled
     token rows, with the gradients of the same call."""
-    _tail_splice_case(W.WORKLOADS[name], dkv_mode=B.DKV_DETERMINISTIC, l1=True)
+    _sampled_full_size_case(W.WORKLOADS[name], dkv_mode=B.DKV_DETERMINISTIC, l1=True)
 
 
 MLA_LONG_ROWS = W.Workload(name="mla_long_rows", select=W.SEL_TOKEN, layout=W.LAYOUT_BSND, seqlens=(2200,),
@@ -319,7 +336,7 @@ def test_bwd_mla_rows_longer_than_the_mla_kernel_takes(mode):
     """Shared-KV 576/512 with 64 heads and 2100 positions per row: past the
     64-head MLA kernel's 2048, so the generic row kernel (two compaction
     passes) runs; the last tokens against the oracle."""
-    _tail_splice_case(MLA_LONG_ROWS, n_tail=8, n_early=2,
+    _sampled_full_size_case(MLA_LONG_ROWS, n_tail=8, n_early=2,
                       dkv_mode=B.DKV_DETERMINISTIC if mode == "det" else B.DKV_ATOMIC)
 
 
@@ -339,5 +356,6 @@ def test_fwd_mla_64_heads_rows_over_several_compaction_passes():
     np.testing.assert_allclose(lse[sel].cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
 
 
-def test_bwd_parity_mla_32k_full_size_sampled():
-    _tail_splice_case(W.WORKLOADS["mla_token_32k_local"], n_tail=32, n_early=4)
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_parity_mla_32k_full_size_sampled(mode):
+    _sampled_full_size_case(W.WORKLOADS["mla_token_32k_local"], n_tail=32, n_early=4, dkv_mode=MODES[mode])
