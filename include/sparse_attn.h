@@ -348,6 +348,20 @@ sa_status_t sparse_attn_indexer_grad_kl_timed(const sa_indexer_desc_t* desc, con
                                               void* workspace, size_t workspace_bytes, void* stream,
                                               void* ev_main_start, void* ev_main_stop);
 
+/* The backward without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, outputs and launch sequence as sparse_attn_bwd; the workspace
+ * is a fixed 128 MiB device array of the library, one per GPU it runs on,
+ * held from the library's load on that GPU until the process ends.
+ * Returns SA_ERR_WORKSPACE_TOO_SMALL when sparse_attn_bwd_workspace_size
+ * gives more than 128 MiB for `desc` (nothing is launched then).  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other host threads) race and give wrong results; calls
+ * ordered on one stream are safe.  Each call clears what must start at
+ * zero itself. */
+sa_status_t sparse_attn_bwd_noalloc(const sa_desc_t* desc, const sa_bwd_args_t* args, void* stream);
+
 /* Static string for a status code (every call returns one, as the pages'
  * operator API returns a status code: aclnnSparseFlashAttentionGrad,
  * "Returns").  Unknown codes give "unknown sa_status_t"; never NULL. */

@@ -28,7 +28,8 @@ DTYPE_FP16 = 1
 EXPORTED = ["sparse_attn_bwd_workspace_size", "sparse_attn_bwd", "sparse_attn_bwd_timed", "sparse_attn_fwd",
             "sparse_attn_csr_size",
             "sparse_attn_csr_transpose", "sparse_attn_indexer_grad_kl_workspace_size", "sparse_attn_indexer_grad_kl",
-            "sparse_attn_indexer_grad_kl_timed", "sparse_attn_status_string", "sparse_attn_version"]
+            "sparse_attn_indexer_grad_kl_timed", "sparse_attn_status_string", "sparse_attn_version",
+            "sparse_attn_bwd_noalloc"]
 
 
 class SaDesc(ctypes.Structure):
@@ -93,6 +94,7 @@ def load() -> ctypes.CDLL:
     lib.sparse_attn_bwd.argtypes = [pd, ctypes.POINTER(SaBwdArgs), _P, ctypes.c_size_t, _P]
     lib.sparse_attn_bwd_timed.argtypes = [pd, ctypes.POINTER(SaBwdArgs), _P, ctypes.c_size_t, _P, _P, _P]
     lib.sparse_attn_fwd.argtypes = [pd, ctypes.POINTER(SaFwdArgs), _P]
+    lib.sparse_attn_bwd_noalloc.argtypes = [pd, ctypes.POINTER(SaBwdArgs), _P]
     lib.sparse_attn_csr_size.argtypes = [pd, _P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)]
     lib.sparse_attn_csr_transpose.argtypes = [pd, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     pi = ctypes.POINTER(SaIndexerDesc)
@@ -103,7 +105,8 @@ def load() -> ctypes.CDLL:
     lib.sparse_attn_status_string.argtypes = [ctypes.c_int]
     lib.sparse_attn_status_string.restype = ctypes.c_char_p
     lib.sparse_attn_version.restype = ctypes.c_int32
-    for fn in ("sparse_attn_bwd_workspace_size", "sparse_attn_bwd", "sparse_attn_bwd_timed", "sparse_attn_fwd",
+    for fn in ("sparse_attn_bwd_workspace_size", "sparse_attn_bwd", "sparse_attn_bwd_timed", "sparse_attn_bwd_noalloc",
+               "sparse_attn_fwd",
                "sparse_attn_csr_size", "sparse_attn_csr_transpose", "sparse_attn_indexer_grad_kl_workspace_size",
                "sparse_attn_indexer_grad_kl", "sparse_attn_indexer_grad_kl_timed"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -215,6 +218,24 @@ def sparse_attn_bwd(desc: SaDesc, tensors: Dict[str, torch.Tensor], outputs: Opt
         _check("sparse_attn_bwd_timed",
                lib.sparse_attn_bwd_timed(ctypes.byref(desc), ctypes.byref(a), _ptr(workspace), workspace.numel(),
                                          _stream(stream), events[0], events[1]))
+    return outputs
+
+
+def sparse_attn_bwd_noalloc(desc: SaDesc, tensors: Dict[str, torch.Tensor],
+                            outputs: Optional[Dict[str, torch.Tensor]] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """The backward on the library's fixed per-GPU workspace (no workspace
+    argument, no allocation inside the call).  Outputs are allocated here
+    when not given; pass them in to allocate nothing at all."""
+    lib = load()
+    if outputs is None:
+        outputs = alloc_bwd_outputs(desc, tensors)
+    a = SaBwdArgs()
+    for name in ("q", "k", "v", "kv", "cmp_kv", "o", "d_o", "lse", "sinks", "topk_indices", "cu_seqlens_q",
+                 "cu_seqlens_kv", "cu_seqlens_cmp", "topk_lengths", "seqused_q", "seqused_kv", "seqused_cmp"):
+        setattr(a, name, _ptr(tensors.get(name)))
+    for name in ("dq", "dk", "dv", "dkv", "d_cmp_kv", "dsinks", "ori_softmax_l1", "cmp_softmax_l1"):
+        setattr(a, name, _ptr(outputs.get(name)))
+    _check("sparse_attn_bwd_noalloc", lib.sparse_attn_bwd_noalloc(ctypes.byref(desc), ctypes.byref(a), _stream(stream)))
     return outputs
 
 
