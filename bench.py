@@ -71,6 +71,42 @@ def measured_traffic(wl_name: str, mode: str):
     return t["fetch_bytes"] + t["write_bytes"]
 
 
+def traffic_fields(wl_name: str, mode: str, off: bool = False):
+    """roofline.traffic and where it comes from: a stored reading (not
+    measured in this run) of two rocprofv3 counter passes, valid for the
+    kernel source whose SHA-256 it was taken on, null otherwise."""
+    t = MEASURED_TRAFFIC.get((wl_name, mode))
+    val = None if off else measured_traffic(wl_name, mode)
+    src = ("stored rocprofv3 FETCH_SIZE + WRITE_SIZE reading (copy-calibrated), taken on "
+           f"{t['kernel_source']} sha256 {t['sha256'][:16]}; null when the source differs") if t else None
+    return {"traffic": val,
+            "traffic_unit": "bytes per launch (HBM fetch + write, copy-calibrated rocprofv3 counters)",
+            "traffic_source": src if val is not None else (src and "not valid for this source or configuration")}
+
+
+def host_info():
+    """CPU model, logical CPU count and numpy's BLAS, for the CPU baseline."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        import threadpoolctl
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpoolctl.threadpool_info()
+                if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or None
+    except Exception:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas": blas}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -174,7 +210,7 @@ def cpu_baseline(inputs, wl, budget_s: float = 15.0, min_tokens: int = 8):
         chunk = min(2 * chunk, 64)
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 numpy oracle sparse_bwd on the last {done} of {T} query tokens of {wl.name} "
-                      f"({flops / 1e12:.3f} TFLOP in {spent:.1f} s, forward excluded)"}
+                      f"({flops / 1e12:.3f} TFLOP in {spent:.1f} s, forward excluded)", **host_info()}
 
 
 def indexer_cpu_baseline(inputs, wl, budget_s: float = 15.0, min_tokens: int = 8):
@@ -199,7 +235,7 @@ def indexer_cpu_baseline(inputs, wl, budget_s: float = 15.0, min_tokens: int = 8
         chunk = min(2 * chunk, 64)
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 numpy oracle indexer_grad_kl on the last {done} of {T} query tokens of {wl.name} "
-                      f"({flops / 1e12:.4f} TFLOP in {spent:.1f} s)"}
+                      f"({flops / 1e12:.4f} TFLOP in {spent:.1f} s)", **host_info()}
 
 
 def bench_indexer(args):
@@ -273,8 +309,7 @@ def bench_indexer(args):
                    "device": device_info()},
         "roofline": {"kernel": "idx_grad_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
-                     "mfma_tflops": round(ktf, 2), "traffic": measured_traffic(wl.name, "idx"),
-                     "traffic_unit": "bytes per launch (HBM fetch + write, copy-calibrated rocprofv3 counters)",
+                     "mfma_tflops": round(ktf, 2), **traffic_fields(wl.name, "idx"),
                      "kernel_ms": round(kern_ms, 4)},
         "cpu_baseline": cpu,
     }
@@ -342,7 +377,7 @@ def bench_forward(args):
             chunk = min(2 * chunk, 64)
         cpu = {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                "sample": f"fp64 numpy oracle sparse_fwd on the last {done} of {T} query tokens of {wl.name} "
-                         f"({fl / 1e12:.3f} TFLOP in {spent:.1f} s)"}
+                         f"({fl / 1e12:.3f} TFLOP in {spent:.1f} s)", **host_info()}
     kernel = "fwd_mla_kernel" if (wl.d_qk, wl.d_v, wl.kv_shared) == (576, 512, True) and wl.group % 64 == 0 \
         else "fwd_rows_kernel"
     line = {
@@ -358,8 +393,7 @@ def bench_forward(args):
                    "device": device_info()},
         "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(kern_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(wl.name, "fwd") if kernel == "fwd_mla_kernel" else None,
-                     "traffic_unit": "bytes per launch (HBM fetch + write, copy-calibrated rocprofv3 counters)",
+                     **traffic_fields(wl.name, "fwd", off=kernel != "fwd_mla_kernel"),
                      "kernel_ms": round(kern_ms, 4)},
         "cpu_baseline": cpu,
     }
@@ -383,6 +417,9 @@ def main():
     ap.add_argument("--evict-cache", action="store_true",
                     help="write 1 GiB before every timed call (evicts the 256 MB Infinity Cache); the step time "
                          "is then the mean of the per-call events")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="after the timed steps, this many calls each preceded by a 1 GiB eviction write, "
+                         "reported as timing.cold_cache (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (read 1 GiB, write 1 GiB): the known-size kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -463,6 +500,25 @@ def main():
     log(f"[bench] {ms:.3f} ms/step, main kernel {kern_ms:.3f} ms, {tflops:.1f} TFLOP/s "
         f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
 
+    # the same call with a cold cache beside the warm figure: 1 GiB written
+    # before each call (outside its events) evicts the 256 MB Infinity Cache
+    cold = None
+    if evict is None and args.cold_steps > 0:
+        big = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            big.fill_(float(i))
+            cold_ev[i][0].record(stream)
+            B.sparse_attn_bwd(desc, dev, outputs, ws, stream=stream)
+            cold_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        cold_ms = [a.elapsed_time(b) for a, b in cold_ev]
+        del big
+        cold = {"calls": args.cold_steps, "call_ms": percentiles(cold_ms),
+                "value": round(flop / (float(np.mean(cold_ms)) * 1e-3) / 1e12, 3)}
+        log(f"[bench] cold cache: {float(np.mean(cold_ms)):.3f} ms/call")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
@@ -495,11 +551,10 @@ def main():
         },
         "timing": {"call_ms": percentiles(call_ms), "cache_evicted_between_calls": evict is not None,
                    "step_time_from": "per-call events" if evict is not None else "bracketed region / steps",
-                   "device": device_info()},
+                   "cold_cache": cold, "device": device_info()},
         "roofline": dict(main_kernel_roofline(wl, args.dkv_mode, idx, flop, kern_ms), **{
             # the stored counter readings are of the kernel without the L1-norm sums
-            "traffic": None if args.softmax_l1 else measured_traffic(wl.name, args.dkv_mode),
-            "traffic_unit": "bytes per launch (HBM fetch + write, copy-calibrated rocprofv3 counters)",
+            **traffic_fields(wl.name, args.dkv_mode, off=args.softmax_l1),
             "kernel_ms": round(kern_ms, 4),
         }),
         "cpu_baseline": cpu,
