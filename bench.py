@@ -176,7 +176,8 @@ def main_kernel_roofline(wl: W.Workload, mode: str, idx: np.ndarray, flop: int, 
                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
                 "block_pairs": block_pairs(wl, idx)}
     tf = flop / (kern_ms * 1e-3) / 1e12
-    name = "mla_bwd_kernel" if (wl.kv_shared and wl.d_qk == 576 and mode == "deterministic") else "bwd_rows_kernel"
+    mla = wl.kv_shared and (wl.d_qk, wl.d_v) == (576, 512) and wl.group % 64 == 0 and wl.dtype == "bf16"
+    name = "mla_bwd_kernel" if mla else "bwd_rows_kernel"
     return {"kernel": name, "bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
 
@@ -409,7 +410,9 @@ def main():
                     choices=W.WORKLOAD_ORDER + list(W.INDEXER_WORKLOADS))
     ap.add_argument("--op", default="bwd", choices=["bwd", "fwd"],
                     help="bwd: the backward (the default line); fwd: the selected-attention forward alone")
-    ap.add_argument("--dkv-mode", default="deterministic", choices=["atomic", "deterministic"])
+    ap.add_argument("--dkv-mode", default="deterministic", choices=["atomic", "deterministic", "atomic_xcd"],
+                    help="dK/dV reduction: fp32 atomics, the deterministic key-major pass, or (shared-KV MLA "
+                         "shapes) fp32 atomics into one accumulator copy per XCD")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--softmax-l1", action="store_true",
                     help="also produce the softmax L1-norm side outputs in every timed call")
@@ -447,7 +450,7 @@ def main():
         bench_forward(args)
         return
     wl = W.WORKLOADS[args.workload]
-    mode = B.DKV_ATOMIC if args.dkv_mode == "atomic" else B.DKV_DETERMINISTIC
+    mode = {"atomic": B.DKV_ATOMIC, "deterministic": B.DKV_DETERMINISTIC, "atomic_xcd": B.DKV_ATOMIC_XCD}[args.dkv_mode]
     log(f"[bench] workload {wl.name}: generating inputs")
     inputs = W.make_inputs(wl, threads=16)
     idx = inputs["idx"].numpy()

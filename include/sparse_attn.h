@@ -93,7 +93,12 @@ typedef enum sa_status {
 
 enum { SA_SEL_TOKEN = 0, SA_SEL_BLOCK = 1, SA_SEL_WINDOW_CMP = 2 };
 enum { SA_LAYOUT_BSND = 0, SA_LAYOUT_TND = 1 };
-enum { SA_DKV_ATOMIC = 0, SA_DKV_DETERMINISTIC = 1 };
+/* dK/dV reduction: fp32 atomics in an unspecified order (the pages'
+ * non-deterministic default, aclnnSparseFlashAttentionGrad, "Deterministic
+ * computation"); a bitwise-repeatable key-major pass; or, for the shared-KV
+ * 576/512 kernel only, fp32 atomics into one accumulator copy per XCD summed
+ * afterwards in a fixed order of the copies. */
+enum { SA_DKV_ATOMIC = 0, SA_DKV_DETERMINISTIC = 1, SA_DKV_ATOMIC_XCD = 2 };
 enum { SA_DTYPE_BF16 = 0, SA_DTYPE_FP16 = 1 };
 
 /* Static problem description (host memory, read during the call only).
@@ -126,7 +131,7 @@ typedef struct sa_desc {
   int32_t win_right;
   int32_t cmp_ratio;    /* SA_SEL_WINDOW_CMP: ori tokens per cmp row */
   int32_t has_sinks;    /* 1: per-head sink logits in the softmax denominator */
-  int32_t dkv_mode;     /* SA_DKV_ATOMIC or SA_DKV_DETERMINISTIC */
+  int32_t dkv_mode;     /* SA_DKV_ATOMIC, SA_DKV_DETERMINISTIC or SA_DKV_ATOMIC_XCD */
   float scale;          /* softmax scale (finite, > 0) */
   int32_t softmax_l1;   /* 1: the backward also writes the softmax L1-norm
                            side outputs (sa_bwd_args_t); 0: it does not */

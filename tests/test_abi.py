@@ -96,14 +96,29 @@ def test_phase1_validation_codes():
 
 def test_softmax_l1_workspace():
     """The L1-norm sums take one fp32 plane per head group of the P kernel:
-    T * Hkv * positions * 4 bytes more for the 64-head MLA kernel."""
+    T * Hkv * positions * 4 bytes more for the 64-head MLA kernel (which
+    serves every dK/dV mode of this shape)."""
     wl = W.WORKLOADS["mla_token_8k"]
     for mode in (B.DKV_ATOMIC, B.DKV_DETERMINISTIC):
         st0, n0 = _ws(B.make_desc(wl, mode))
         st1, n1 = _ws(B.make_desc(wl, mode, softmax_l1=1))
         assert st0 == st1 == 0
-        planes = 1 if mode == B.DKV_DETERMINISTIC else 4    # 64 heads: 1 MLA group, 4 row-kernel chunks
+        planes = 1                                          # 64 heads: one head group of the MLA kernel
         assert n1 - n0 == planes * wl.total_q * wl.n_kv_heads * wl.topk * 4
+
+
+def test_atomic_modes_workspace():
+    """MLA shape: atomic mode holds one fp32 dKV accumulator (plus the D
+    plane), the per-XCD form eight; the per-XCD form is only built for the
+    shared-KV MLA kernel."""
+    wl = W.WORKLOADS["mla_token_8k"]
+    acc = wl.total_kv * wl.d_qk * 4
+    st1, n1 = _ws(B.make_desc(wl, B.DKV_ATOMIC))
+    st8, n8 = _ws(B.make_desc(wl, B.DKV_ATOMIC_XCD))
+    assert st1 == st8 == 0
+    assert n8 - n1 == 7 * acc
+    assert _ws(B.make_desc(W.WORKLOADS["nsa_block_gqa"], B.DKV_ATOMIC_XCD))[0] == 3
+    assert _ws(B.make_desc(wl, 3))[0] == 7
 
 
 def test_window_cmp_requires_shared_kv():

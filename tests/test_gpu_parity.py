@@ -75,6 +75,17 @@ def test_bwd_parity_small(name, mode, l1):
         assert ("cmp_softmax_l1" in res) == (SMALL[name].select == W.SEL_WINDOW_CMP)
 
 
+@pytest.mark.parametrize("l1", [False, True], ids=["grads", "grads+l1"])
+@pytest.mark.parametrize("name", ["mla_64h", "mla_128h_local", "mla_wcmp_sinks_varlen"])
+def test_bwd_parity_small_per_xcd_atomics(name, l1):
+    """The per-XCD atomic form of the shared-KV MLA kernel (one fp32
+    accumulator copy per XCD, summed in a fixed order of the copies)."""
+    inputs, Ob, Lb, ref = _oracle_small(name)
+    if not l1:
+        ref = {k: v for k, v in ref.items() if not k.endswith("_l1")}
+    U.run_full_case(SMALL[name], dkv_mode=B.DKV_ATOMIC_XCD, l1=l1, oracle=(inputs, Ob, Lb, ref))
+
+
 @pytest.mark.parametrize("name", ["token_gqa_d128_g20", "block_gqa_d128", "mla_wcmp_sinks_varlen"])
 def test_bwd_deterministic_mode_is_bitwise_repeatable(name):
     wl = SMALL[name]
@@ -304,18 +315,21 @@ def test_bwd_parity_nsa_block_full_size_sampled(mode):
     _sampled_full_size_case(W.WORKLOADS["nsa_block_gqa"], dkv_mode=MODES[mode])
 
 
-@pytest.mark.parametrize("mode", list(MODES))
+MLA_MODES = dict(MODES, xcd=B.DKV_ATOMIC_XCD)
+
+
+@pytest.mark.parametrize("mode", list(MLA_MODES))
 def test_bwd_parity_mla_cmp_sinks_varlen_full_size_sampled(mode):
     """Window + cmp with sinks, varlen {1024, 3000, 6000, 16000}, at full
     size: sampled dq rows, every dKV and cmp row and the full dSinks (the
     sum over all 26 024 tokens, of which only the sampled ones carry a
     non-zero dO)."""
-    _sampled_full_size_case(W.WORKLOADS["mla_cmp_sinks_varlen"], dkv_mode=MODES[mode])
+    _sampled_full_size_case(W.WORKLOADS["mla_cmp_sinks_varlen"], dkv_mode=MLA_MODES[mode])
 
 
-@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("mode", list(MLA_MODES))
 def test_bwd_parity_mla_8k_full_size_sampled(mode):
-    _sampled_full_size_case(W.WORKLOADS["mla_token_8k"], dkv_mode=MODES[mode])
+    _sampled_full_size_case(W.WORKLOADS["mla_token_8k"], dkv_mode=MLA_MODES[mode])
 
 
 @pytest.mark.parametrize("name", ["mla_token_8k", "nsa_block_gqa", "mla_cmp_sinks_varlen"])
@@ -356,6 +370,6 @@ def test_fwd_mla_64_heads_rows_over_several_compaction_passes():
     np.testing.assert_allclose(lse[sel].cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
 
 
-@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("mode", list(MLA_MODES))
 def test_bwd_parity_mla_32k_full_size_sampled(mode):
-    _sampled_full_size_case(W.WORKLOADS["mla_token_32k_local"], n_tail=32, n_early=4, dkv_mode=MODES[mode])
+    _sampled_full_size_case(W.WORKLOADS["mla_token_32k_local"], n_tail=32, n_early=4, dkv_mode=MLA_MODES[mode])

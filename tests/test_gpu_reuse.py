@@ -1,6 +1,7 @@
 """GPU parity where the dK/dV (dKV) reduction is long: every output row of
 shared-KV 576/512 cases whose key rows are named by thousands of (token,
-slot) entries, against the fp64 oracle, in both dK/dV modes.
+slot) entries, against the fp64 oracle, in every dK/dV mode (the per-XCD
+atomic form included).
 
 SparseFlashMlaGrad README, "Computation formula", Stage 3: dKV of a row
 collects scale dS^T Q + P^T dO from every query that gathered it
@@ -35,7 +36,7 @@ CASES = {
         index_policy="local_half", local_window=512),
 }
 
-MODES = {"atomic": B.DKV_ATOMIC, "det": B.DKV_DETERMINISTIC}
+MODES = {"atomic": B.DKV_ATOMIC, "det": B.DKV_DETERMINISTIC, "xcd": B.DKV_ATOMIC_XCD}
 
 _ORACLE = {}
 

@@ -22,6 +22,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL_PTR", 2: "SA_ERR_BAD_SHAPE", 3: "SA_
                 7: "SA_ERR_BAD_ARG"}
 DKV_ATOMIC = 0
 DKV_DETERMINISTIC = 1
+DKV_ATOMIC_XCD = 2     # shared-KV MLA kernel only: fp32 atomics into one accumulator copy per XCD
 DTYPE_BF16 = 0
 DTYPE_FP16 = 1
 

@@ -41,7 +41,8 @@ sa_status_t validate(const sa_desc_t* d) {
   if (!d) return SA_ERR_NULL_PTR;
   if (d->layout != SA_LAYOUT_BSND && d->layout != SA_LAYOUT_TND) return SA_ERR_BAD_ARG;
   if (d->select < SA_SEL_TOKEN || d->select > SA_SEL_WINDOW_CMP) return SA_ERR_BAD_ARG;
-  if (d->dkv_mode != SA_DKV_ATOMIC && d->dkv_mode != SA_DKV_DETERMINISTIC) return SA_ERR_BAD_ARG;
+  if (d->dkv_mode != SA_DKV_ATOMIC && d->dkv_mode != SA_DKV_DETERMINISTIC && d->dkv_mode != SA_DKV_ATOMIC_XCD)
+    return SA_ERR_BAD_ARG;
   if (d->kv_shared != 0 && d->kv_shared != 1) return SA_ERR_BAD_ARG;
   if (d->mask_causal < 0 || d->mask_causal > 2) return SA_ERR_BAD_ARG;
   if (d->has_sinks != 0 && d->has_sinks != 1) return SA_ERR_BAD_ARG;
@@ -110,7 +111,9 @@ long long csr_keys_bound(const sa_desc_t* d) {
 Params make_params(const sa_desc_t* d);
 
 struct BwdLayout {
-  size_t D, sink_term, acc_k, acc_v, acc_cmp;                   // atomic mode
+  size_t D, sink_term, acc_k, acc_v, acc_cmp;                   // atomic modes
+  size_t rep_floats;                                            // MLA atomic: floats per accumulator replica
+  int n_rep, mla;
   size_t l1;                                                    // softmax L1-norm head-chunk sums
   int n_hg_l1;
   size_t blk_base, row_ptr, entries, csr_ws, partial, dump, acc;   // deterministic mode
@@ -132,12 +135,27 @@ BwdLayout bwd_layout(const sa_desc_t* d, const Params& p) {
   // head chunks of the kernel that computes P (it writes one plane of
   // softmax L1-norm sums per chunk)
   const bool det = d->dkv_mode == SA_DKV_DETERMINISTIC;
-  if (det && sa::mla_bwd_supported(p)) L.n_hg_l1 = sa::mla_bwd_head_groups(p);
+  L.mla = sa::mla_bwd_supported(p) ? 1 : 0;
+  if (L.mla) L.n_hg_l1 = sa::mla_bwd_head_groups(p);
   else if (det && sa::blk_dkv_supported(p) && sa::blk_dq_supported(p)) L.n_hg_l1 = sa::blk_dkv_head_chunks(p);
   else L.n_hg_l1 = sa::bwd_rows_head_chunks(p);
   L.l1 = off;
   if (d->softmax_l1) off += align_up((size_t)L.n_hg_l1 * T * Hkv * (size_t)n_positions_host(d) * sizeof(float));
-  if (d->dkv_mode == SA_DKV_ATOMIC) {
+  if (d->dkv_mode != SA_DKV_DETERMINISTIC && L.mla) {
+    // the MLA kernel's atomic forms: dKV rows then cmp rows in one fp32
+    // array, one copy per XCD for the per-XCD form, and an fp32 dump row
+    L.n_rep = d->dkv_mode == SA_DKV_ATOMIC_XCD ? sa::kXcdReplicas : 1;
+    L.rep_floats = (size_t)(rows_kv(d) + rows_cmp(d)) * Hkv * d->d_qk;
+    L.acc_k = off;
+    L.acc_cmp = off + (size_t)rows_kv(d) * Hkv * d->d_qk * sizeof(float);
+    off += align_up((size_t)L.n_rep * L.rep_floats * sizeof(float));
+    L.dump = off;
+    off += align_up((size_t)d->d_qk * sizeof(float));
+    L.Tc = (int)T;
+    L.total = off;
+    return L;
+  }
+  if (d->dkv_mode != SA_DKV_DETERMINISTIC) {
     L.acc_k = off;
     off += align_up((size_t)rows_kv(d) * Hkv * d->d_qk * sizeof(float));
     L.acc_v = off;
@@ -437,7 +455,10 @@ sa_status_t sparse_attn_bwd_workspace_size(const sa_desc_t* desc, size_t* bytes)
   sa_status_t st = validate(desc);
   if (st != SA_OK) return st;
   if (!sa::bwd_rows_supported(desc->d_qk, desc->d_v, desc->kv_shared)) return SA_ERR_UNSUPPORTED;
-  *bytes = bwd_layout(desc, make_params(desc)).total;
+  const Params p = make_params(desc);
+  // the per-XCD atomic form exists for the shared-KV MLA kernel only
+  if (desc->dkv_mode == SA_DKV_ATOMIC_XCD && !sa::mla_bwd_supported(p)) return SA_ERR_UNSUPPORTED;
+  *bytes = bwd_layout(desc, p).total;
   return SA_OK;
 }
 
@@ -509,13 +530,35 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   // staged dO and O: the separate pass would re-read dO and O of many tokens
   // per unit of main-kernel work.  Every other call takes them from the
   // preprocess.
-  const bool fused_d = desc->dkv_mode == SA_DKV_DETERMINISTIC && L.fast && n_positions_host(desc) <= 1024;
+  const bool fused_d = L.mla && n_positions_host(desc) <= 1024;
   w.fuse_d = fused_d ? 1 : 0;
   if (!fused_d) {
     SA_TRY_HIP(sa::launch_preprocess(p, w, s));
     if (desc->has_sinks) SA_TRY_HIP(sa::launch_dsinks(p, w, s));
   }
 
+  if (desc->dkv_mode != SA_DKV_DETERMINISTIC && L.mla) {
+    // shared-KV MLA kernel, fp32 atomic adds (into the XCD's replica in the
+    // per-XCD form), then one pass that sums the replicas in a fixed order
+    // and casts
+    w.acc_k = reinterpret_cast<float*>(ws + L.acc_k);
+    w.acc_cmp = reinterpret_cast<float*>(ws + L.acc_cmp);
+    w.out = L.n_rep > 1 ? sa::kOutAtomicXcd : sa::kOutAtomic;
+    w.rep_stride = (long long)L.rep_floats;
+    w.dump = ws + L.dump;
+    w.npos = (int)n_positions_host(desc);
+    w.RW = desc->d_qk;
+    SA_TRY_HIP(sa::launch_fill_zero(w.acc_k, (size_t)L.n_rep * L.rep_floats, s));
+    if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
+    SA_TRY_HIP(sa::launch_bwd_mla(p, w, s));
+    if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
+    if (fused_d && desc->has_sinks) SA_TRY_HIP(sa::launch_dsinks(p, w, s));
+    SA_TRY_HIP(l1_norm());
+    const long long n_a = rows_kv(desc) * (long long)Hkv * desc->d_qk;
+    SA_TRY_HIP(sa::launch_replica_sum_cast(w.acc_k, (long long)L.rep_floats, L.n_rep, (long long)L.rep_floats, n_a,
+                                           a->dkv, a->d_cmp_kv, p.fp16, s));
+    return SA_OK;
+  }
   if (desc->dkv_mode == SA_DKV_ATOMIC) {
     w.acc_k = reinterpret_cast<float*>(ws + L.acc_k);
     w.acc_v = desc->kv_shared ? nullptr : reinterpret_cast<float*>(ws + L.acc_v);

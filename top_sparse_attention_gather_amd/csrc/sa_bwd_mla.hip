@@ -154,9 +154,23 @@ __device__ __forceinline__ void gather_tile(const Params& p, const MlaSmem& sm, 
     load_lds16(src + sg * 64, d + sg * kSegElems);
 }
 
+// The XCD (accelerator complex die) the wave runs on, 0..7: it picks the
+// fp32 accumulator replica of the per-XCD atomic form.  Any value is
+// correct (the adds are device-scope atomics); one replica per XCD keeps
+// the XCDs off each other's lines.
+__device__ __forceinline__ int xcc_id() {
+  int x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 7;
+}
+
 // L1: also write the head sums of P behind the softmax L1-norm outputs
 // (SparseFlashMlaGrad README, parameter table).
-template <bool L1>
+// OUT: how phase B's per-(token, key) dKV rows leave the kernel -- kOutPartial:
+// bf16 partial rows for the deterministic key-major reduce; kOutAtomic: fp32
+// atomic adds into the accumulator; kOutAtomicXcd: the same into the
+// accumulator replica of the wave's XCD (summed in a fixed order afterwards).
+template <bool L1, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffers w) {
   __shared__ MlaSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -377,6 +391,52 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     *reinterpret_cast<uint2*>(h.row + col_block(c) + lq * 4) = v;
   };
 
+  // ---- atomic forms of phase B: the same products with the operands
+  // swapped, dKV[key][col] = (scale dS)^T Q + P^T dO, so that lane (l16, lq)
+  // holds keys 4lq..4lq+3 of column l16 of a 16-column block and one atomic
+  // instruction adds 4 keys x 16 contiguous columns.
+  float* const acc_k = OUT == kOutAtomicXcd ? w.acc_k + (size_t)xcc_id() * w.rep_stride : w.acc_k;
+  float* const acc_c = OUT == kOutAtomicXcd ? w.acc_cmp + (size_t)xcc_id() * w.rep_stride : w.acc_cmp;
+  struct AHalf {
+    bf16x8 d0, d1, p0, p1;
+    float* row[4];            // accumulator rows of keys 4lq + r (or the dump row)
+  };
+  auto a_setup = [&](int itb, int kb) {
+    AHalf h;
+    const bf16* xd = sm.xds[itb & 1];
+    const bf16* xpp = sm.xp[itb & 1];
+    const int krow = kb * 16 + l16;
+    h.d0 = *reinterpret_cast<const bf16x8*>(&xd[krow * kXS + lq * 8]);
+    h.d1 = *reinterpret_cast<const bf16x8*>(&xd[krow * kXS + 32 + lq * 8]);
+    h.p0 = *reinterpret_cast<const bf16x8*>(&xpp[krow * kXS + lq * 8]);
+    h.p1 = *reinterpret_cast<const bf16x8*>(&xpp[krow * kXS + 32 + lq * 8]);
+    const int k0 = itb * kNT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = kb * 16 + lq * 4 + r;
+      const bool valid = key < cnt - k0;
+      const int code = valid ? sm.rows[k0 + key] : 0;   // k0 + key < kMaxPos
+      float* const rp = (code & kCmpFlag) ? acc_c + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * kDQK
+                                          : acc_k + ((size_t)code * p.Hkv + g) * kDQK;
+      h.row[r] = valid ? rp : static_cast<float*>(w.dump);
+    }
+    return h;
+  };
+  auto a_chain = [&](const AHalf& h, int cc, const bf16x8& o0, const bf16x8& o1) {
+    f32x4 acc = mfma16x16x32(h.d0, QT[cc][0], f32x4{0.f, 0.f, 0.f, 0.f});
+    acc = mfma16x16x32(h.d1, QT[cc][1], acc);
+    if (cc < 8) {
+      acc = mfma16x16x32(h.p0, o0, acc);
+      acc = mfma16x16x32(h.p1, o1, acc);
+    }
+    return acc;
+  };
+  auto a_add = [&](const AHalf& h, int c, const f32x4& a) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      __hip_atomic_fetch_add(h.row[r] + col_block(c) + l16, a[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
   // One tile.  kvb (read) and kvn (filled by direct loads for the next
   // tile) are restrict-qualified: they never overlap, and the alias scopes
   // this gives every LDS access let the compiler skip waiting for the
@@ -434,7 +494,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
       f32x4 S = {0.f, 0.f, 0.f, 0.f}, dP = S;
       // phase B of the previous tile, key half b (none for the first tile)
       BHalf hb;
-      if constexpr (PB) hb = b_setup(it - 1, b, true);
+      AHalf ha;
+      if constexpr (PB) {
+        if constexpr (OUT == kOutPartial) hb = b_setup(it - 1, b, true);
+        else ha = a_setup(it - 1, b);
+      }
       f32x4 br[9];
       // the dO^T operands of each chain are read one chain ahead (and the
       // KV fragments kPF steps ahead): the scheduling barriers keep those
@@ -448,12 +512,19 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
       for (int kk = 0; kk < 18; ++kk) {
         if (PB && (kk & 1) == 0) {
           const int cc = kk >> 1;
-          br[cc] = b_chain(hb, cc, cc < kDotLds ? od0 : dot_op(cc, 0), cc < kDotLds ? od1 : dot_op(cc, 1));
+          if constexpr (OUT == kOutPartial)
+            br[cc] = b_chain(hb, cc, cc < kDotLds ? od0 : dot_op(cc, 0), cc < kDotLds ? od1 : dot_op(cc, 1));
+          else
+            br[cc] = a_chain(ha, cc, cc < kDotLds ? od0 : dot_op(cc, 0), cc < kDotLds ? od1 : dot_op(cc, 1));
           if (cc + 1 < kDotLds) {
             od0 = dot_op(cc + 1, 0);
             od1 = dot_op(cc + 1, 1);
           }
-          if (cc >= 2 && (cc & 1) == 0) b_put_pair(hb, cc - 2, br[cc - 2], br[cc - 1]);
+          if constexpr (OUT == kOutPartial) {
+            if (cc >= 2 && (cc & 1) == 0) b_put_pair(hb, cc - 2, br[cc - 2], br[cc - 1]);
+          } else {
+            if (cc >= 2) a_add(ha, cc - 2, br[cc - 2]);
+          }
         }
         if (kk + kPF < 18) {
           const int k2 = kk + kPF;
@@ -471,7 +542,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
         if (kk < 16) dP = mfma16x16x32(a, dOA[kk], dP);
         if (b == 1 && kk == 2) softmax_grad(0, Sh0, Ph0);
       }
-      if constexpr (PB) b_put_single(hb, 8, br[8]);
+      if constexpr (PB) {
+        if constexpr (OUT == kOutPartial) {
+          b_put_single(hb, 8, br[8]);
+        } else {
+          a_add(ha, 7, br[7]);
+          a_add(ha, 8, br[8]);
+        }
+      }
       if (b == 0) {
         Sh0 = S;
         Ph0 = dP;
@@ -529,14 +607,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   if (ntiles > 0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const BHalf h = b_setup(ntiles - 1, kb, true);
       f32x4 br[9];
+      if constexpr (OUT == kOutPartial) {
+        const BHalf h = b_setup(ntiles - 1, kb, true);
 #pragma unroll
-      for (int cc = 0; cc < 9; ++cc) {
-        br[cc] = b_chain(h, cc, dot_op(cc, 0), dot_op(cc, 1));
-        if (cc >= 2 && (cc & 1) == 0) b_put_pair(h, cc - 2, br[cc - 2], br[cc - 1]);
+        for (int cc = 0; cc < 9; ++cc) {
+          br[cc] = b_chain(h, cc, dot_op(cc, 0), dot_op(cc, 1));
+          if (cc >= 2 && (cc & 1) == 0) b_put_pair(h, cc - 2, br[cc - 2], br[cc - 1]);
+        }
+        b_put_single(h, 8, br[8]);
+      } else {
+        const AHalf h = a_setup(ntiles - 1, kb);
+#pragma unroll
+        for (int cc = 0; cc < 9; ++cc) {
+          br[cc] = a_chain(h, cc, dot_op(cc, 0), dot_op(cc, 1));
+          if (cc >= 2) a_add(h, cc - 2, br[cc - 2]);
+        }
+        a_add(h, 7, br[7]);
+        a_add(h, 8, br[8]);
       }
-      b_put_single(h, 8, br[8]);
     }
   }
   // no direct load may still be writing this workgroup's LDS when it ends
@@ -568,8 +657,20 @@ int mla_bwd_head_groups(const Params& p) { return p.G / kHeads; }
 
 hipError_t launch_bwd_mla(const Params& p, const BwdBuffers& w, hipStream_t s) {
   dim3 grid((unsigned)(w.Tc * p.Hkv), (unsigned)(p.G / kHeads));
-  if (w.l1) hipLaunchKernelGGL(mla_bwd_kernel<true>, grid, dim3(kThreads), 0, s, p, w);
-  else hipLaunchKernelGGL(mla_bwd_kernel<false>, grid, dim3(kThreads), 0, s, p, w);
+  const bool l1 = w.l1 != nullptr;
+  switch (w.out) {
+    case kOutAtomic:
+      if (l1) hipLaunchKernelGGL((mla_bwd_kernel<true, kOutAtomic>), grid, dim3(kThreads), 0, s, p, w);
+      else hipLaunchKernelGGL((mla_bwd_kernel<false, kOutAtomic>), grid, dim3(kThreads), 0, s, p, w);
+      break;
+    case kOutAtomicXcd:
+      if (l1) hipLaunchKernelGGL((mla_bwd_kernel<true, kOutAtomicXcd>), grid, dim3(kThreads), 0, s, p, w);
+      else hipLaunchKernelGGL((mla_bwd_kernel<false, kOutAtomicXcd>), grid, dim3(kThreads), 0, s, p, w);
+      break;
+    default:
+      if (l1) hipLaunchKernelGGL((mla_bwd_kernel<true, kOutPartial>), grid, dim3(kThreads), 0, s, p, w);
+      else hipLaunchKernelGGL((mla_bwd_kernel<false, kOutPartial>), grid, dim3(kThreads), 0, s, p, w);
+  }
   return hipGetLastError();
 }
 

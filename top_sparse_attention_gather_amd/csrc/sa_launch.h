@@ -12,6 +12,12 @@
 
 namespace sa {
 
+// Output forms of the shared-KV MLA kernel's phase B.
+constexpr int kOutPartial = 0;     // bf16 partial rows, key-major reduce afterwards
+constexpr int kOutAtomic = 1;      // fp32 atomic adds into one accumulator
+constexpr int kOutAtomicXcd = 2;   // fp32 atomic adds into the XCD's accumulator replica
+constexpr int kXcdReplicas = 8;
+
 // Output/workspace pointers of one backward call.
 struct BwdBuffers {
   float* D;          // [T][Hq] softmax-grad term
@@ -20,6 +26,11 @@ struct BwdBuffers {
   float* acc_k;      // fp32 dK (or shared dKV) accumulator, rows x Hkv x dqk (atomic mode)
   float* acc_v;      // fp32 dV accumulator (separate V, atomic mode)
   float* acc_cmp;    // fp32 dCmpKV accumulator (window+cmp, atomic mode)
+  // MLA kernel: how phase B leaves the kernel (kOutPartial, kOutAtomic or
+  // kOutAtomicXcd); with kOutAtomicXcd, replica x of acc_k / acc_cmp starts
+  // x * rep_stride floats further on
+  int out;
+  long long rep_stride;
   bf16* dq;
   float* dsinks;
   // deterministic mode: one partial row per (head chunk, token, kv head,
@@ -74,6 +85,10 @@ hipError_t launch_csr_transpose(const Params& p, int t0, int t1, long long n_key
 hipError_t launch_reduce(const Params& p, const ReduceArgs& r, hipStream_t s);
 hipError_t launch_split_cast(const float* acc, long long n_rows, int RW, int dqk, void* a, void* b, int fp16,
                              hipStream_t s);
+// out[i] = sum over x = 0..n_rep-1, in that order, of acc[x * stride + i],
+// cast to the 16-bit output: elements [0, n_a) to a, [n_a, n) to b
+hipError_t launch_replica_sum_cast(const float* acc, long long stride, int n_rep, long long n, long long n_a, void* a,
+                                   void* b, int fp16, hipStream_t s);
 
 // Softmax L1-norm outputs from the head-chunk sums `l1` ([n_hg][T * Hkv]
 // [npos]): per (token, kv head) row, the chunk sums of every used position

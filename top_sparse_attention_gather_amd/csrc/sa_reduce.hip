@@ -251,7 +251,33 @@ __global__ void split_cast_kernel(const float* __restrict__ acc, long long n, in
   else b[row * (RW - dqk) + (c - dqk)] = (E)acc[i];
 }
 
+// Fixed-order sum of the accumulator replicas of the per-XCD atomic form,
+// cast to the 16-bit output (the first n_a elements to a, the rest to b).
+template <typename E>
+__global__ void replica_sum_cast_kernel(const float* __restrict__ acc, long long stride, int n_rep, long long n,
+                                        long long n_a, E* __restrict__ a, E* __restrict__ b) {
+  const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v = acc[i];
+  for (int x = 1; x < n_rep; ++x) v += acc[x * stride + i];
+  if (i < n_a) a[i] = (E)v;
+  else b[i - n_a] = (E)v;
+}
+
 }  // namespace
+
+hipError_t launch_replica_sum_cast(const float* acc, long long stride, int n_rep, long long n, long long n_a, void* a,
+                                   void* b, int fp16, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (fp16)
+    hipLaunchKernelGGL(replica_sum_cast_kernel<f16>, grid, dim3(256), 0, s, acc, stride, n_rep, n, n_a,
+                       static_cast<f16*>(a), static_cast<f16*>(b));
+  else
+    hipLaunchKernelGGL(replica_sum_cast_kernel<bf16>, grid, dim3(256), 0, s, acc, stride, n_rep, n, n_a,
+                       static_cast<bf16*>(a), static_cast<bf16*>(b));
+  return hipGetLastError();
+}
 
 hipError_t launch_reduce(const Params& p, const ReduceArgs& r, hipStream_t s) {
   if (r.n_out_rows == 0) return hipSuccess;
