@@ -17,6 +17,7 @@ bounded sample on the host cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -176,7 +177,7 @@ def main_kernel_roofline(wl: W.Workload, mode: str, idx: np.ndarray, flop: int, 
                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
                 "block_pairs": block_pairs(wl, idx)}
     tf = flop / (kern_ms * 1e-3) / 1e12
-    mla = wl.kv_shared and (wl.d_qk, wl.d_v) == (576, 512) and wl.group % 64 == 0 and wl.dtype == "bf16"
+    mla = wl.kv_shared and (wl.d_qk, wl.d_v) == (576, 512) and wl.select != W.SEL_BLOCK
     name = "mla_bwd_kernel" if mla else "bwd_rows_kernel"
     return {"kernel": name, "bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
@@ -317,6 +318,22 @@ def bench_indexer(args):
     print(json.dumps(line), flush=True)
 
 
+def workload_of(args) -> W.Workload:
+    """The named workload with the command line's head, top-k and format
+    overrides (named in the workload's name)."""
+    wl = W.WORKLOADS[args.workload]
+    over = {}
+    if args.heads:
+        over["n_q_heads"] = args.heads * wl.n_kv_heads
+    if args.topk:
+        over["topk"] = args.topk
+    if args.dtype:
+        over["dtype"] = args.dtype
+    if over:
+        wl = dataclasses.replace(wl, name=wl.name + "".join(f"+{k}={v}" for k, v in over.items()), **over)
+    return wl
+
+
 def fwd_flops_per_pair(wl: W.Workload) -> int:
     """S = q K^T and O = P V: 2 (d_qk + d_v) per head and selected row."""
     return wl.group * 2 * (wl.d_qk + wl.d_v)
@@ -326,7 +343,7 @@ def bench_forward(args):
     """Selected-attention forward (O and lse), the step before the backward:
     one step = one sparse_attn_fwd call, a single kernel launch, so the
     per-call events time that kernel."""
-    wl = W.WORKLOADS[args.workload]
+    wl = workload_of(args)
     log(f"[bench] workload {wl.name} (forward): generating inputs")
     inputs = W.make_inputs(wl, threads=16)
     idx = inputs["idx"].numpy()
@@ -379,13 +396,13 @@ def bench_forward(args):
         cpu = {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                "sample": f"fp64 numpy oracle sparse_fwd on the last {done} of {T} query tokens of {wl.name} "
                          f"({fl / 1e12:.3f} TFLOP in {spent:.1f} s)", **host_info()}
-    kernel = "fwd_mla_kernel" if (wl.d_qk, wl.d_v, wl.kv_shared) == (576, 512, True) and wl.group % 64 == 0 \
+    kernel = "fwd_mla_kernel" if (wl.d_qk, wl.d_v, wl.kv_shared) == (576, 512, True) and wl.group >= 16 \
         else "fwd_rows_kernel"
     line = {
         "metric": "sparse-attn fwd TFLOP/s (selected-KV FLOPs), 1 GPU",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": f"{wl.name} forward: B={wl.batch} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} "
                                f"d_qk={wl.d_qk} d_v={wl.d_v} top-{wl.topk}",
                    "valid_pairs": pairs, "selected_kv_tflop": round(flop / 1e12, 4),
@@ -410,6 +427,10 @@ def main():
                     choices=W.WORKLOAD_ORDER + list(W.INDEXER_WORKLOADS))
     ap.add_argument("--op", default="bwd", choices=["bwd", "fwd"],
                     help="bwd: the backward (the default line); fwd: the selected-attention forward alone")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="override the workload's query heads per kv head (sweeps off the 64-head shape)")
+    ap.add_argument("--topk", type=int, default=0, help="override the workload's index slots per row")
+    ap.add_argument("--dtype", default="", choices=["", "bf16", "fp16"], help="override the 16-bit input format")
     ap.add_argument("--dkv-mode", default="deterministic", choices=["atomic", "deterministic", "atomic_xcd"],
                     help="dK/dV reduction: fp32 atomics, the deterministic key-major pass, or (shared-KV MLA "
                          "shapes) fp32 atomics into one accumulator copy per XCD")
@@ -449,7 +470,7 @@ def main():
     if args.op == "fwd":
         bench_forward(args)
         return
-    wl = W.WORKLOADS[args.workload]
+    wl = workload_of(args)
     mode = {"atomic": B.DKV_ATOMIC, "deterministic": B.DKV_DETERMINISTIC, "atomic_xcd": B.DKV_ATOMIC_XCD}[args.dkv_mode]
     log(f"[bench] workload {wl.name}: generating inputs")
     inputs = W.make_inputs(wl, threads=16)
@@ -539,7 +560,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wl.dtype,
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: B={wl.batch} S={wl.seqlens[0] if wl.batch == 1 else list(wl.seqlens)} "

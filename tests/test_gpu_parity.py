@@ -207,8 +207,8 @@ def test_bwd_block_sizes_off_the_block_dq_kernel(mode, bs):
 @pytest.mark.parametrize("mode", list(MODES))
 def test_bwd_mla_head_counts_off_the_mla_kernel(mode, heads):
     """Shared-KV 576/512 with a head count that is not a multiple of 64 (the
-    pages allow 1 to 128): the generic row kernel, with a ragged head chunk
-    for 20 heads, both dK/dV modes."""
+    pages allow 1 to 128): the 64-head kernel with 63 (1 head) or 44 (20
+    heads) heads masked; both dK/dV modes."""
     wl = _wl(name=f"mla_{heads}h", seqlens=(200,), n_q_heads=heads, d_qk=576, d_v=512, kv_shared=True, topk=80,
              kv_std=0.5, seed=90 + heads)
     U.say(f"[mla heads={heads}] {mode}")
@@ -275,7 +275,8 @@ def _sampled_full_size_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DET
     U.say(f"[full] {wl.name}: oracle forward on {toks.size} tokens")
     pb = O.Problem(inp)
     out_ref, lse_ref = O.sparse_fwd(pb, toks.tolist())
-    Ob, Lb = O.round_fwd_outputs(out_ref, lse_ref)
+    dt16 = torch.float16 if wl.dtype == "fp16" else torch.bfloat16
+    Ob, Lb = O.round_fwd_outputs(out_ref, lse_ref, dt16)
     o[torch.from_numpy(toks).cuda()] = Ob.cuda()
     lse[torch.from_numpy(toks).cuda()] = Lb.cuda()
     dev["o"], dev["lse"] = o, lse
@@ -284,7 +285,7 @@ def _sampled_full_size_case(wl, n_tail=48, n_early=6, seed=0, dkv_mode=B.DKV_DET
     torch.cuda.synchronize()
     got = {k: v.float().cpu().numpy() for k, v in out.items()}
     del o, lse, dev, out
-    O_full = torch.zeros(T, wl.n_q_heads, wl.d_v, dtype=torch.bfloat16)
+    O_full = torch.zeros(T, wl.n_q_heads, wl.d_v, dtype=dt16)
     L_full = torch.zeros(T, wl.n_q_heads, dtype=torch.float32)
     O_full[torch.from_numpy(toks)] = Ob
     L_full[torch.from_numpy(toks)] = Lb
@@ -346,10 +347,10 @@ MLA_LONG_ROWS = W.Workload(name="mla_long_rows", select=W.SEL_TOKEN, layout=W.LA
 
 
 @pytest.mark.parametrize("mode", ["det", "atomic"])
-def test_bwd_mla_rows_longer_than_the_mla_kernel_takes(mode):
-    """Shared-KV 576/512 with 64 heads and 2100 positions per row: past the
-    64-head MLA kernel's 2048, so the generic row kernel (two compaction
-    passes) runs; the last tokens against the oracle."""
+def test_bwd_mla_rows_longer_than_one_mla_pass(mode):
+    """Shared-KV 576/512 with 64 heads and 2100 positions per row: past one
+    2048-position compaction pass of the 64-head MLA kernel, so the late
+    tokens take two passes; every dKV row and the sampled dq rows."""
     _sampled_full_size_case(MLA_LONG_ROWS, n_tail=8, n_early=2,
                       dkv_mode=B.DKV_DETERMINISTIC if mode == "det" else B.DKV_ATOMIC)
 

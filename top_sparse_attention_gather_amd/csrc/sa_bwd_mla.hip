@@ -120,6 +120,34 @@ __device__ __forceinline__ bf16x8 join(i16x4 a, i16x4 b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// The two 16-bit input formats.  Operands travel through LDS and registers
+// as raw 16-bit containers (typed bf16 here); only the MFMA, the
+// conversions from and to fp32 and the exchange factor depend on the
+// format.  fp16 multiplies the exchanged P and scale dS (small at long
+// lists: about 1/2048 and 2e-5) by 2^10, which keeps them out of fp16's
+// subnormal range; the fp32 results are divided by it (exact).
+template <typename E>
+struct Fmt;
+
+template <>
+struct Fmt<bf16> {
+  static constexpr float kX = 1.f;
+  __device__ static f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c) { return mfma16x16x32(a, b, c); }
+  __device__ static bf16 to16(float x) { return (bf16)x; }
+  __device__ static float from16(bf16 x) { return (float)x; }
+};
+
+template <>
+struct Fmt<f16> {
+  static constexpr float kX = 1024.f;
+  __device__ static f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+  __device__ static bf16 to16(float x) { return __builtin_bit_cast(bf16, (f16)x); }
+  __device__ static float from16(bf16 x) { return (float)__builtin_bit_cast(f16, x); }
+};
+
 __device__ __forceinline__ const bf16* row_ptr(const Params& p, int code, int g) {
   return (code & kCmpFlag) ? p.cmp + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * kDQK
                            : p.k + ((size_t)code * p.Hkv + g) * kDQK;
@@ -170,8 +198,16 @@ __device__ __forceinline__ int xcc_id() {
 // bf16 partial rows for the deterministic key-major reduce; kOutAtomic: fp32
 // atomic adds into the accumulator; kOutAtomicXcd: the same into the
 // accumulator replica of the wave's XCD (summed in a fixed order afterwards).
-template <bool L1, int OUT>
+// E: the inputs' 16-bit format (bf16 or fp16).  The workgroup's head group
+// may hold fewer than 64 heads (the last group when the heads per kv head
+// are not a multiple of 64): the missing heads are masked (P = 0, so they
+// add nothing; their loads repeat a present head's row and their dQ is not
+// stored).  Rows longer than kMaxPos positions are compacted and processed
+// in passes of kMaxPos positions.
+template <typename E, bool L1, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffers w) {
+  using F = Fmt<E>;
+  constexpr float kX = F::kX, kInvX = 1.f / F::kX;
   __shared__ MlaSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform: keep it (and everything derived from it,
@@ -181,25 +217,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   const int row = w.t0 * p.Hkv + blockIdx.x;   // (token, kv head)
   const int t = row / p.Hkv, g = row - t * p.Hkv;
   const int h0 = g * p.G + blockIdx.y * kHeads;
+  const int gh = min(kHeads, p.G - (int)blockIdx.y * kHeads);   // heads present in this group
   const SeqPos s = seq_pos(p, t);
   const int* irow = p.idx + (size_t)row * p.topk;
   bf16* part_row0 = static_cast<bf16*>(w.partial) +
                     (((size_t)blockIdx.y * w.Tc * p.Hkv + blockIdx.x) * w.npos) * kDQK;
 
-  // ---- compacted selection (positions and their row codes) --------------
+  // ---- compacted selection (positions and their row codes) of the first
+  // pass of at most kMaxPos positions --------------------------------------
   const int npos = n_positions(p);
-  const int cnt =
-      compact_positions_batched<kMaxPos / 256>(p, s, irow, npos, sm.rows, sm.wave, sm.vpos, row_len(p, row));
+  const int len = row_len(p, row);
+  int cnt = compact_positions_batched<kMaxPos / 256>(p, s, irow, min(npos, kMaxPos), sm.rows, sm.wave, sm.vpos,
+                                                     len, 0);
 
   // ---- lse / D of the wave's heads (phase-A layout: head = 16 wv + l16);
   // with fuse_d, D follows from the staged dO and O below -------------------
-  const int hA = h0 + wv * 16 + l16;
+  const bool head_ok = wv * 16 + l16 < gh;
+  const int hA = h0 + min(wv * 16 + l16, gh - 1);
   const float lse = p.lse[(size_t)t * p.Hq + hA];
   float Dv = w.fuse_d ? 0.f : w.D[(size_t)t * p.Hq + hA];
   const float kLog2e = 1.4426950408889634f;
   const float lse2 = lse * kLog2e;
   const float sl2 = p.scale * kLog2e;
-  const bool row_live = lse > -INFINITY;
+  const bool row_live = head_ok && lse > -INFINITY;
 
   // ---- Q and dO into registers, via LDS, in both operand layouts ---------
   // Q goes to the two KV tile buffers and dO to the exchange / dO^T-block
@@ -215,24 +255,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     const int hr = wv * 8 + (lane >> 3);
     const int sc = seg_chunk(lane) * 8;
     {
-      const bf16* src = p.q + ((size_t)t * p.Hq + h0 + hr) * kDQK + sc;
-      const bf16* srcd = p.dO + ((size_t)t * p.Hq + h0 + hr) * kDV + sc;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
+        const int hq = h0 + min(hb * 32 + hr, gh - 1);   // a missing head repeats the last present one
+        const bf16* src = p.q + ((size_t)t * p.Hq + hq) * kDQK + sc;
+        const bf16* srcd = p.dO + ((size_t)t * p.Hq + hq) * kDV + sc;
 #pragma unroll
         for (int sg = 0; sg < 9; ++sg)
-          load_lds16(src + (size_t)hb * 32 * kDQK + sg * 64, sm.kv + hb * kTileElems + group_base(wv) + sg * kSegElems);
+          load_lds16(src + sg * 64, sm.kv + hb * kTileElems + group_base(wv) + sg * kSegElems);
 #pragma unroll
         for (int sg = 0; sg < 8; ++sg)
-          load_lds16(srcd + (size_t)hb * 32 * kDV + sg * 64,
-                     sm.dost + hb * kDoTileElems + group_base(wv, kDoGroupStride) + sg * kSegElems);
+          load_lds16(srcd + sg * 64, sm.dost + hb * kDoTileElems + group_base(wv, kDoGroupStride) + sg * kSegElems);
       }
     }
     uint4 orow[16];   // O of head 16wv + i, columns 8 lane .. 8 lane + 7
     if (w.fuse_d) {
-      const bf16* ob = p.o + ((size_t)t * p.Hq + h0 + wv * 16) * kDV + lane * 8;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) orow[i] = *reinterpret_cast<const uint4*>(ob + (size_t)i * kDV);
+      for (int i = 0; i < 16; ++i)
+        orow[i] = *reinterpret_cast<const uint4*>(p.o + ((size_t)t * p.Hq + h0 + min(wv * 16 + i, gh - 1)) * kDV +
+                                                  lane * 8);
     }
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     // D of head 16wv + i: the lane's 8 products with chunk `lane` of the
@@ -246,13 +287,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
         const bf16x8 ov = __builtin_bit_cast(bf16x8, orow[i]);
         float a = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) a += (float)ov[j] * (float)dv[j];
+        for (int j = 0; j < 8; ++j) a += F::from16(ov[j]) * F::from16(dv[j]);
         a = wave_sum(a);
         Dv = l16 == i ? a : Dv;
       }
       // the dSinks term of each (token, head) row (SparseFlashMlaGrad
       // README, Stage 3), summed over the tokens after the kernel
-      if (p.has_sinks && lq == 0)
+      if (p.has_sinks && lq == 0 && head_ok)
         w.sink_term[(size_t)t * p.Hq + hA] = lse > -INFINITY ? -__expf(p.sinks[hA] - lse) * Dv : 0.f;
     }
     // QA / dOA: head 16wv + l16 = buffer wv / 2, local row 16 (wv % 2) + l16
@@ -294,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
 #pragma unroll
   for (int m = 0; m < 36; ++m) dQ[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ntiles = (cnt + kNT - 1) / kNT;
+  int ntiles = (cnt + kNT - 1) / kNT;
   if (ntiles > 0) gather_tile(p, sm, sm.kv, 0, cnt, g, wv, lane);
 
   // per-lane LDS offsets inside a tile: phase-A fragments (row l16 or
@@ -362,11 +403,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   // one column-block chain: Q^T (scale dS) + dO^T P (no dO part for the
   // rope columns, cc = 8); o0 / o1 are its dO^T operands
   auto b_chain = [&](const BHalf& h, int cc, const bf16x8& o0, const bf16x8& o1) {
-    f32x4 acc = mfma16x16x32(QT[cc][0], h.d0, f32x4{0.f, 0.f, 0.f, 0.f});
-    acc = mfma16x16x32(QT[cc][1], h.d1, acc);
+    f32x4 acc = F::mma(QT[cc][0], h.d0, f32x4{0.f, 0.f, 0.f, 0.f});
+    acc = F::mma(QT[cc][1], h.d1, acc);
     if (cc < 8) {
-      acc = mfma16x16x32(o0, h.p0, acc);
-      acc = mfma16x16x32(o1, h.p1, acc);
+      acc = F::mma(o0, h.p0, acc);
+      acc = F::mma(o1, h.p1, acc);
     }
     return acc;
   };
@@ -380,13 +421,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(unsigned, bf16x2{(bf16)a, (bf16)b});
   };
-  auto b_put_pair = [&](const BHalf& h, int c, const f32x4& a, const f32x4& b) {
+  auto b_put_pair = [&](const BHalf& h, int c, f32x4 a, f32x4 b) {
+    if constexpr (kX != 1.f) {
+      a *= kInvX;
+      b *= kInvX;
+    }
     const auto s0 = __builtin_amdgcn_permlane16_swap(pk2(a[0], a[1]), pk2(b[0], b[1]), false, false);
     const auto s1 = __builtin_amdgcn_permlane16_swap(pk2(a[2], a[3]), pk2(b[2], b[3]), false, false);
     const uint4 v = {s0[0], s1[0], s0[1], s1[1]};
     *reinterpret_cast<uint4*>(h.row + col_block(c) + (lq & 1) * 16 + (lq >> 1) * 8) = v;
   };
-  auto b_put_single = [&](const BHalf& h, int c, const f32x4& a) {
+  auto b_put_single = [&](const BHalf& h, int c, f32x4 a) {
+    if constexpr (kX != 1.f) a *= kInvX;
     const uint2 v = {pk2(a[0], a[1]), pk2(a[2], a[3])};
     *reinterpret_cast<uint2*>(h.row + col_block(c) + lq * 4) = v;
   };
@@ -423,18 +469,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     return h;
   };
   auto a_chain = [&](const AHalf& h, int cc, const bf16x8& o0, const bf16x8& o1) {
-    f32x4 acc = mfma16x16x32(h.d0, QT[cc][0], f32x4{0.f, 0.f, 0.f, 0.f});
-    acc = mfma16x16x32(h.d1, QT[cc][1], acc);
+    f32x4 acc = F::mma(h.d0, QT[cc][0], f32x4{0.f, 0.f, 0.f, 0.f});
+    acc = F::mma(h.d1, QT[cc][1], acc);
     if (cc < 8) {
-      acc = mfma16x16x32(h.p0, o0, acc);
-      acc = mfma16x16x32(h.p1, o1, acc);
+      acc = F::mma(h.p0, o0, acc);
+      acc = F::mma(h.p1, o1, acc);
     }
     return acc;
   };
   auto a_add = [&](const AHalf& h, int c, const f32x4& a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      __hip_atomic_fetch_add(h.row[r] + col_block(c) + l16, a[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(h.row[r] + col_block(c) + l16, a[r] * kInvX, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
   // One tile.  kvb (read) and kvn (filled by direct loads for the next
@@ -467,8 +513,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
         const bool v = row_live && key < nvalid;
         const float pr = v ? __builtin_amdgcn_exp2f(S[r] * sl2 - lse2) : 0.f;
         const float ds = pr * (dP[r] - Dv);
-        xw[key * kXS + wv * 16 + l16] = (bf16)(ds * p.scale);
-        pw[key * kXS + wv * 16 + l16] = (bf16)pr;
+        xw[key * kXS + wv * 16 + l16] = F::to16(ds * (p.scale * kX));
+        pw[key * kXS + wv * 16 + l16] = F::to16(pr * kX);
         prs[r] = pr;
       }
       if constexpr (L1) {
@@ -538,8 +584,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
           load_lds16(gsrc + sg * 64, gdst + sg * kSegElems);
         }
         const bf16x8 a = f[kk % (kPF + 1)];
-        S = mfma16x16x32(a, QA[kk], S);
-        if (kk < 16) dP = mfma16x16x32(a, dOA[kk], dP);
+        S = F::mma(a, QA[kk], S);
+        if (kk < 16) dP = F::mma(a, dOA[kk], dP);
         if (b == 1 && kk == 2) softmax_grad(0, Sh0, Ph0);
       }
       if constexpr (PB) {
@@ -592,10 +638,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) dQ[c * 4 + hb] = mfma16x16x32(fa[c % (kPF + 1)], bt[hb], dQ[c * 4 + hb]);
+        for (int hb = 0; hb < 4; ++hb) dQ[c * 4 + hb] = F::mma(fa[c % (kPF + 1)], bt[hb], dQ[c * 4 + hb]);
       }
     }
   };
+  for (int pos0 = 0; pos0 < npos; pos0 += kMaxPos) {
+  if (pos0 > 0) {
+    // the next pass of positions: the previous pass's loads into the tile
+    // buffers have landed and every wave is done with its rows, positions,
+    // tiles and exchange before they are rewritten
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    cnt = compact_positions_batched<kMaxPos / 256>(p, s, irow, min(kMaxPos, npos - pos0), sm.rows, sm.wave, sm.vpos,
+                                                   len, pos0);
+    ntiles = (cnt + kNT - 1) / kNT;
+    if (ntiles > 0) gather_tile(p, sm, sm.kv, 0, cnt, g, wv, lane);
+  }
   if (ntiles > 0) step(std::false_type{}, sm.kv, sm.kv + kTileElems, 0);
   for (int it = 1; it < ntiles; ++it) {
     const bf16* b0 = sm.kv + (it & 1) * kTileElems;
@@ -603,7 +661,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     step(std::true_type{}, b0, b1, it);
   }
 
-  // phase B of the last tile
+  // phase B of the pass's last tile
   if (ntiles > 0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -628,6 +686,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
       }
     }
   }
+  }   // passes of positions
   // no direct load may still be writing this workgroup's LDS when it ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -637,10 +696,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   for (int c = 0; c < 9; ++c) {
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
+      if (hb * 16 + l16 >= gh) continue;   // a missing head
       bf16* dq = w.dq + ((size_t)t * p.Hq + h0 + hb * 16 + l16) * kDQK + col_block(c) + lq * 4;
-      const f32x4 v = dQ[c * 4 + hb];
+      const f32x4 v = dQ[c * 4 + hb] * kInvX;
       typedef short i16x4v __attribute__((ext_vector_type(4)));
-      i16x4v o = {bf16_bits((bf16)v[0]), bf16_bits((bf16)v[1]), bf16_bits((bf16)v[2]), bf16_bits((bf16)v[3])};
+      i16x4v o = {bf16_bits(F::to16(v[0])), bf16_bits(F::to16(v[1])), bf16_bits(F::to16(v[2])),
+                  bf16_bits(F::to16(v[3]))};
       *reinterpret_cast<i16x4v*>(dq) = o;
     }
   }
@@ -648,30 +709,41 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
 
 }  // namespace
 
+// Heads per kv head from which the 64-head kernel (with the missing heads of
+// its last group masked) serves a request: any count.  It computes all 64
+// heads of a group, but gathers each row and writes each partial row once
+// per group, and measured 4.3x faster than the 16-head row kernel even for
+// one head (MLA 8K shape: 5.96 against 25.7 ms).
+constexpr int kMinHeads = 1;
+
 bool mla_bwd_supported(const Params& p) {
-  return !p.fp16 && p.shared && p.dqk == kDQK && p.dv == kDV && p.G % kHeads == 0 && p.select != kSelBlock &&
-         (p.select == kSelToken ? p.topk : p.win_left + 1 + p.win_right + p.topk) <= kMaxPos;
+  return p.shared && p.dqk == kDQK && p.dv == kDV && p.G >= kMinHeads && p.select != kSelBlock;
 }
 
-int mla_bwd_head_groups(const Params& p) { return p.G / kHeads; }
+int mla_bwd_head_groups(const Params& p) { return (p.G + kHeads - 1) / kHeads; }
 
-hipError_t launch_bwd_mla(const Params& p, const BwdBuffers& w, hipStream_t s) {
-  dim3 grid((unsigned)(w.Tc * p.Hkv), (unsigned)(p.G / kHeads));
+template <typename E>
+hipError_t launch_bwd_mla_t(const Params& p, const BwdBuffers& w, hipStream_t s) {
+  dim3 grid((unsigned)(w.Tc * p.Hkv), (unsigned)mla_bwd_head_groups(p));
   const bool l1 = w.l1 != nullptr;
   switch (w.out) {
     case kOutAtomic:
-      if (l1) hipLaunchKernelGGL((mla_bwd_kernel<true, kOutAtomic>), grid, dim3(kThreads), 0, s, p, w);
-      else hipLaunchKernelGGL((mla_bwd_kernel<false, kOutAtomic>), grid, dim3(kThreads), 0, s, p, w);
+      if (l1) hipLaunchKernelGGL((mla_bwd_kernel<E, true, kOutAtomic>), grid, dim3(kThreads), 0, s, p, w);
+      else hipLaunchKernelGGL((mla_bwd_kernel<E, false, kOutAtomic>), grid, dim3(kThreads), 0, s, p, w);
       break;
     case kOutAtomicXcd:
-      if (l1) hipLaunchKernelGGL((mla_bwd_kernel<true, kOutAtomicXcd>), grid, dim3(kThreads), 0, s, p, w);
-      else hipLaunchKernelGGL((mla_bwd_kernel<false, kOutAtomicXcd>), grid, dim3(kThreads), 0, s, p, w);
+      if (l1) hipLaunchKernelGGL((mla_bwd_kernel<E, true, kOutAtomicXcd>), grid, dim3(kThreads), 0, s, p, w);
+      else hipLaunchKernelGGL((mla_bwd_kernel<E, false, kOutAtomicXcd>), grid, dim3(kThreads), 0, s, p, w);
       break;
     default:
-      if (l1) hipLaunchKernelGGL((mla_bwd_kernel<true, kOutPartial>), grid, dim3(kThreads), 0, s, p, w);
-      else hipLaunchKernelGGL((mla_bwd_kernel<false, kOutPartial>), grid, dim3(kThreads), 0, s, p, w);
+      if (l1) hipLaunchKernelGGL((mla_bwd_kernel<E, true, kOutPartial>), grid, dim3(kThreads), 0, s, p, w);
+      else hipLaunchKernelGGL((mla_bwd_kernel<E, false, kOutPartial>), grid, dim3(kThreads), 0, s, p, w);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_mla(const Params& p, const BwdBuffers& w, hipStream_t s) {
+  return p.fp16 ? launch_bwd_mla_t<f16>(p, w, s) : launch_bwd_mla_t<bf16>(p, w, s);
 }
 
 }  // namespace sa

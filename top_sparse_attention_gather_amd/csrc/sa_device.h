@@ -200,19 +200,21 @@ __device__ __forceinline__ int compact_positions(const Params& p, const SeqPos& 
   return total;
 }
 
-// Same result as compact_positions for n <= 256 * ROUNDS, with every
-// position decoded (and its index loaded) before the first ballot, so the
-// index loads overlap instead of costing one round trip per round.
+// Same result as compact_positions for positions [pos0, pos0 + n), n <=
+// 256 * ROUNDS, with every position decoded (and its index loaded) before
+// the first ballot, so the index loads overlap instead of costing one round
+// trip per round.  sVpos receives the positions themselves (pos0 + i).
 template <int ROUNDS>
 __device__ __forceinline__ int compact_positions_batched(const Params& p, const SeqPos& s,
                                                          const int* __restrict__ irow, int n, int* sRows,
-                                                         int* sWave, int* sVpos, int len = 0x7fffffff) {
+                                                         int* sWave, int* sVpos, int len = 0x7fffffff,
+                                                         int pos0 = 0) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int code[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int pos = r * 256 + tid;
-    code[r] = pos < n ? decode_position(p, s, irow, pos, len) : -1;
+    code[r] = pos < n ? decode_position(p, s, irow, pos0 + pos, len) : -1;
   }
   int total = 0;
 #pragma unroll
@@ -226,7 +228,7 @@ __device__ __forceinline__ int compact_positions_batched(const Params& p, const 
     for (int i = 0; i < w; ++i) off += sWave[i];
     if (code[r] >= 0) {
       sRows[off + before] = code[r];
-      sVpos[off + before] = r * 256 + tid;
+      sVpos[off + before] = pos0 + r * 256 + tid;
     }
     total += sWave[0] + sWave[1] + sWave[2] + sWave[3];
     __syncthreads();

@@ -260,6 +260,10 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
   const int row = blockIdx.x;
   const int t = row / p.Hkv, g = row - t * p.Hkv;
   const int h0 = g * p.G + blockIdx.y * kHeads + wv * 16;   // the wave's first head
+  // heads of this group present (the last group may hold fewer than 64: the
+  // missing ones repeat a present head's Q and are not stored)
+  const int gh = min(kHeads, p.G - (int)blockIdx.y * kHeads);
+  const int hq = g * p.G + blockIdx.y * kHeads + min(wv * 16 + l16, gh - 1);   // lane's head, clamped
   const SeqPos s = seq_pos(p, t);
   const int* irow = p.idx + (size_t)row * p.topk;
   const E* Kg = reinterpret_cast<const E*>(p.k);
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
   // Q of head h0 + l16, columns 32kk + 8lq .. +7 (B operand of S^T)
   V8 q[kD / 32];
   {
-    const E* qrow = reinterpret_cast<const E*>(p.q) + ((size_t)t * p.Hq + h0 + l16) * kD + lq * 8;
+    const E* qrow = reinterpret_cast<const E*>(p.q) + ((size_t)t * p.Hq + hq) * kD + lq * 8;
 #pragma unroll
     for (int kk = 0; kk < kD / 32; ++kk) q[kk] = *reinterpret_cast<const V8*>(qrow + kk * 32);
     // wait for Q here: the compiler does not count the direct loads below,
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
   }
   // running max (log2 units) and sum of head h0 + l16
   const bool sk = p.has_sinks;
-  float m_run = sk ? p.sinks[h0 + l16] * 1.4426950408889634f : -INFINITY;
+  float m_run = sk ? p.sinks[hq] * 1.4426950408889634f : -INFINITY;
   float l_run = sk ? 1.f : 0.f;
   f32x4 acc[kDV / 16];
 #pragma unroll
@@ -402,8 +406,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restri
   for (int c = 0; c < kDV / 16; ++c)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      out_o[((size_t)t * p.Hq + h0 + lq * 4 + i) * kDV + c * 16 + l16] = (E)(acc[c][i] * linv[i]);
-  if (lq == 0)
+      if (wv * 16 + lq * 4 + i < gh)
+        out_o[((size_t)t * p.Hq + h0 + lq * 4 + i) * kDV + c * 16 + l16] = (E)(acc[c][i] * linv[i]);
+  if (lq == 0 && wv * 16 + l16 < gh)
     out_lse[(size_t)t * p.Hq + h0 + l16] =
         l_run > 0.f ? m_run * 0.6931471805599453f + __logf(l_run) : -INFINITY;
 }
@@ -426,8 +431,10 @@ bool fwd_rows_supported(int dqk, int dv, int shared) {
 }
 
 hipError_t launch_fwd_rows(const Params& p, void* o, float* lse, hipStream_t s) {
-  if (p.dqk == 576 && p.dv == 512 && p.shared && p.G % mla_fwd::kHeads == 0) {
-    const dim3 grid((unsigned)(p.T * p.Hkv), (unsigned)(p.G / mla_fwd::kHeads));
+  // 64 heads per workgroup from 16 heads per kv head up (the last group's
+  // missing heads masked); fewer heads go to the 16-head row kernel
+  if (p.dqk == 576 && p.dv == 512 && p.shared && p.G >= 16) {
+    const dim3 grid((unsigned)(p.T * p.Hkv), (unsigned)((p.G + mla_fwd::kHeads - 1) / mla_fwd::kHeads));
     if (p.fp16)
       hipLaunchKernelGGL(fwd_mla_kernel<f16>, grid, dim3(kThreads), 0, s, p, static_cast<f16*>(o), lse);
     else
