@@ -46,8 +46,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     ("mla_token_8k", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
-        "sha256": "bd5fe81f12724817e0ff7ba51034c3534d3a9cf92527330caa06f3e7d4d3dd34",
-        "fetch_bytes": 8163138173, "write_bytes": 17521873056,
+        "sha256": "46c75607c6aa74130e627a0005077474d522b16ea7f0654306ca4b0d7b4f02ee",
+        "fetch_bytes": 8390663602, "write_bytes": 17525839872,
     },
     ("indexer_8k", "idx"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_indexer.hip",
@@ -56,8 +56,13 @@ MEASURED_TRAFFIC = {
     },
     ("mla_token_8k", "fwd"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_fwd_rows.hip",
-        "sha256": "700634eaa3f72e5cb3688b1fb892ff7124fd67af5abae81062eb97f8f196528a",
-        "fetch_bytes": 5255923790, "write_bytes": 538968064,
+        "sha256": "5d440ea41a4fd8707b9475cdd9b9fcfd598e4c53811fe6475f88a21e5564859d",
+        "fetch_bytes": 5274537480, "write_bytes": 538968064,
+    },
+    ("nsa_block_gqa", "deterministic"): {
+        "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_blk.hip",
+        "sha256": "b1c1bbe1179b355006edb58d36b6a36790e60f7f356ca8d5094c052d4e36502e",
+        "fetch_bytes": 103938179, "write_bytes": 33554432,
     },
 }
 
@@ -161,20 +166,27 @@ def block_pairs(wl: W.Workload, idx: np.ndarray) -> int:
 def main_kernel_roofline(wl: W.Workload, mode: str, idx: np.ndarray, flop: int, kern_ms: float):
     """Roofline of the dominant kernel: the MFMA row kernel (selected-KV
     FLOP / its time against the bf16 peak), or for block selection in
-    deterministic mode the dQ pass over the selected blocks, bound by the
-    block gathers (algorithmic bytes / its time against HBM, every gathered
-    row counted as if it came from HBM; the K/V of this shape is 4 MB and is
-    in fact served from L2, so the fraction can exceed 1)."""
+    deterministic mode the dQ pass over the selected blocks against HBM: its
+    algorithmic HBM bytes are every input it needs read once (Q, dO, lse, D,
+    the K/V rows, the indices) and dQ written once.  The selected blocks'
+    rows are gathered again for every query (the gathered-row bytes, also
+    reported with their rate), but the K/V of this shape is 4 MB and those
+    re-reads come from L2, so HBM does not bound the kernel: the rate of its
+    direct global->LDS block loads does."""
     if wl.select == W.SEL_BLOCK and mode == "deterministic":
         pairs = W.expected_pair_count(wl)
-        T, H = wl.total_q, wl.n_q_heads
+        T, H, Hkv = wl.total_q, wl.n_q_heads, wl.n_kv_heads
         nbytes = (T * H * (wl.d_qk + wl.d_v) * 2               # Q and dO read once
                   + T * H * 8                                   # lse and D
-                  + pairs * (wl.d_qk + wl.d_v) * 2              # gathered K and V rows
+                  + wl.total_kv * Hkv * (wl.d_qk + wl.d_v) * 2  # K and V read once
+                  + int(idx.size) * 4                           # indices
                   + T * H * wl.d_qk * 2)                        # dQ written
+        gathered = pairs * (wl.d_qk + wl.d_v) * 2
         gbs = nbytes / (kern_ms * 1e-3) / 1e9
         return {"kernel": "blk_dq_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
+                "gathered_row_bytes": gathered,
+                "gathered_row_rate_gbs": round(gathered / (kern_ms * 1e-3) / 1e9, 1),
                 "block_pairs": block_pairs(wl, idx)}
     tf = flop / (kern_ms * 1e-3) / 1e12
     mla = wl.kv_shared and (wl.d_qk, wl.d_v) == (576, 512) and wl.select != W.SEL_BLOCK
