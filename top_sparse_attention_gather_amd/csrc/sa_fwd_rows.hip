@@ -188,28 +188,38 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
 // rows of one (token, kv head) are gathered once for all 64 heads (the
 // generic kernel above gathers them once per 16-head chunk).
 //
-// Wave w owns heads 16w..16w+15.  Per tile of kRows rows it forms S^T =
-// K Q^T (16x16x32 MFMA, K from LDS, Q resident in registers), so that each
-// lane holds one head's logits for 4 consecutive rows of each 16-row block:
-// with two blocks side by side that is an A operand of the 16x16x32 MFMA,
-// so P = exp(S - m) feeds O += P V straight from registers.  V is the first
-// 512 columns of the same LDS rows, read as B operands by transposing LDS
-// reads.  The running max and sum of a
-// head live in the 4 lanes of its column (log2 domain); a sink logit
-// starts them at (sink, 1).  Tiles come by direct global->LDS loads, the
-// next one issued while the current one is computed (two buffers: on the
-// 8192-token top-2048 shape, loads issued two or three tiles ahead measured
-// no faster).
+// 8 waves in two roles, two per SIMD, pipelined over the row's tiles of
+// kRows rows (three tile buffers):
+//  - softmax waves 0..3, wave w with heads 16w..16w+15, at stage st:
+//    S^T = K Q^T for tile st (16x16x32 MFMA, K from LDS, Q resident in
+//    registers), each lane holding one head's logits for 4 rows of each
+//    16-row block; the online softmax (running max and sum of a head in the
+//    4 lanes of its column, log2 domain, a sink logit starting them at
+//    (sink, 1)); P = exp(S - m) to an LDS exchange [head][k-slot] in the
+//    row order an A operand of the 16x16x32 MFMA wants, the rescale factor
+//    of each head beside it; and the direct global->LDS loads of tile
+//    st + 1;
+//  - P.V waves 4..7, wave 4 + c with O columns 128c..128c+127 of all 64
+//    heads, at stage st: O = O alpha + P V for tile st - 1, with P from the
+//    exchange and V^T from transposing LDS reads of the wave's columns only.
+// Splitting O by columns makes every V^T element read once per tile instead
+// of once per 16 heads, which bounded the single-role form (each of 4 waves
+// reading the whole V^T for its 16 heads: 6.3-6.5 ms on the 8192-token
+// top-2048 shape).
 namespace mla_fwd {
 constexpr int kD = 576, kDV = 512;
 constexpr int kKS = kD + 8;                    // LDS row stride (elements)
-constexpr int kRows = 32;                      // rows per tile (a multiple of 32)
-constexpr int kNB = kRows / 16;                // 16-row blocks per tile
+constexpr int kRows = 32;                      // rows per tile (one 16x16x32 K step of P V)
 constexpr int kHeads = 64;                     // query heads per workgroup
+constexpr int kWaves = 8;                      // 4 softmax waves, 4 P.V waves
+constexpr int kThreadsF = kWaves * 64;
+constexpr int kBufs = 3;                       // tiles in LDS: P.V reads st - 1, softmax st, loads st + 1
 constexpr int kCompact = 1024;                 // positions compacted at a time
 constexpr int kRowChunks = kKS / 8;            // 16-byte chunks per LDS row (the last one padding)
 constexpr int kTileChunks = kRows * kRowChunks;
-static_assert(kRows % 32 == 0 && kCompact % kRows == 0, "tile shape");
+constexpr int kPS = kRows + 8;                 // P exchange row stride (elements)
+constexpr int kColsPV = kDV / 4;               // O columns per P.V wave
+static_assert(kCompact % kRows == 0, "tile shape");
 }  // namespace mla_fwd
 
 typedef __attribute__((address_space(3))) i16x4 fwd_lds_i16x4;
@@ -247,170 +257,216 @@ __device__ __forceinline__ float add_xor32(float x) {
 }
 
 template <typename E>
-__global__ __launch_bounds__(kThreads) void fwd_mla_kernel(Params p, E* __restrict__ out_o,
-                                                           float* __restrict__ out_lse) {
+__global__ __launch_bounds__(mla_fwd::kThreadsF, 1) void fwd_mla_kernel(Params p, E* __restrict__ out_o,
+                                                                       float* __restrict__ out_lse) {
   using namespace mla_fwd;
   typedef typename Elem<E>::V8 V8;
-  __shared__ __attribute__((aligned(16))) E sK[2][kRows * kKS];
+  __shared__ __attribute__((aligned(16))) E sK[kBufs][kRows * kKS];
+  __shared__ __attribute__((aligned(16))) E sP[2][kHeads * kPS];   // P of a tile, [head][k-slot]
+  __shared__ float sAl[2][kHeads];                                  // its rescale factor per head
+  __shared__ int sFl[2][4];                                         // per head block: any factor != 1
+  __shared__ float sL[kHeads];                                      // final softmax sum per head
   __shared__ int sRows[kCompact];
-  __shared__ int sWave[4];
+  __shared__ int sWave[kWaves];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lq = lane >> 4;
   const int row = blockIdx.x;
   const int t = row / p.Hkv, g = row - t * p.Hkv;
-  const int h0 = g * p.G + blockIdx.y * kHeads + wv * 16;   // the wave's first head
+  const int hg = g * p.G + blockIdx.y * kHeads;                     // the group's first head
   // heads of this group present (the last group may hold fewer than 64: the
   // missing ones repeat a present head's Q and are not stored)
   const int gh = min(kHeads, p.G - (int)blockIdx.y * kHeads);
-  const int hq = g * p.G + blockIdx.y * kHeads + min(wv * 16 + l16, gh - 1);   // lane's head, clamped
   const SeqPos s = seq_pos(p, t);
   const int* irow = p.idx + (size_t)row * p.topk;
   const E* Kg = reinterpret_cast<const E*>(p.k);
   const E* Cg = reinterpret_cast<const E*>(p.cmp);
-  const float sl2 = p.scale * 1.4426950408889634f;   // scale * log2(e)
-
-  // Q of head h0 + l16, columns 32kk + 8lq .. +7 (B operand of S^T)
-  V8 q[kD / 32];
-  {
-    const E* qrow = reinterpret_cast<const E*>(p.q) + ((size_t)t * p.Hq + hq) * kD + lq * 8;
-#pragma unroll
-    for (int kk = 0; kk < kD / 32; ++kk) q[kk] = *reinterpret_cast<const V8*>(qrow + kk * 32);
-    // wait for Q here: the compiler does not count the direct loads below,
-    // so a wait for Q inside the tile loop would not be one it could place
-#pragma unroll
-    for (int kk = 0; kk < kD / 32; ++kk) asm volatile("" ::"v"(q[kk]));
-  }
-  // running max (log2 units) and sum of head h0 + l16
-  const bool sk = p.has_sinks;
-  float m_run = sk ? p.sinks[hq] * 1.4426950408889634f : -INFINITY;
-  float l_run = sk ? 1.f : 0.f;
-  f32x4 acc[kDV / 16];
-#pragma unroll
-  for (int c = 0; c < kDV / 16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int npos = n_positions(p);
+  const int len = row_len(p, row);
 
   auto src_of = [&](int code) -> const E* {
     return (code & kCmpFlag) ? Cg + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * kD : Kg + ((size_t)code * p.Hkv + g) * kD;
   };
-  // rows k0 .. k0 + kRows - 1 of the compacted list into `buf` by direct loads;
-  // rows past cnt repeat row cnt - 1 (finite values, masked out of S), the
-  // padding chunk of each LDS row repeats its first chunk
-  auto issue_tile = [&](int k0, int cnt, E* buf) {
+  // positions [pos0, pos0 + n) of the row compacted into sRows over all 8
+  // waves, in position order (same code and barriers in both roles)
+  auto compact = [&](int pos0, int n) -> int {
+    int total = 0;
+    for (int base = 0; base < n; base += kThreadsF) {
+      const int pos = base + tid;
+      const int code = pos < n ? decode_position(p, s, irow, pos0 + pos, len) : -1;
+      const unsigned long long m = __ballot(code >= 0);
+      const int before = __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == 0) sWave[wv] = __popcll(m);
+      __syncthreads();
+      int off = total;
+      for (int i = 0; i < wv; ++i) off += sWave[i];
+      if (code >= 0) sRows[off + before] = code;
+      for (int i = 0; i < kWaves; ++i) total += sWave[i];
+      __syncthreads();
+    }
+    return total;
+  };
+  // one barrier per stage: every softmax wave's loads of the stage's tile
+  // have landed, the exchange of the previous stage is written, and the
+  // buffers the P.V waves read at the previous stage are free
+  auto stage_barrier = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  if (wv < 4) {
+    // ---- softmax waves: heads hg + 16 wv + l16 --------------------------
+    const int hl = wv * 16 + l16;                       // the lane's head in the group
+    const int hq = hg + min(hl, gh - 1);                // clamped to a present head
+    const float sl2 = p.scale * 1.4426950408889634f;    // scale * log2(e)
+    // rows k0 .. k0 + kRows - 1 of the compacted list into `buf` by direct
+    // loads (the softmax waves issue them); rows past cnt repeat row cnt - 1
+    // (finite values, masked out of S), the padding chunk of each LDS row
+    // repeats its first chunk
+    auto issue_tile = [&](int k0, int cnt, E* buf) {
 #pragma unroll
-    for (int j = 0; j < (kTileChunks + kThreads - 1) / kThreads; ++j) {
-      const int c0 = (j * 4 + wv) * 64;
-      if (c0 < kTileChunks) {
-        const int c = c0 + lane;
-        if (c < kTileChunks) {
-          const int r = c / kRowChunks, ch = c - r * kRowChunks;
-          const E* src = src_of(sRows[min(k0 + r, cnt - 1)]) + (ch < kD / 8 ? ch : 0) * 8;
-          fwd_load_lds16(src, buf + c0 * 8);
+      for (int j = 0; j < (kTileChunks / 64 + 4) / 4; ++j) {
+        const int c0 = (j * 4 + wv) * 64;
+        if (c0 < kTileChunks) {
+          const int c = c0 + lane;
+          if (c < kTileChunks) {
+            const int r = c / kRowChunks, ch = c - r * kRowChunks;
+            const E* src = src_of(sRows[min(k0 + r, cnt - 1)]) + (ch < kD / 8 ? ch : 0) * 8;
+            fwd_load_lds16(src, buf + c0 * 8);
+          }
         }
+      }
+    };
+    // Q of the lane's head, columns 32kk + 8lq .. +7 (B operand of S^T)
+    V8 q[kD / 32];
+    {
+      const E* qrow = reinterpret_cast<const E*>(p.q) + ((size_t)t * p.Hq + hq) * kD + lq * 8;
+#pragma unroll
+      for (int kk = 0; kk < kD / 32; ++kk) q[kk] = *reinterpret_cast<const V8*>(qrow + kk * 32);
+      // wait for Q here: the compiler does not count the direct loads below,
+      // so a wait for Q inside the tile loop would not be one it could place
+#pragma unroll
+      for (int kk = 0; kk < kD / 32; ++kk) asm volatile("" ::"v"(q[kk]));
+    }
+    const bool sk = p.has_sinks;
+    float m_run = sk ? p.sinks[hq] * 1.4426950408889634f : -INFINITY;
+    float l_run = sk ? 1.f : 0.f;
+    for (int pos0 = 0; pos0 < npos; pos0 += kCompact) {
+      __syncthreads();   // the previous pass's rows and tiles are no longer read
+      const int cnt = compact(pos0, min(kCompact, npos - pos0));
+      const int ntiles = (cnt + kRows - 1) / kRows;
+      if (ntiles > 0) issue_tile(0, cnt, sK[0]);
+      for (int st = 0; st <= ntiles; ++st) {
+        stage_barrier();
+        if (st + 1 < ntiles) issue_tile((st + 1) * kRows, cnt, sK[(st + 1) % kBufs]);
+        if (st == ntiles) continue;
+        const int k0 = st * kRows;
+        const E* kb = sK[st % kBufs];
+        // S^T for rows k0 + 16b + 4lq + i (i < 4), head hl
+        float sv[2][4];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const E* arow = kb + (b * 16 + l16) * kKS + lq * 8;
+#pragma unroll
+          for (int kk = 0; kk < kD / 32; ++kk)
+            acc = Elem<E>::mma32(*reinterpret_cast<const V8*>(arow + kk * 32), q[kk], acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[b][i] = (k0 + b * 16 + lq * 4 + i < cnt) ? acc[i] * sl2 : -INFINITY;
+        }
+        float mx = sv[0][0];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[b][i]);
+        mx = max_xor32(max_xor16(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const float base = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - base);
+        V8 pv;
+        float sum = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pr = __builtin_amdgcn_exp2f(sv[b][i] - base);
+            sum += pr;
+            pv[b * 4 + i] = (E)pr;
+          }
+        sum = add_xor32(add_xor16(sum));
+        l_run = l_run * alpha + sum;
+        m_run = m_new;
+        // k-slot 8lq + 4b + i of head hl holds row 16b + 4lq + i: the order
+        // of the transposing V reads of the P.V waves
+        *reinterpret_cast<V8*>(&sP[st & 1][hl * kPS + lq * 8]) = pv;
+        if (lq == 0) sAl[st & 1][hl] = alpha;
+        const bool moved = __ballot(alpha != 1.f) != 0ull;
+        if (lane == 0) sFl[st & 1][wv] = moved ? 1 : 0;
       }
     }
-  };
-  // every wave's loads of tile it are done (the tile is complete) and tile
-  // it - 1 is no longer read, so its buffer takes tile it + 1
-  auto wait_tile = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-
-  const int npos = n_positions(p);
-  for (int pos0 = 0; pos0 < npos; pos0 += kCompact) {
-    __syncthreads();   // the previous chunk's rows and tiles are no longer read
-    const int cnt =
-        compact_positions(p, s, irow, pos0, min(kCompact, npos - pos0), sRows, sWave, nullptr, row_len(p, row));
-    const int ntiles = (cnt + kRows - 1) / kRows;
-    if (ntiles == 0) continue;
-    issue_tile(0, cnt, sK[0]);
-    for (int it = 0; it < ntiles; ++it) {
-      const int k0 = it * kRows;
-      const E* kb = sK[it & 1];
-      wait_tile();
-      if (it + 1 < ntiles) issue_tile(k0 + kRows, cnt, sK[(it + 1) & 1]);
-
-      // S^T for rows k0 + 16b + 4lq + i (i < 4), head h0 + l16
-      float sv[kNB][4];
+    if (lq == 0) sL[hl] = l_run;
+    __syncthreads();
+    if (lq == 0 && hl < gh)
+      out_lse[(size_t)t * p.Hq + hg + hl] = l_run > 0.f ? m_run * 0.6931471805599453f + __logf(l_run) : -INFINITY;
+  } else {
+    // ---- P.V waves: O columns c0 .. c0 + kColsPV - 1 of all 64 heads ------
+    const int c0 = (wv - 4) * kColsPV;
+    f32x4 acc[4][kColsPV / 16];
 #pragma unroll
-      for (int b = 0; b < kNB; ++b) {
-        f32x4 st = {0.f, 0.f, 0.f, 0.f};
-        const E* arow = kb + (b * 16 + l16) * kKS + lq * 8;
+    for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-        for (int kk = 0; kk < kD / 32; ++kk)
-          st = Elem<E>::mma32(*reinterpret_cast<const V8*>(arow + kk * 32), q[kk], st);
+      for (int c = 0; c < kColsPV / 16; ++c) acc[hb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int pos0 = 0; pos0 < npos; pos0 += kCompact) {
+      __syncthreads();
+      const int cnt = compact(pos0, min(kCompact, npos - pos0));
+      const int ntiles = (cnt + kRows - 1) / kRows;
+      for (int st = 0; st <= ntiles; ++st) {
+        stage_barrier();
+        if (st == 0) continue;
+        const int ts = st - 1;                  // the tile whose P the softmax waves wrote
+        const E* kb = sK[ts % kBufs];
+        const E* pb = sP[ts & 1];
+        // O rows are heads 16hb + 4lq + i: rescale by their factors (a
+        // block whose heads' maxima did not move keeps its rows: factor 1)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[b][i] = (k0 + b * 16 + lq * 4 + i < cnt) ? st[i] * sl2 : -INFINITY;
-      }
-      // online softmax over the tile's rows (the 4 lanes of head l16)
-      float mx = sv[0][0];
+        for (int hb = 0; hb < 4; ++hb) {
+          if (sFl[ts & 1][hb]) {
+            f32x4 al;
 #pragma unroll
-      for (int b = 0; b < kNB; ++b)
+            for (int i = 0; i < 4; ++i) al[i] = sAl[ts & 1][hb * 16 + lq * 4 + i];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[b][i]);
-      mx = max_xor32(max_xor16(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float base = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-      float pr[kNB][4];
-      float sum = 0.f;
-#pragma unroll
-      for (int b = 0; b < kNB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[b][i] = __builtin_amdgcn_exp2f(sv[b][i] - base);
-          sum += pr[b][i];
+            for (int c = 0; c < kColsPV / 16; ++c) acc[hb][c] = acc[hb][c] * al;
+          }
         }
-      sum = add_xor32(add_xor16(sum));
-      l_run = l_run * alpha + sum;
-      m_run = m_new;
-      // O rows are heads 4lq + i: their rescale factors from lanes 4lq + i
-      // (skipped when no head's max moved: the factors are then exactly 1)
-      if (__ballot(alpha != 1.f)) {
-        f32x4 al;
+        V8 pa[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, lq * 4 + i);
+        for (int hb = 0; hb < 4; ++hb) pa[hb] = *reinterpret_cast<const V8*>(&pb[(hb * 16 + l16) * kPS + lq * 8]);
+        // B = V^T of 16 columns: k-slot 8lq + j is row 4lq + j (j < 4) or
+        // 12 + 4lq + j, from two transposing reads (rows 4lq + l16/4 and
+        // 16 + 4lq + l16/4, columns 4(l16 % 4) of the block)
+        const E* vrow = kb + (lq * 4 + (l16 >> 2)) * kKS + c0 + (l16 & 3) * 4;
 #pragma unroll
-        for (int c = 0; c < kDV / 16; ++c) acc[c] = acc[c] * al;
-      }
-      // O += P V, one 16x16x32 MFMA per 16 columns and 32 rows: k-slot
-      // 8lq + j stands for row 4lq + j of the step's first 16-row block
-      // (j < 4) or row 12 + 4lq + j of its second, in A (P of head l16) and
-      // in B alike; B = V^T from two transposing reads (rows 16b + 4lq +
-      // l16/4, columns 16c + 4(l16 % 4))
-#pragma unroll
-      for (int ks = 0; ks < kNB / 2; ++ks) {   // 32 rows (two 16-row blocks) per MFMA
-        V8 pa;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pa[i] = (E)pr[2 * ks][i];
-          pa[4 + i] = (E)pr[2 * ks + 1][i];
-        }
-        const E* vrow = kb + (32 * ks + lq * 4 + (l16 >> 2)) * kKS + (l16 & 3) * 4;
-#pragma unroll
-        for (int c = 0; c < kDV / 16; ++c) {
+        for (int c = 0; c < kColsPV / 16; ++c) {
           const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fwd_lds_i16x4*)(vrow + c * 16));
           const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fwd_lds_i16x4*)(vrow + 16 * kKS + c * 16));
           const fwd_i16x8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[c] = Elem<E>::mma32(pa, __builtin_bit_cast(V8, vb), acc[c]);
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) acc[hb][c] = Elem<E>::mma32(pa[hb], __builtin_bit_cast(V8, vb), acc[hb][c]);
         }
       }
     }
+    __syncthreads();   // the softmax waves' final sums are in sL
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = hb * 16 + lq * 4 + i;
+        if (h >= gh) continue;
+        const float l = sL[h];
+        const float linv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int c = 0; c < kColsPV / 16; ++c)
+          out_o[((size_t)t * p.Hq + hg + h) * kDV + c0 + c * 16 + l16] = (E)(acc[hb][c][i] * linv);
+      }
   }
-
-  // O = acc / l for heads h0 + 4lq + i; lse of head h0 + l16
-  float linv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float l = __shfl(l_run, lq * 4 + i);
-    linv[i] = l > 0.f ? 1.f / l : 0.f;
-  }
-#pragma unroll
-  for (int c = 0; c < kDV / 16; ++c)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (wv * 16 + lq * 4 + i < gh)
-        out_o[((size_t)t * p.Hq + h0 + lq * 4 + i) * kDV + c * 16 + l16] = (E)(acc[c][i] * linv[i]);
-  if (lq == 0 && wv * 16 + l16 < gh)
-    out_lse[(size_t)t * p.Hq + h0 + l16] =
-        l_run > 0.f ? m_run * 0.6931471805599453f + __logf(l_run) : -INFINITY;
 }
 
 template <int DQK, int DV, bool SHARED>
@@ -436,9 +492,9 @@ hipError_t launch_fwd_rows(const Params& p, void* o, float* lse, hipStream_t s) 
   if (p.dqk == 576 && p.dv == 512 && p.shared && p.G >= 16) {
     const dim3 grid((unsigned)(p.T * p.Hkv), (unsigned)((p.G + mla_fwd::kHeads - 1) / mla_fwd::kHeads));
     if (p.fp16)
-      hipLaunchKernelGGL(fwd_mla_kernel<f16>, grid, dim3(kThreads), 0, s, p, static_cast<f16*>(o), lse);
+      hipLaunchKernelGGL(fwd_mla_kernel<f16>, grid, dim3(mla_fwd::kThreadsF), 0, s, p, static_cast<f16*>(o), lse);
     else
-      hipLaunchKernelGGL(fwd_mla_kernel<bf16>, grid, dim3(kThreads), 0, s, p, static_cast<bf16*>(o), lse);
+      hipLaunchKernelGGL(fwd_mla_kernel<bf16>, grid, dim3(mla_fwd::kThreadsF), 0, s, p, static_cast<bf16*>(o), lse);
     return hipGetLastError();
   }
   if (p.dqk == 64 && p.dv == 64) return p.shared ? launch_t<64, 64, true>(p, o, lse, s) : launch_t<64, 64, false>(p, o, lse, s);
