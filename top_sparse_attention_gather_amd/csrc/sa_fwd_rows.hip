@@ -321,18 +321,22 @@ __global__ __launch_bounds__(mla_fwd::kThreadsF, 1) void fwd_mla_kernel(Params p
     // loads (the softmax waves issue them); rows past cnt repeat row cnt - 1
     // (finite values, masked out of S), the padding chunk of each LDS row
     // repeats its first chunk
+    // (all source addresses first: the loads are asm statements that the
+    // compiler does not move LDS reads across, so reading each row number
+    // just before its load would wait out one LDS latency per load)
+    constexpr int kJ = (kTileChunks / 64 + 4) / 4;
     auto issue_tile = [&](int k0, int cnt, E* buf) {
+      const E* src[kJ];
 #pragma unroll
-      for (int j = 0; j < (kTileChunks / 64 + 4) / 4; ++j) {
+      for (int j = 0; j < kJ; ++j) {
+        const int c = (j * 4 + wv) * 64 + lane;
+        const int r = c / kRowChunks, ch = c - r * kRowChunks;
+        src[j] = src_of(sRows[min(k0 + r, cnt - 1)]) + (ch < kD / 8 ? ch : 0) * 8;
+      }
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
         const int c0 = (j * 4 + wv) * 64;
-        if (c0 < kTileChunks) {
-          const int c = c0 + lane;
-          if (c < kTileChunks) {
-            const int r = c / kRowChunks, ch = c - r * kRowChunks;
-            const E* src = src_of(sRows[min(k0 + r, cnt - 1)]) + (ch < kD / 8 ? ch : 0) * 8;
-            fwd_load_lds16(src, buf + c0 * 8);
-          }
-        }
+        if (c0 < kTileChunks && c0 + lane < kTileChunks) fwd_load_lds16(src[j], buf + c0 * 8);
       }
     };
     // Q of the lane's head, columns 32kk + 8lq .. +7 (B operand of S^T)
