@@ -211,7 +211,8 @@ constexpr int kD = 576, kDV = 512;
 constexpr int kKS = kD + 8;                    // LDS row stride (elements)
 constexpr int kRows = 32;                      // rows per tile (one 16x16x32 K step of P V)
 constexpr int kHeads = 64;                     // query heads per workgroup
-constexpr int kWaves = 8;                      // 4 softmax waves, 4 P.V waves
+constexpr int kLoaders = 4;                    // waves that only issue the tile loads (0: the softmax waves do)
+constexpr int kWaves = 8 + kLoaders;           // 4 softmax waves, 4 P.V waves, the loaders
 constexpr int kThreadsF = kWaves * 64;
 constexpr int kBufs = 3;                       // tiles in LDS: P.V reads st - 1, softmax st, loads st + 1
 constexpr int kCompact = 1024;                 // positions compacted at a time
@@ -311,34 +312,34 @@ __global__ __launch_bounds__(mla_fwd::kThreadsF, 1) void fwd_mla_kernel(Params p
   // have landed, the exchange of the previous stage is written, and the
   // buffers the P.V waves read at the previous stage are free
   auto stage_barrier = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // rows k0 .. k0 + kRows - 1 of the compacted list into `buf` by direct
+  // loads, issuing wave iw (of 4) taking the 64-chunk blocks iw, iw + 4, ...;
+  // rows past cnt repeat row cnt - 1 (finite values, masked out of S), the
+  // padding chunk of each LDS row repeats its first chunk.  All source
+  // addresses come first: the loads are asm statements that the compiler
+  // does not move LDS reads across, so reading each row number just before
+  // its load would wait out one LDS latency per load.
+  constexpr int kJ = (kTileChunks / 64 + 4) / 4;
+  auto issue_tile = [&](int iw, int k0, int cnt, E* buf) {
+    const E* src[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int c = (j * 4 + iw) * 64 + lane;
+      const int r = c / kRowChunks, ch = c - r * kRowChunks;
+      src[j] = src_of(sRows[min(k0 + r, cnt - 1)]) + (ch < kD / 8 ? ch : 0) * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int c0 = (j * 4 + iw) * 64;
+      if (c0 < kTileChunks && c0 + lane < kTileChunks) fwd_load_lds16(src[j], buf + c0 * 8);
+    }
+  };
 
   if (wv < 4) {
     // ---- softmax waves: heads hg + 16 wv + l16 --------------------------
     const int hl = wv * 16 + l16;                       // the lane's head in the group
     const int hq = hg + min(hl, gh - 1);                // clamped to a present head
     const float sl2 = p.scale * 1.4426950408889634f;    // scale * log2(e)
-    // rows k0 .. k0 + kRows - 1 of the compacted list into `buf` by direct
-    // loads (the softmax waves issue them); rows past cnt repeat row cnt - 1
-    // (finite values, masked out of S), the padding chunk of each LDS row
-    // repeats its first chunk
-    // (all source addresses first: the loads are asm statements that the
-    // compiler does not move LDS reads across, so reading each row number
-    // just before its load would wait out one LDS latency per load)
-    constexpr int kJ = (kTileChunks / 64 + 4) / 4;
-    auto issue_tile = [&](int k0, int cnt, E* buf) {
-      const E* src[kJ];
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        const int c = (j * 4 + wv) * 64 + lane;
-        const int r = c / kRowChunks, ch = c - r * kRowChunks;
-        src[j] = src_of(sRows[min(k0 + r, cnt - 1)]) + (ch < kD / 8 ? ch : 0) * 8;
-      }
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        const int c0 = (j * 4 + wv) * 64;
-        if (c0 < kTileChunks && c0 + lane < kTileChunks) fwd_load_lds16(src[j], buf + c0 * 8);
-      }
-    };
     // Q of the lane's head, columns 32kk + 8lq .. +7 (B operand of S^T)
     V8 q[kD / 32];
     {
@@ -357,10 +358,10 @@ __global__ __launch_bounds__(mla_fwd::kThreadsF, 1) void fwd_mla_kernel(Params p
       __syncthreads();   // the previous pass's rows and tiles are no longer read
       const int cnt = compact(pos0, min(kCompact, npos - pos0));
       const int ntiles = (cnt + kRows - 1) / kRows;
-      if (ntiles > 0) issue_tile(0, cnt, sK[0]);
+      if (kLoaders == 0 && ntiles > 0) issue_tile(wv, 0, cnt, sK[0]);
       for (int st = 0; st <= ntiles; ++st) {
         stage_barrier();
-        if (st + 1 < ntiles) issue_tile((st + 1) * kRows, cnt, sK[(st + 1) % kBufs]);
+        if (kLoaders == 0 && st + 1 < ntiles) issue_tile(wv, (st + 1) * kRows, cnt, sK[(st + 1) % kBufs]);
         if (st == ntiles) continue;
         const int k0 = st * kRows;
         const E* kb = sK[st % kBufs];
@@ -410,6 +411,19 @@ __global__ __launch_bounds__(mla_fwd::kThreadsF, 1) void fwd_mla_kernel(Params p
     __syncthreads();
     if (lq == 0 && hl < gh)
       out_lse[(size_t)t * p.Hq + hg + hl] = l_run > 0.f ? m_run * 0.6931471805599453f + __logf(l_run) : -INFINITY;
+  } else if (wv >= 8) {
+    // ---- loader waves: the direct loads of tile st + 1 at stage st --------
+    for (int pos0 = 0; pos0 < npos; pos0 += kCompact) {
+      __syncthreads();
+      const int cnt = compact(pos0, min(kCompact, npos - pos0));
+      const int ntiles = (cnt + kRows - 1) / kRows;
+      if (ntiles > 0) issue_tile(wv - 8, 0, cnt, sK[0]);
+      for (int st = 0; st <= ntiles; ++st) {
+        stage_barrier();
+        if (st + 1 < ntiles) issue_tile(wv - 8, (st + 1) * kRows, cnt, sK[(st + 1) % kBufs]);
+      }
+    }
+    __syncthreads();
   } else {
     // ---- P.V waves: O columns c0 .. c0 + kColsPV - 1 of all 64 heads ------
     const int c0 = (wv - 4) * kColsPV;
