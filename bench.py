@@ -408,7 +408,7 @@ def bench_forward(args):
         cpu = {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                "sample": f"fp64 numpy oracle sparse_fwd on the last {done} of {T} query tokens of {wl.name} "
                          f"({fl / 1e12:.3f} TFLOP in {spent:.1f} s)", **host_info()}
-    kernel = "fwd_mla_kernel" if (wl.d_qk, wl.d_v, wl.kv_shared) == (576, 512, True) and wl.group >= 16 \
+    kernel = "fwd_mla_kernel" if (wl.d_qk, wl.d_v, wl.kv_shared) == (576, 512, True) \
         else "fwd_rows_kernel"
     line = {
         "metric": "sparse-attn fwd TFLOP/s (selected-KV FLOPs), 1 GPU",

@@ -33,11 +33,11 @@ _ORACLE = {}
 
 
 @pytest.mark.parametrize("mode", list(MODES))
-@pytest.mark.parametrize("heads", [16, 48, 96])
+@pytest.mark.parametrize("heads", [1, 16, 48, 96])
 def test_bwd_mla_masked_heads(heads, mode):
-    """16 and 48 heads: one 64-head group with 48 and 16 heads masked; 96
-    heads: a full group and one with 32 masked.  Every output row, with the
-    softmax L1-norm outputs."""
+    """1, 16 and 48 heads: one 64-head group with 63, 48 and 16 heads
+    masked; 96 heads: a full group and one with 32 masked.  Every output row,
+    with the softmax L1-norm outputs."""
     wl = _mla(heads)
     if heads not in _ORACLE:
         _ORACLE.clear()
@@ -48,7 +48,7 @@ def test_bwd_mla_masked_heads(heads, mode):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("heads", [20, 48, 96])
+@pytest.mark.parametrize("heads", [1, 8, 20, 48, 96])
 def test_fwd_mla_masked_heads(heads, dtype):
     wl = _mla(heads, dtype=dtype)
     inp = W.make_inputs(wl)

@@ -188,8 +188,8 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
 // rows of one (token, kv head) are gathered once for all 64 heads (the
 // generic kernel above gathers them once per 16-head chunk).
 //
-// 8 waves in two roles, two per SIMD, pipelined over the row's tiles of
-// kRows rows (three tile buffers):
+// 12 waves in three roles, three per SIMD, pipelined over the row's tiles of
+// kRows rows (three tile buffers, one barrier per stage):
 //  - softmax waves 0..3, wave w with heads 16w..16w+15, at stage st:
 //    S^T = K Q^T for tile st (16x16x32 MFMA, K from LDS, Q resident in
 //    registers), each lane holding one head's logits for 4 rows of each
@@ -197,22 +197,25 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
 //    4 lanes of its column, log2 domain, a sink logit starting them at
 //    (sink, 1)); P = exp(S - m) to an LDS exchange [head][k-slot] in the
 //    row order an A operand of the 16x16x32 MFMA wants, the rescale factor
-//    of each head beside it; and the direct global->LDS loads of tile
-//    st + 1;
+//    of each head beside it;
 //  - P.V waves 4..7, wave 4 + c with O columns 128c..128c+127 of all 64
 //    heads, at stage st: O = O alpha + P V for tile st - 1, with P from the
-//    exchange and V^T from transposing LDS reads of the wave's columns only.
+//    exchange and V^T from transposing LDS reads of the wave's columns only;
+//  - loader waves 8..11: the direct global->LDS loads of tile st + 1.
 // Splitting O by columns makes every V^T element read once per tile instead
 // of once per 16 heads, which bounded the single-role form (each of 4 waves
 // reading the whole V^T for its 16 heads: 6.3-6.5 ms on the 8192-token
-// top-2048 shape).
+// top-2048 shape: 3.2 ms split).  A direct load waits at issue while the
+// CU's address unit works through the loads queued before it (the 37 of a
+// tile take it ~1700 cycles), so the waves that issue them do nothing else:
+// issued by the softmax waves the loads held each stage's S^T back (3.2 ->
+// 2.8 ms with loader waves).
 namespace mla_fwd {
 constexpr int kD = 576, kDV = 512;
 constexpr int kKS = kD + 8;                    // LDS row stride (elements)
 constexpr int kRows = 32;                      // rows per tile (one 16x16x32 K step of P V)
 constexpr int kHeads = 64;                     // query heads per workgroup
-constexpr int kLoaders = 4;                    // waves that only issue the tile loads (0: the softmax waves do)
-constexpr int kWaves = 8 + kLoaders;           // 4 softmax waves, 4 P.V waves, the loaders
+constexpr int kWaves = 12;                     // 4 softmax waves, 4 P.V waves, 4 loader waves
 constexpr int kThreadsF = kWaves * 64;
 constexpr int kBufs = 3;                       // tiles in LDS: P.V reads st - 1, softmax st, loads st + 1
 constexpr int kCompact = 1024;                 // positions compacted at a time
@@ -289,8 +292,8 @@ __global__ __launch_bounds__(mla_fwd::kThreadsF, 1) void fwd_mla_kernel(Params p
   auto src_of = [&](int code) -> const E* {
     return (code & kCmpFlag) ? Cg + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * kD : Kg + ((size_t)code * p.Hkv + g) * kD;
   };
-  // positions [pos0, pos0 + n) of the row compacted into sRows over all 8
-  // waves, in position order (same code and barriers in both roles)
+  // positions [pos0, pos0 + n) of the row compacted into sRows over all 12
+  // waves, in position order (same code and barriers in every role)
   auto compact = [&](int pos0, int n) -> int {
     int total = 0;
     for (int base = 0; base < n; base += kThreadsF) {
@@ -308,9 +311,9 @@ __global__ __launch_bounds__(mla_fwd::kThreadsF, 1) void fwd_mla_kernel(Params p
     }
     return total;
   };
-  // one barrier per stage: every softmax wave's loads of the stage's tile
+  // one barrier per stage: every loader wave's loads of the stage's tile
   // have landed, the exchange of the previous stage is written, and the
-  // buffers the P.V waves read at the previous stage are free
+  // buffer the P.V waves read at the previous stage is free
   auto stage_barrier = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   // rows k0 .. k0 + kRows - 1 of the compacted list into `buf` by direct
   // loads, issuing wave iw (of 4) taking the 64-chunk blocks iw, iw + 4, ...;
@@ -346,10 +349,6 @@ __global__ __launch_bounds__(mla_fwd::kThreadsF, 1) void fwd_mla_kernel(Params p
       const E* qrow = reinterpret_cast<const E*>(p.q) + ((size_t)t * p.Hq + hq) * kD + lq * 8;
 #pragma unroll
       for (int kk = 0; kk < kD / 32; ++kk) q[kk] = *reinterpret_cast<const V8*>(qrow + kk * 32);
-      // wait for Q here: the compiler does not count the direct loads below,
-      // so a wait for Q inside the tile loop would not be one it could place
-#pragma unroll
-      for (int kk = 0; kk < kD / 32; ++kk) asm volatile("" ::"v"(q[kk]));
     }
     const bool sk = p.has_sinks;
     float m_run = sk ? p.sinks[hq] * 1.4426950408889634f : -INFINITY;
@@ -358,10 +357,8 @@ __global__ __launch_bounds__(mla_fwd::kThreadsF, 1) void fwd_mla_kernel(Params p
       __syncthreads();   // the previous pass's rows and tiles are no longer read
       const int cnt = compact(pos0, min(kCompact, npos - pos0));
       const int ntiles = (cnt + kRows - 1) / kRows;
-      if (kLoaders == 0 && ntiles > 0) issue_tile(wv, 0, cnt, sK[0]);
       for (int st = 0; st <= ntiles; ++st) {
         stage_barrier();
-        if (kLoaders == 0 && st + 1 < ntiles) issue_tile(wv, (st + 1) * kRows, cnt, sK[(st + 1) % kBufs]);
         if (st == ntiles) continue;
         const int k0 = st * kRows;
         const E* kb = sK[st % kBufs];
@@ -505,9 +502,10 @@ bool fwd_rows_supported(int dqk, int dv, int shared) {
 }
 
 hipError_t launch_fwd_rows(const Params& p, void* o, float* lse, hipStream_t s) {
-  // 64 heads per workgroup from 16 heads per kv head up (the last group's
-  // missing heads masked); fewer heads go to the 16-head row kernel
-  if (p.dqk == 576 && p.dv == 512 && p.shared && p.G >= 16) {
+  // 64 heads per workgroup at any number of heads per kv head (the last
+  // group's missing heads masked: one head runs in about the time of 64,
+  // still below the 16-head row kernel's time for 1-15 heads)
+  if (p.dqk == 576 && p.dv == 512 && p.shared) {
     const dim3 grid((unsigned)(p.T * p.Hkv), (unsigned)((p.G + mla_fwd::kHeads - 1) / mla_fwd::kHeads));
     if (p.fp16)
       hipLaunchKernelGGL(fwd_mla_kernel<f16>, grid, dim3(mla_fwd::kThreadsF), 0, s, p, static_cast<f16*>(o), lse);
