@@ -56,8 +56,8 @@ MEASURED_TRAFFIC = {
     },
     ("mla_token_8k", "fwd"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_fwd_rows.hip",
-        "sha256": "5d440ea41a4fd8707b9475cdd9b9fcfd598e4c53811fe6475f88a21e5564859d",
-        "fetch_bytes": 5274537480, "write_bytes": 538968064,
+        "sha256": "f45d5acb8c6315112410e5d58c20b52d2cfcff3a02276bf0648a3cb35bebe7bc",
+        "fetch_bytes": 1995059675, "write_bytes": 538968064,
     },
     ("nsa_block_gqa", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_blk.hip",
