@@ -56,7 +56,7 @@ MEASURED_TRAFFIC = {
     },
     ("mla_token_8k", "fwd"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_fwd_rows.hip",
-        "sha256": "f45d5acb8c6315112410e5d58c20b52d2cfcff3a02276bf0648a3cb35bebe7bc",
+        "sha256": "bdd7188ca26aded38114aeefc85e7e04a8c5c481e3082206325eb7eb908981de",
         "fetch_bytes": 1995059675, "write_bytes": 538968064,
     },
     ("nsa_block_gqa", "deterministic"): {

@@ -206,10 +206,10 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
 // of once per 16 heads, which bounded the single-role form (each of 4 waves
 // reading the whole V^T for its 16 heads: 6.3-6.5 ms on the 8192-token
 // top-2048 shape: 3.2 ms split).  A direct load waits at issue while the
-// CU's address unit works through the loads queued before it (the 37 of a
-// tile take it ~1700 cycles), so the waves that issue them do nothing else:
-// issued by the softmax waves the loads held each stage's S^T back (3.2 ->
-// 2.8 ms with loader waves).
+// CU's vector-memory path works through the loads queued before it (the 37
+// of a tile keep it busy ~2200 cycles), so the waves that issue them do
+// nothing else: issued by the softmax waves the loads held each stage's S^T
+// back (3.2 -> 2.8 ms with loader waves).
 namespace mla_fwd {
 constexpr int kD = 576, kDV = 512;
 constexpr int kKS = kD + 8;                    // LDS row stride (elements)
