@@ -2,7 +2,9 @@
 counts per kv head that are not a multiple of 64 (SparseFlashMlaGrad
 README, constraints: 1 to 128 query heads), rows of more than one
 2048-position compaction pass, and fp16 inputs (the README's parameter
-table: BFLOAT16 or FLOAT16) at full size."""
+table: BFLOAT16 or FLOAT16) at full size; and the edge cases of the index
+lists (padding in any slot, duplicates, out-of-range indices, empty rows
+with sinks) on these kernels."""
 import dataclasses
 
 import numpy as np
@@ -92,3 +94,60 @@ def test_fwd_mla_rows_of_three_passes_fp16():
     sel = torch.tensor(toks, device=o.device)
     check_close("fwd 3 passes fp16:o", o[sel].float().cpu().numpy(), out_ref)
     np.testing.assert_allclose(lse[sel].cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
+
+
+def _mla_edge_inputs(dtype="bf16"):
+    """20 heads with sinks (one 64-head group, 44 masked): -1 shuffled into
+    any slot, a duplicated index, an out-of-range index, and rows with no
+    valid key (lse = the sink alone)."""
+    wl = dataclasses.replace(_mla(20, dtype=dtype), name=f"mla_edge_{dtype}", has_sinks=True, seed=141)
+    inp = W.make_inputs(wl)
+    idx = inp["idx"].numpy().copy()
+    rng = np.random.default_rng(11)
+    for t in range(idx.shape[0]):
+        rng.shuffle(idx[t, 0])
+    idx[150, 0, 0] = idx[150, 0, 1] = 7          # duplicate
+    idx[151, 0, 2] = 5000                          # out of range -> unused
+    idx[60] = -1                                   # no valid key
+    idx[61, 0, :] = -1
+    inp["idx"] = torch.from_numpy(idx)
+    return wl, inp
+
+
+_EDGE = {}
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bwd_mla_edge_padding_duplicates_empty_rows(mode):
+    """The MLA backward on shuffled padding, a duplicate, an out-of-range
+    index and empty rows with sinks: every output row against the oracle;
+    an empty row's dq is 0 and its dsinks term still counts (SparseFlashMlaGrad
+    README, Stage 3: dSinks over every row)."""
+    if not _EDGE:
+        wl, inp = _mla_edge_inputs()
+        _EDGE["case"] = (wl, U.oracle_case(wl, inp, l1=True))
+    wl, orc = _EDGE["case"]
+    U.say(f"[mla edge] {mode}")
+    res, got, ref = U.run_full_case(wl, dkv_mode=MODES[mode], l1=True, oracle=orc)
+    assert "dsinks" in res
+    assert np.all(got["dq"].reshape(ref["dq"].shape)[60] == 0)
+    l1 = got["ori_softmax_l1"].reshape(ref["ori_l1"].shape)
+    assert np.all(l1[60] == 0) and np.all(l1[61] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fwd_mla_edge_padding_duplicates_empty_rows(dtype):
+    """The MLA forward on the same edge cases: an empty row's O is 0 and its
+    lse is the sink logit (aclnnNsaSelectedAttentionInfer, "Formula", with the
+    sink in the softmax denominator)."""
+    wl, inp = _mla_edge_inputs(dtype)
+    U.say(f"[fwd mla edge {dtype}]")
+    out_ref, lse_ref = O.sparse_fwd(O.Problem(inp))
+    o, lse = B.sparse_attn_fwd(B.make_desc(wl), B.device_tensors(inp))
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    check_close(f"fwd edge {dtype}:o", o, out_ref)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
+    assert np.all(o[60] == 0) and np.all(o[61] == 0)
+    np.testing.assert_allclose(lse[60], inp["sinks"].numpy(), rtol=1e-6)
