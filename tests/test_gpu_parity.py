@@ -208,7 +208,8 @@ def test_bwd_block_sizes_off_the_block_dq_kernel(mode, bs):
 def test_bwd_mla_head_counts_off_a_multiple_of_64(mode, heads):
     """Shared-KV 576/512 with a head count that is not a multiple of 64 (the
     pages allow 1 to 128): the 64-head kernel with 63 (1 head) or 44 (20
-    heads) heads masked; every dK/dV mode."""
+    heads) heads masked; the atomic and deterministic modes (the per-XCD
+    form at these head counts: tests/test_gpu_mla_shapes.py)."""
     wl = _wl(name=f"mla_{heads}h", seqlens=(200,), n_q_heads=heads, d_qk=576, d_v=512, kv_shared=True, topk=80,
              kv_std=0.5, seed=90 + heads)
     U.say(f"[mla heads={heads}] {mode}")
