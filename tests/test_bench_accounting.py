@@ -55,3 +55,23 @@ def test_multi_gpu_request_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_stored_traffic_is_keyed_to_its_kernel_source(monkeypatch):
+    """roofline.traffic is a stored counter reading: it is reported only
+    while the kernel source it was taken on is unchanged (SHA-256), and is
+    null otherwise."""
+    import hashlib
+    for key, t in bench.MEASURED_TRAFFIC.items():
+        path = os.path.join(ROOT, t["kernel_source"])
+        assert os.path.exists(path), key
+        with open(path, "rb") as f:
+            current = hashlib.sha256(f.read()).hexdigest()
+        got = bench.measured_traffic(*key)
+        assert got == (t["fetch_bytes"] + t["write_bytes"] if current == t["sha256"] else None), key
+    key = next(iter(bench.MEASURED_TRAFFIC))
+    stale = dict(bench.MEASURED_TRAFFIC[key], sha256="0" * 64)
+    monkeypatch.setitem(bench.MEASURED_TRAFFIC, key, stale)
+    assert bench.measured_traffic(*key) is None
+    f = bench.traffic_fields(*key)
+    assert f["traffic"] is None and "not valid" in f["traffic_source"]
