@@ -61,8 +61,8 @@ MEASURED_TRAFFIC = {
     },
     ("nsa_block_gqa", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_blk.hip",
-        "sha256": "b1c1bbe1179b355006edb58d36b6a36790e60f7f356ca8d5094c052d4e36502e",
-        "fetch_bytes": 103938179, "write_bytes": 33554432,
+        "sha256": "532ff8dfd4707336ca19dc19d843505c0e62d394226ffa79b2c1eb1a0b2e7721",
+        "fetch_bytes": 103939855, "write_bytes": 33554432,
     },
 }
 

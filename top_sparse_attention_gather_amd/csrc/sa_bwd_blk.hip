@@ -370,6 +370,11 @@ __global__ __launch_bounds__(kThreads) void blk_dq_kernel(Params p, BwdBuffers w
   const int tq = l16 & 3;
 
   if (nb > 0) load_block(0, 0);
+  // Two of these workgroups share a CU and do equal work, so they would run
+  // in lockstep, both waiting for their block loads at the same time;
+  // starting a pseudo-random half of them ~500 cycles late lets one compute
+  // while the other waits (0.360 -> 0.331 ms on the NSA block workload).
+  if ((blockIdx.x * 2654435761u) >> 31) __builtin_amdgcn_s_sleep(8);
   for (int bi = 0; bi < nb; ++bi) {
     const int buf = bi & 1;
     // this block's loads are done and every wave has left the other buffer
