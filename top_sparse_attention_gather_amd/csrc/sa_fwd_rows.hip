@@ -18,6 +18,8 @@ constexpr int kNT = 32;
 constexpr int kHC = 16;
 constexpr int kMaxPos = 2048;
 
+typedef __attribute__((address_space(3))) i16x4 gen_lds_i16x4;
+
 template <int DQK, int DV, bool SHARED, typename E>
 __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restrict__ out_o,
                                                             float* __restrict__ out_lse) {
@@ -147,14 +149,19 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
         f32x4 al;
 #pragma unroll
         for (int r = 0; r < 4; ++r) al[r] = sAlpha[lq * 4 + r];
+        // B = V^T of 16 columns, keys 8lq .. 8lq + 7 in order: two
+        // transposing reads of 4 rows each (rows 8lq + l16/4 and
+        // 8lq + 4 + l16/4, columns 4(l16 % 4) of the block)
+        const E* vrow = vt + (lq * 8 + (l16 >> 2)) * VT + (l16 & 3) * 4;
 #pragma unroll
         for (int i = 0; i < NVB_W; ++i) {
           const int cb = wv + 4 * i;
           if (cb < NVB) {
-            V8 b;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) b[jj] = vt[(lq * 8 + jj) * VT + cb * 16 + l16];
-            accO[i] = Elem<E>::mma32(a, b, accO[i] * al);
+            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((gen_lds_i16x4*)(vrow + cb * 16));
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((gen_lds_i16x4*)(vrow + 4 * VT + cb * 16));
+            typedef short i16x8_t __attribute__((ext_vector_type(8)));
+            const i16x8_t vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            accO[i] = Elem<E>::mma32(a, __builtin_bit_cast(V8, vb), accO[i] * al);
           }
         }
       }
