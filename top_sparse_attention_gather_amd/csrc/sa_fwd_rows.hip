@@ -28,6 +28,10 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
   constexpr int PS = kNT + 8;
   constexpr int NVB = DV / 16;
   constexpr int NVB_W = (NVB + 3) / 4;
+  // 16-byte chunks of a tile's K (V) rows per thread
+  constexpr int CK = (kNT * (DQK / 8) + kThreads - 1) / kThreads;
+  constexpr int CV = SHARED ? 0 : (kNT * (DV / 8) + kThreads - 1) / kThreads;
+  constexpr int CVA = CV > 0 ? CV : 1;   // register array size
   static_assert(DQK % 32 == 0 && DV % 32 == 0 && DV <= DQK, "head dims");
 
   typedef typename Elem<E>::V8 V8;
@@ -75,29 +79,48 @@ __global__ __launch_bounds__(kThreads) void fwd_rows_kernel(Params p, E* __restr
     __syncthreads();
     const int cnt =
         compact_positions(p, s, irow, pos0, min(kMaxPos, npos - pos0), sRows, sWave, nullptr, row_len(p, row));
-    for (int k0 = 0; k0 < cnt; k0 += kNT) {
-      for (int c = tid; c < kNT * (DQK / 8); c += kThreads) {
+    // the tile's K (and V) rows are loaded into registers one tile ahead,
+    // while the previous tile is computed, and written to LDS at the top of
+    // its own iteration (rows past cnt are zero)
+    uint4 kreg[CK], vreg[CVA];
+    auto load_tile = [&](int k0) {
+#pragma unroll
+      for (int j = 0; j < CK; ++j) {
+        const int c = tid + j * kThreads;
         const int r = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (k0 + r < cnt) {
+        kreg[j] = make_uint4(0, 0, 0, 0);
+        if (c < kNT * (DQK / 8) && k0 + r < cnt) {
           const int code = sRows[k0 + r];
           const E* src = (code & kCmpFlag) ? Cg + ((size_t)(code & ~kCmpFlag) * p.Hkv + g) * DQK
                                            : Kg + ((size_t)code * p.Hkv + g) * DQK;
-          v = *reinterpret_cast<const uint4*>(src + col);
-        }
-        *reinterpret_cast<uint4*>(&sK[r * QS + col]) = v;
-      }
-      if (!SHARED) {
-        for (int c = tid; c < kNT * (DV / 8); c += kThreads) {
-          const int r = c / (DV / 8), col = (c % (DV / 8)) * 8;
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (k0 + r < cnt) {
-            const int code = sRows[k0 + r];
-            v = *reinterpret_cast<const uint4*>(Vbase + ((size_t)code * p.Hkv + g) * DV + col);
-          }
-          *reinterpret_cast<uint4*>(&sV[r * VS + col]) = v;
+          kreg[j] = *reinterpret_cast<const uint4*>(src + col);
         }
       }
+#pragma unroll
+      for (int j = 0; j < CV; ++j) {
+        const int c = tid + j * kThreads;
+        const int r = c / (DV / 8), col = (c % (DV / 8)) * 8;
+        vreg[j] = make_uint4(0, 0, 0, 0);
+        if (c < kNT * (DV / 8) && k0 + r < cnt) {
+          const int code = sRows[k0 + r];
+          vreg[j] = *reinterpret_cast<const uint4*>(Vbase + ((size_t)code * p.Hkv + g) * DV + col);
+        }
+      }
+    };
+    if (cnt > 0) load_tile(0);
+    for (int k0 = 0; k0 < cnt; k0 += kNT) {
+#pragma unroll
+      for (int j = 0; j < CK; ++j) {
+        const int c = tid + j * kThreads;
+        if (c < kNT * (DQK / 8))
+          *reinterpret_cast<uint4*>(&sK[(c / (DQK / 8)) * QS + (c % (DQK / 8)) * 8]) = kreg[j];
+      }
+#pragma unroll
+      for (int j = 0; j < CV; ++j) {
+        const int c = tid + j * kThreads;
+        if (c < kNT * (DV / 8)) *reinterpret_cast<uint4*>(&sV[(c / (DV / 8)) * VS + (c % (DV / 8)) * 8]) = vreg[j];
+      }
+      if (k0 + kNT < cnt) load_tile(k0 + kNT);
       __syncthreads();
 
       if (wv < 2) {
