@@ -51,8 +51,8 @@ MEASURED_TRAFFIC = {
     },
     ("indexer_8k", "idx"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_indexer.hip",
-        "sha256": "355a1e89c78e00580e8e919c47d6f142165ee5e76d448c9617cab9a8e0c05303",
-        "fetch_bytes": 660554130, "write_bytes": 3894948864,
+        "sha256": "e63cc54c0b194997f09ab5cf77abc245dbe96352570fe41017a31092db3956d1",
+        "fetch_bytes": 669436718, "write_bytes": 3894950976,
     },
     ("mla_token_8k", "fwd"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_fwd_rows.hip",

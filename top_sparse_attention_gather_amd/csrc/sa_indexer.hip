@@ -74,7 +74,9 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(kThreads) void idx_grad_kernel(Params p, IdxArgs a) {
+// (at most 168 registers, so three workgroups share a CU instead of two:
+// 1.95 -> 1.91 ms on the 8192-token top-2048 shape, no spills)
+__global__ __launch_bounds__(kThreads, 3) void idx_grad_kernel(Params p, IdxArgs a) {
   __shared__ IdxSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
