@@ -46,8 +46,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     ("mla_token_8k", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
-        "sha256": "46c75607c6aa74130e627a0005077474d522b16ea7f0654306ca4b0d7b4f02ee",
-        "fetch_bytes": 8390663602, "write_bytes": 17525839872,
+        "sha256": "1e57cd9e15fcf7ff0b5524b9a62ab29f34102d2fa723f56e9406e8b7ba14633b",
+        "fetch_bytes": 8346248813, "write_bytes": 17517302208,
     },
     ("indexer_8k", "idx"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_indexer.hip",

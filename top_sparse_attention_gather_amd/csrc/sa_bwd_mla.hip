@@ -99,7 +99,7 @@ struct __attribute__((aligned(16))) MlaSmem {
   };
   int rows[kMaxPos];
   int vpos[kMaxPos];
-  int wave[4];
+  int wave[4 * (kMaxPos / 256)];   // per-round wave counts of the compaction
   float l1s[4][kNT];               // softmax L1-norm: P summed over each wave's 16 heads, per key
 };
 
@@ -223,12 +223,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   bf16* part_row0 = static_cast<bf16*>(w.partial) +
                     (((size_t)blockIdx.y * w.Tc * p.Hkv + blockIdx.x) * w.npos) * kDQK;
 
-  // ---- compacted selection (positions and their row codes) of the first
-  // pass of at most kMaxPos positions --------------------------------------
+  // ---- indices of the first pass of at most kMaxPos positions: loaded
+  // here, compacted (positions and their row codes) once they and the Q / dO
+  // staging loads below have landed -- one wait for both ----------------------
   const int npos = n_positions(p);
   const int len = row_len(p, row);
-  int cnt = compact_positions_batched<kMaxPos / 256>(p, s, irow, min(npos, kMaxPos), sm.rows, sm.wave, sm.vpos,
-                                                     len, 0);
+  constexpr int kRounds = kMaxPos / 256;
+  int raw[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int pos = r * 256 + tid;
+    raw[r] = pos < min(npos, kMaxPos) ? position_index(p, irow, pos, len) : -1;
+  }
 
   // ---- lse / D of the wave's heads (phase-A layout: head = 16 wv + l16);
   // with fuse_d, D follows from the staged dO and O below -------------------
@@ -245,10 +251,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   // Q goes to the two KV tile buffers and dO to the exchange / dO^T-block
   // area (both free until the tile loop), with all the loads in flight
   // together (with fuse_d, so do the O rows of the wave's 16 heads, into
-  // registers); one wait, then (fuse_d) D = rowsum(dO o O) (SparseFlashMlaGrad
-  // README, Stage 2) and the operand layouts are read out.
+  // registers).  The first pass's positions are compacted behind them (the
+  // index loads went out first, so their latency and the staging's overlap
+  // instead of adding up); one wait, then (fuse_d) D = rowsum(dO o O)
+  // (SparseFlashMlaGrad README, Stage 2) and the operand layouts are read out.
   bf16x8 QA[18], dOA[16];          // phase A: [head 16wv + l16][32kk + 8lq .. +8]
   bf16x8 QT[9][2], dOT[8][2];      // phase B: [col][heads 32ks + 8lq .. +8]
+  int cnt;
   {
     // 32 heads per buffer, in the tile layout; wave w loads row group w of
     // both buffers (heads 32hb + 8w + lane / 8)
@@ -275,6 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
         orow[i] = *reinterpret_cast<const uint4*>(p.o + ((size_t)t * p.Hq + h0 + min(wv * 16 + i, gh - 1)) * kDV +
                                                   lane * 8);
     }
+    cnt = compact_loaded(p, s, raw, min(npos, kMaxPos), sm.rows, sm.wave, sm.vpos);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     // D of head 16wv + i: the lane's 8 products with chunk `lane` of the
     // staged dO row, summed over the 64 lanes; lane l16 keeps head l16's
@@ -649,8 +659,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
     // tiles and exchange before they are rewritten
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    cnt = compact_positions_batched<kMaxPos / 256>(p, s, irow, min(kMaxPos, npos - pos0), sm.rows, sm.wave, sm.vpos,
-                                                   len, pos0);
+    int rawp[kRounds];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int pos = r * 256 + tid;
+      rawp[r] = pos < min(kMaxPos, npos - pos0) ? position_index(p, irow, pos0 + pos, len) : -1;
+    }
+    cnt = compact_loaded(p, s, rawp, min(kMaxPos, npos - pos0), sm.rows, sm.wave, sm.vpos, pos0);
     ntiles = (cnt + kNT - 1) / kNT;
     if (ntiles > 0) gather_tile(p, sm, sm.kv, 0, cnt, g, wv, lane);
   }
@@ -691,19 +706,33 @@ __global__ __launch_bounds__(kThreads, 1) void mla_bwd_kernel(Params p, BwdBuffe
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- dQ (already scaled: the exchange holds scale dS) -------------------
+  // The 64 heads' rows of the token are contiguous in dq: they go through
+  // LDS (the tile buffers, free once every wave is past its last dQ
+  // product) so that every store writes 16 contiguous bytes per lane and
+  // whole lines per instruction, instead of 8 bytes of 16 rows apart.
   // lane: columns col_block(c) + 4lq .. +3 of head 16hb + l16
+  __syncthreads();
+  bf16* sq = sm.kv;   // [head][kKS]
 #pragma unroll
   for (int c = 0; c < 9; ++c) {
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
-      if (hb * 16 + l16 >= gh) continue;   // a missing head
-      bf16* dq = w.dq + ((size_t)t * p.Hq + h0 + hb * 16 + l16) * kDQK + col_block(c) + lq * 4;
       const f32x4 v = dQ[c * 4 + hb] * kInvX;
       typedef short i16x4v __attribute__((ext_vector_type(4)));
       i16x4v o = {bf16_bits(F::to16(v[0])), bf16_bits(F::to16(v[1])), bf16_bits(F::to16(v[2])),
                   bf16_bits(F::to16(v[3]))};
-      *reinterpret_cast<i16x4v*>(dq) = o;
+      *reinterpret_cast<i16x4v*>(&sq[(hb * 16 + l16) * kKS + col_block(c) + lq * 4]) = o;
     }
+  }
+  __syncthreads();
+  bf16* dqb = w.dq + ((size_t)t * p.Hq + h0) * kDQK;
+  constexpr int kRowChunks = kDQK / 8;   // 16-byte pieces of a row
+#pragma unroll
+  for (int i = 0; i < kHeads * kRowChunks / kThreads; ++i) {
+    const int id = i * kThreads + tid;
+    const int hh = id / kRowChunks, ch = id - hh * kRowChunks;
+    if (hh < gh)   // a missing head has no row
+      *reinterpret_cast<uint4*>(dqb + (size_t)hh * kDQK + ch * 8) = *reinterpret_cast<const uint4*>(&sq[hh * kKS + ch * 8]);
   }
 }
 

@@ -136,38 +136,53 @@ __device__ __forceinline__ int n_positions(const Params& p) {
   return p.win_left + 1 + p.win_right + p.topk;
 }
 
-// Decode virtual position `pos` of row (t, g): the encoded selected row, or
-// -1 when the slot is unused or masked.  `irow` points at idx[t][g][0];
-// `len` is the row's selectable slot count (row_len).
-__device__ __forceinline__ int decode_position(const Params& p, const SeqPos& s,
-                                               const int* __restrict__ irow, int pos, int len = 0x7fffffff) {
+// The index slot that virtual position `pos` reads, loaded (-1 where it
+// reads none: a window position, or a slot at or past `len`).  It depends
+// on nothing of the query's sequence, so the loads of a row's positions can
+// be issued before anything else is known about the row.
+__device__ __forceinline__ int position_index(const Params& p, const int* __restrict__ irow, int pos, int len) {
+  if (p.select == kSelToken) return pos < len ? irow[pos] : -1;
+  if (p.select == kSelBlock) {
+    const int slot = pos / p.bs;
+    return slot < len ? irow[slot] : -1;
+  }
+  const int q = pos - (p.win_left + 1 + p.win_right);
+  return q >= 0 && q < len ? irow[q] : -1;
+}
+
+// Decode virtual position `pos` of row (t, g) from its loaded index `raw`
+// (position_index): the encoded selected row, or -1 when the slot is unused
+// or masked.
+__device__ __forceinline__ int decode_loaded(const Params& p, const SeqPos& s, int pos, int raw) {
   if (!s.active) return -1;   // a padding query row selects nothing
   if (p.select == kSelToken) {
-    if (pos >= len) return -1;
-    int j = irow[pos];
+    const int j = raw;
     if (j < 0 || j >= s.kv_len || (p.causal && j > s.tl)) return -1;
     return s.kv_base + j;
   }
   if (p.select == kSelBlock) {
-    int slot = pos / p.bs;
-    if (slot >= len) return -1;
-    int blk = irow[slot];
-    if (blk < 0) return -1;
-    long long j = (long long)blk * p.bs + (pos - slot * p.bs);
+    if (raw < 0) return -1;
+    const long long j = (long long)raw * p.bs + (pos - (pos / p.bs) * p.bs);
     if (j >= s.kv_len || (p.causal && j > s.tl)) return -1;
     return s.kv_base + (int)j;
   }
   const int nwin = p.win_left + 1 + p.win_right;
   if (pos < nwin) {
-    int j = s.tl - p.win_left + pos;
+    const int j = s.tl - p.win_left + pos;
     if (j < 0 || j >= s.kv_len || (p.causal && j > s.tl)) return -1;
     return s.kv_base + j;
   }
-  if (pos - nwin >= len) return -1;
-  int j = irow[pos - nwin];
+  const int j = raw;
   if (j < 0 || j >= s.cmp_len) return -1;
   if (p.causal && (long long)p.cmp_ratio * j + p.cmp_ratio - 1 > s.tl) return -1;
   return (s.cmp_base + j) | kCmpFlag;
+}
+
+// Decode virtual position `pos` of row (t, g).  `irow` points at
+// idx[t][g][0]; `len` is the row's selectable slot count (row_len).
+__device__ __forceinline__ int decode_position(const Params& p, const SeqPos& s,
+                                               const int* __restrict__ irow, int pos, int len = 0x7fffffff) {
+  return decode_loaded(p, s, pos, position_index(p, irow, pos, len));
 }
 
 // Compact positions [pos0, pos0 + n) of a row into sRows, keeping position
@@ -233,6 +248,46 @@ __device__ __forceinline__ int compact_positions_batched(const Params& p, const 
     total += sWave[0] + sWave[1] + sWave[2] + sWave[3];
     __syncthreads();
   }
+  return total;
+}
+
+// compact_positions_batched over indices already loaded -- raw[r] is
+// position_index of position pos0 + 256 r + tid (-1 past n) -- with one
+// barrier for all rounds instead of two per round: each wave ballots its
+// ROUNDS rounds and publishes the counts (sCnt holds 4 ROUNDS ints), and a
+// used position's slot is the number of used positions before it in
+// (round, wave, lane) order, i.e. in position order, as round by round.
+// The barriers are LDS-only (loads of the caller's may stay in flight);
+// ends with one.
+template <int ROUNDS>
+__device__ __forceinline__ int compact_loaded(const Params& p, const SeqPos& s, const int (&raw)[ROUNDS], int n,
+                                              int* sRows, int* sCnt, int* sVpos, int pos0 = 0) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int code[ROUNDS];
+  unsigned long long m[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int pos = r * 256 + tid;
+    code[r] = pos < n ? decode_loaded(p, s, pos0 + pos, raw[r]) : -1;
+    m[r] = __ballot(code[r] >= 0);
+  }
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r)
+    if (lane == r) sCnt[r * 4 + w] = __popcll(m[r]);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  int total = 0;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int c0 = sCnt[r * 4], c1 = sCnt[r * 4 + 1], c2 = sCnt[r * 4 + 2], c3 = sCnt[r * 4 + 3];
+    const int off = total + (w > 0 ? c0 : 0) + (w > 1 ? c1 : 0) + (w > 2 ? c2 : 0) +
+                    __popcll(m[r] & ((1ull << lane) - 1ull));
+    if (code[r] >= 0) {
+      sRows[off] = code[r];
+      sVpos[off] = pos0 + r * 256 + tid;
+    }
+    total += c0 + c1 + c2 + c3;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   return total;
 }
 
