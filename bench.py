@@ -51,8 +51,8 @@ MEASURED_TRAFFIC = {
     },
     ("indexer_8k", "idx"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_indexer.hip",
-        "sha256": "e63cc54c0b194997f09ab5cf77abc245dbe96352570fe41017a31092db3956d1",
-        "fetch_bytes": 669436718, "write_bytes": 3894950976,
+        "sha256": "c011a9bac216114f734119104d90f9d5329e55a712b851d3cfe6e4cc5800d4d7",
+        "fetch_bytes": 681986366, "write_bytes": 3894948128,
     },
     ("mla_token_8k", "fwd"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_fwd_rows.hip",

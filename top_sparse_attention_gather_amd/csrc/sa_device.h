@@ -216,49 +216,15 @@ __device__ __forceinline__ int compact_positions(const Params& p, const SeqPos& 
 }
 
 // Same result as compact_positions for positions [pos0, pos0 + n), n <=
-// 256 * ROUNDS, with every position decoded (and its index loaded) before
-// the first ballot, so the index loads overlap instead of costing one round
-// trip per round.  sVpos receives the positions themselves (pos0 + i).
-template <int ROUNDS>
-__device__ __forceinline__ int compact_positions_batched(const Params& p, const SeqPos& s,
-                                                         const int* __restrict__ irow, int n, int* sRows,
-                                                         int* sWave, int* sVpos, int len = 0x7fffffff,
-                                                         int pos0 = 0) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int code[ROUNDS];
-#pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    const int pos = r * 256 + tid;
-    code[r] = pos < n ? decode_position(p, s, irow, pos0 + pos, len) : -1;
-  }
-  int total = 0;
-#pragma unroll
-  for (int r = 0; r < ROUNDS; ++r) {
-    if (r * 256 >= n) break;
-    const unsigned long long m = __ballot(code[r] >= 0);
-    const int before = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) sWave[w] = __popcll(m);
-    __syncthreads();
-    int off = total;
-    for (int i = 0; i < w; ++i) off += sWave[i];
-    if (code[r] >= 0) {
-      sRows[off + before] = code[r];
-      sVpos[off + before] = pos0 + r * 256 + tid;
-    }
-    total += sWave[0] + sWave[1] + sWave[2] + sWave[3];
-    __syncthreads();
-  }
-  return total;
-}
-
-// compact_positions_batched over indices already loaded -- raw[r] is
-// position_index of position pos0 + 256 r + tid (-1 past n) -- with one
-// barrier for all rounds instead of two per round: each wave ballots its
-// ROUNDS rounds and publishes the counts (sCnt holds 4 ROUNDS ints), and a
-// used position's slot is the number of used positions before it in
-// (round, wave, lane) order, i.e. in position order, as round by round.
-// The barriers are LDS-only (loads of the caller's may stay in flight);
-// ends with one.
+// 256 * ROUNDS, from indices the caller has already loaded -- raw[r] is
+// position_index of position pos0 + 256 r + tid (-1 past n) -- so that
+// their loads can be in flight with the caller's others.  One barrier for
+// all rounds instead of two per round: each wave ballots its ROUNDS rounds
+// and publishes the counts (sCnt holds 4 ROUNDS ints), and a used
+// position's slot is the number of used positions before it in (round,
+// wave, lane) order, i.e. in position order.  sVpos receives the positions
+// themselves.  The barriers are LDS-only (the caller's loads may stay in
+// flight); ends with one.
 template <int ROUNDS>
 __device__ __forceinline__ int compact_loaded(const Params& p, const SeqPos& s, const int (&raw)[ROUNDS], int n,
                                               int* sRows, int* sCnt, int* sVpos, int pos0 = 0) {

@@ -50,7 +50,7 @@ struct __attribute__((aligned(16))) IdxSmem {
   float red[3][4];
   int rows[kMaxPos];
   int vpos[kMaxPos];
-  int wave[4];
+  int wave[4 * (kMaxPos / 256)];   // per-round wave counts of the compaction
 };
 
 // element offset of 16-byte chunk `chunk` of tile row r
@@ -88,19 +88,34 @@ __global__ __launch_bounds__(kThreads, 3) void idx_grad_kernel(Params p, IdxArgs
   const SeqPos s = seq_pos(p, t);
   const int* irow = p.idx + (size_t)t * p.topk;
 
-  // ---- the token's used slots, compacted ---------------------------------
-  const int cnt = compact_positions_batched<kMaxPos / 256>(p, s, irow, p.topk, sm.rows, sm.wave, sm.vpos);
-
+  // ---- the token's slots and q~ of its 64 heads, all loads in flight
+  // together; then the used slots compacted, and q~ via LDS into both
+  // operand layouts ---------------------------------------------------------
+  constexpr int kRounds = kMaxPos / 256;
+  int raw[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int pos = r * 256 + tid;
+    raw[r] = pos < p.topk ? position_index(p, irow, pos, 0x7fffffff) : -1;
+  }
+  constexpr int kQPer = kHeads * kD / 8 / kThreads;   // 16-byte pieces of q~ per thread
+  uint4 qv[kQPer];
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i) {
+    const int c = i * kThreads + tid;
+    const int h = c / (kD / 8), col = (c % (kD / 8)) * 8;
+    qv[i] = h < H ? *reinterpret_cast<const uint4*>(a.q + ((size_t)t * H + h) * kD + col) : make_uint4(0, 0, 0, 0);
+  }
   const int hl = wv * 16 + l16;   // this lane's head in the S~^T layout
   const float wh = hl < H ? a.w[(size_t)t * H + hl] : 0.f;
+  const int cnt = compact_loaded(p, s, raw, p.topk, sm.rows, sm.wave, sm.vpos);
 
-  // ---- q~ of the 64 heads via LDS into both operand layouts --------------
   bf16* qs = &sm.k[0][0];
-  for (int c = tid; c < kHeads * kD / 8; c += kThreads) {
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i) {
+    const int c = i * kThreads + tid;
     const int h = c / (kD / 8), col = (c % (kD / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (h < H) v = *reinterpret_cast<const uint4*>(a.q + ((size_t)t * H + h) * kD + col);
-    *reinterpret_cast<uint4*>(qs + h * kD + col) = v;
+    *reinterpret_cast<uint4*>(qs + h * kD + col) = qv[i];
   }
   __syncthreads();
   bf16x8 QB[kD / 32];             // B operand: head hl, dims 32kk + 8lq .. +8
