@@ -46,8 +46,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     ("mla_token_8k", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_mla.hip",
-        "sha256": "1e57cd9e15fcf7ff0b5524b9a62ab29f34102d2fa723f56e9406e8b7ba14633b",
-        "fetch_bytes": 8346248813, "write_bytes": 17517302208,
+        "sha256": "d2c60c708983d71f54a451fb466db0cf0692e85f5dace0a3e6859f9564944931",
+        "fetch_bytes": 8135253022, "write_bytes": 17517237920,
     },
     ("indexer_8k", "idx"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_indexer.hip",

@@ -525,12 +525,11 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   };
 
   const size_t Hkv = (size_t)desc->n_kv_heads;
-  // With short rows (at most 1024 positions, e.g. window + cmp) the MLA
-  // kernel (deterministic mode) forms D and the dSinks terms from its own
-  // staged dO and O: the separate pass would re-read dO and O of many tokens
-  // per unit of main-kernel work.  Every other call takes them from the
-  // preprocess.
-  const bool fused_d = L.mla && n_positions_host(desc) <= 1024;
+  // The MLA kernel forms D and the dSinks terms from its own staged dO and
+  // the O rows it loads beside them (their loads ride with the Q/dO staging),
+  // which saves the separate pass's re-read of dO and O; every other call
+  // takes them from the preprocess.
+  const bool fused_d = L.mla;
   w.fuse_d = fused_d ? 1 : 0;
   if (!fused_d) {
     SA_TRY_HIP(sa::launch_preprocess(p, w, s));

@@ -25,9 +25,10 @@
 //   before it and the last tile's runs after the loop.  The next KV tile is
 //   gathered with direct global->LDS loads during phase A, so the gather
 //   latency is off the MFMA path.
-// D = rowsum(dO o O) comes from the preprocess pass, or, for rows of at
-// most 1024 positions, is formed at the workgroup's start from the staged
-// dO and the O rows (with the dSinks terms).  Partial rows go to the
+// D = rowsum(dO o O) is formed at the workgroup's start from the staged dO
+// and the O rows (with the dSinks terms) when the launch asks for it (the
+// library always does), else read from the preprocess pass's output.
+// Partial rows go to the
 // token-major buffer consumed by the key-major reduce (deterministic sum in
 // CSR order).
 #include <type_traits>
