@@ -167,29 +167,42 @@ __global__ __launch_bounds__(kThreads) void slot_keys_hist_kernel(Params p, long
   const long long i1 = std::min(n, i0 + per_block);
   // The thread's slots are i0 + tid, i0 + tid + 256, ...: its (row, slot in
   // row) pair advances by 256 slots per step, and the row's sequence data
-  // is recomputed only when the row changes.
+  // is recomputed only when the row changes.  The indices of kBatch steps
+  // are loaded before any is used, so their loads overlap.
+  constexpr int kBatch = 8;
   long long i = i0 + threadIdx.x;
   if (i < i1) {
     int row = (int)((slot0 + i) / p.topk);
     int sl = (int)(slot0 + i - (long long)row * p.topk);
     int cur = -1, g = 0, len = 0;
     SeqPos s;
-    for (; i < i1; i += kThreads) {
-      if (row != cur) {
-        cur = row;
-        const int t = row / p.Hkv;
-        g = row - t * p.Hkv;
-        s = seq_pos(p, t);
-        len = row_len(p, row);
+    for (; i < i1; i += kBatch * kThreads) {
+      int j[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const long long iu = i + (long long)u * kThreads;
+        j[u] = iu < i1 ? p.idx[slot0 + iu] : -1;
       }
-      const int key = sl < len ? slot_key(p, s, g, p.idx[slot0 + i], blk_base, sentinel) : sentinel;
-      keys[i] = key;
-      if (key != sentinel) atomicAdd(&hist[key], 1);
-      sl += kThreads;
-      if (sl >= p.topk) {
-        const int q = sl / p.topk;
-        row += q;
-        sl -= q * p.topk;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const long long iu = i + (long long)u * kThreads;
+        if (iu >= i1) break;
+        if (row != cur) {
+          cur = row;
+          const int t = row / p.Hkv;
+          g = row - t * p.Hkv;
+          s = seq_pos(p, t);
+          len = row_len(p, row);
+        }
+        const int key = sl < len ? slot_key(p, s, g, j[u], blk_base, sentinel) : sentinel;
+        keys[iu] = key;
+        if (key != sentinel) atomicAdd(&hist[key], 1);
+        sl += kThreads;
+        if (sl >= p.topk) {
+          const int q = sl / p.topk;
+          row += q;
+          sl -= q * p.topk;
+        }
       }
     }
   }
@@ -250,20 +263,20 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(const int* __re
   __syncthreads();
   const long long base = (long long)blockIdx.x * kTile;
   const unsigned long long lt = (1ull << lane) - 1ull;
+  // every round's element loaded up front, so that the loads overlap
+  // instead of one round trip per round
+  int2 kvs[kItems];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const long long i = base + r * kThreads + tid;
+    kvs[r] = make_int2(0, 0);
+    if (i < n) kvs[r] = FIRST ? make_int2(keys_in[i], (int)(val0 + i)) : pairs_in[i];
+  }
+#pragma unroll
   for (int r = 0; r < kItems; ++r) {
     const long long i = base + r * kThreads + tid;
     const bool ok = i < n;
-    int key = 0, val = 0;
-    if (ok) {
-      if (FIRST) {
-        key = keys_in[i];
-        val = (int)(val0 + i);
-      } else {
-        const int2 kv = pairs_in[i];
-        key = kv.x;
-        val = kv.y;
-      }
-    }
+    const int key = kvs[r].x, val = kvs[r].y;
     const int d = (key >> shift) & 255;
     // lanes of this wave holding the same digit
     unsigned long long peers = __ballot(ok);
