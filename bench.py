@@ -56,8 +56,8 @@ MEASURED_TRAFFIC = {
     },
     ("mla_token_8k", "fwd"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_fwd_rows.hip",
-        "sha256": "bdd7188ca26aded38114aeefc85e7e04a8c5c481e3082206325eb7eb908981de",
-        "fetch_bytes": 1995059675, "write_bytes": 538968064,
+        "sha256": "b9e32a8b63797b9541203708503992ca55c0f67ede2e50dc2edeb25cee685ef6",
+        "fetch_bytes": 2041776385, "write_bytes": 538968064,
     },
     ("nsa_block_gqa", "deterministic"): {
         "kernel_source": "top_sparse_attention_gather_amd/csrc/sa_bwd_blk.hip",
