@@ -78,7 +78,19 @@ __global__ __launch_bounds__(kThreads) void dsinks_kernel(Params p, const float*
   __shared__ double part[kThreads];
   const int h = blockIdx.x;
   double acc = 0.0;
-  for (int t = threadIdx.x; t < p.T; t += kThreads) acc += (double)sink_term[(size_t)t * p.Hq + h];
+  // tokens tid, tid + 256, ... in that order; eight loads in flight at a time
+  constexpr int kU = 8;
+  for (int t0 = threadIdx.x; t0 < p.T; t0 += kU * kThreads) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int t = t0 + u * kThreads;
+      v[u] = t < p.T ? sink_term[(size_t)t * p.Hq + h] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (t0 + u * kThreads < p.T) acc += (double)v[u];
+  }
   part[threadIdx.x] = acc;
   __syncthreads();
   for (int w = kThreads / 2; w > 0; w >>= 1) {
