@@ -67,8 +67,11 @@
  * "Constraints": an empty query returns directly).
  *
  * Ownership: the caller allocates every input, output and workspace
- * buffer.  The library keeps no device memory and no mutable global
- * state; calls on different streams with disjoint buffers may overlap.
+ * buffer.  The library's own state is one stream and two events per
+ * device for the block-selection backward (sparse_attn_bwd) and the fixed
+ * scratch array of the allocation-free entry point
+ * (sparse_attn_bwd_noalloc); calls on different streams with disjoint
+ * buffers may overlap.
  */
 #ifndef SPARSE_ATTN_H_
 #define SPARSE_ATTN_H_
@@ -244,7 +247,14 @@ sa_status_t sparse_attn_bwd_workspace_size(const sa_desc_t* desc, size_t* bytes)
  * 256-byte aligned; its contents on entry are ignored.  Outputs are fully
  * overwritten (gradients are not accumulated into them).  dkv_mode =
  * SA_DKV_DETERMINISTIC gives bitwise-repeatable results; SA_DKV_ATOMIC
- * sums dK/dV contributions with fp32 atomics in an unspecified order. */
+ * sums dK/dV contributions with fp32 atomics in an unspecified order.
+ * Block selection in deterministic mode runs its key-major dK/dV chain on
+ * a stream the library makes on first use on each device (default
+ * priority, kept until the process ends), forked from and joined back
+ * into `stream` with events, so the call still completes in `stream`'s
+ * order; calls from several host threads are serialized while they
+ * enqueue.  The environment variable SPARSE_ATTN_SIDE_STREAM=0 keeps every
+ * launch on `stream`. */
 sa_status_t sparse_attn_bwd(const sa_desc_t* desc, const sa_bwd_args_t* args,
                             void* workspace, size_t workspace_bytes, void* stream);
 

@@ -6,7 +6,9 @@
 // parameter verification); the empty-query early return follows the same
 // page's "Constraints".
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/sparse_attn.h"
 #include "sa_launch.h"
@@ -347,6 +349,52 @@ IdxLayout idx_layout(const sa_indexer_desc_t* d) {
   return L;
 }
 
+// ---- the two block-selection passes side by side ----------------------------
+//
+// With block selection in deterministic mode the dQ pass (query-major) and
+// the CSR build, chunk count and key-major dK/dV pass do not depend on each
+// other; both passes are latency-bound and one workgroup of each fits a CU
+// together (registers and LDS).  The second chain runs on a library-owned
+// stream (default priority, no CU mask) forked from and joined back into the
+// caller's stream.  SPARSE_ATTN_SIDE_STREAM=0 keeps everything on the
+// caller's stream.
+constexpr int kMaxDev = 64;
+
+struct SideCtx {
+  int state = 0;                   // 0: not tried, 1: ready, -1: unavailable
+  hipStream_t s = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+};
+
+std::mutex g_side_mu;
+SideCtx g_side[kMaxDev];
+
+int stream_device(hipStream_t stream) {
+  int dev = -1;
+  if (!stream) return hipGetDevice(&dev) == hipSuccess ? dev : -1;
+  hipDevice_t d;
+  return hipStreamGetDevice(stream, &d) == hipSuccess ? (int)d : -1;
+}
+
+// The side stream of device `dev`, made on first use with that device
+// current (null if it cannot be made).  Called with g_side_mu held.
+SideCtx* side_ctx(int dev) {
+  if (dev < 0 || dev >= kMaxDev) return nullptr;
+  SideCtx& c = g_side[dev];
+  if (c.state) return c.state > 0 ? &c : nullptr;
+  c.state = -1;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  const bool ok = hipStreamCreateWithFlags(&c.s, hipStreamNonBlocking) == hipSuccess &&
+                  hipEventCreateWithFlags(&c.ev_fork, hipEventDisableTiming) == hipSuccess &&
+                  hipEventCreateWithFlags(&c.ev_join, hipEventDisableTiming) == hipSuccess;
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (!ok) return nullptr;
+  c.state = 1;
+  return &c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -462,9 +510,14 @@ sa_status_t sparse_attn_bwd_workspace_size(const sa_desc_t* desc, size_t* bytes)
   return SA_OK;
 }
 
-sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a, void* workspace,
-                                  size_t workspace_bytes, void* stream, void* ev_main_start,
-                                  void* ev_main_stop) {
+}  // extern "C"
+
+namespace sa {
+
+// The backward's launch sequence; allow_side = 0 keeps every launch on the
+// caller's stream (no library-owned stream: the allocation-free entry point).
+sa_status_t bwd_entry(const sa_desc_t* desc, const sa_bwd_args_t* a, void* workspace, size_t workspace_bytes,
+                      void* stream, void* ev_main_start, void* ev_main_stop, int allow_side) {
   size_t need = 0;
   sa_status_t st = sparse_attn_bwd_workspace_size(desc, &need);
   if (st != SA_OK) return st;
@@ -588,15 +641,25 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
   const bool has_slots = desc->topk > 0;
   if (desc->select == SA_SEL_BLOCK) SA_TRY_HIP(sa::launch_block_base(p, blk_base, s));
   if (L.blk_km) {
-    // dQ from the row kernel; dK/dV key-major over the CSR of block keys
-    if (has_slots) SA_TRY_HIP(sa::launch_csr_transpose(p, 0, p.T, nk, blk_base, row_ptr, entries, ws + L.csr_ws, s));
-    w.det = 1;
-    w.dq_only = 1;
-    // the timed "main" kernel of this path: the dQ pass (the larger one)
-    if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
-    SA_TRY_HIP(sa::blk_dq_supported(p) ? sa::launch_blk_dq(p, w, s) : sa::launch_bwd_rows(p, w, s));
-    if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
-    SA_TRY_HIP(l1_norm());
+    // dQ from the row kernel; dK/dV key-major over the CSR of block keys.
+    // The CSR, chunk count and key-major pass run on the side stream beside
+    // the dQ pass where there is one (see above).
+    std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+    SideCtx* side = nullptr;
+    if (allow_side) {
+      const char* env = std::getenv("SPARSE_ATTN_SIDE_STREAM");
+      if (!env || std::atoi(env) != 0) {
+        side_lock.lock();
+        side = side_ctx(stream_device(s));
+        if (!side) side_lock.unlock();
+      }
+    }
+    hipStream_t ks = s;   // the key-major chain's stream
+    if (side) {
+      SA_TRY_HIP(hipEventRecord(side->ev_fork, s));
+      SA_TRY_HIP(hipStreamWaitEvent(side->s, side->ev_fork, 0));
+      ks = side->s;
+    }
     sa::BlkArgs ba;
     std::memset(&ba, 0, sizeof(ba));
     ba.row_ptr = row_ptr;
@@ -609,11 +672,23 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     ba.n_hc = L.n_hc_blk;
     ba.n_keys = nk;
     const long long nrows = rows_kv(desc) * (long long)Hkv;
-    if (!has_slots) SA_TRY_HIP(sa::launch_fill_zero(reinterpret_cast<float*>(row_ptr), (size_t)(nk + 1), s));
+    if (has_slots) SA_TRY_HIP(sa::launch_csr_transpose(p, 0, p.T, nk, blk_base, row_ptr, entries, ws + L.csr_ws, ks));
+    else SA_TRY_HIP(sa::launch_fill_zero(reinterpret_cast<float*>(row_ptr), (size_t)(nk + 1), ks));
     SA_TRY_HIP(sa::launch_blk_chunks(row_ptr, nk, reinterpret_cast<int*>(ws + L.bcnt), ba.chunk_base,
-                                     reinterpret_cast<int*>(ws + L.bscan), s));
+                                     reinterpret_cast<int*>(ws + L.bscan), ks));
     if (has_slots) {
-      SA_TRY_HIP(sa::launch_blk_dkv(p, ba, s));
+      SA_TRY_HIP(sa::launch_blk_dkv(p, ba, ks));
+    }
+    w.det = 1;
+    w.dq_only = 1;
+    // the timed "main" kernel of this path: the dQ pass (the larger one)
+    if (ev_main_start) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_start), s));
+    SA_TRY_HIP(sa::blk_dq_supported(p) ? sa::launch_blk_dq(p, w, s) : sa::launch_bwd_rows(p, w, s));
+    if (ev_main_stop) SA_TRY_HIP(hipEventRecord(reinterpret_cast<hipEvent_t>(ev_main_stop), s));
+    SA_TRY_HIP(l1_norm());
+    if (side) {
+      SA_TRY_HIP(hipEventRecord(side->ev_join, side->s));
+      SA_TRY_HIP(hipStreamWaitEvent(s, side->ev_join, 0));
     }
     SA_TRY_HIP(sa::launch_blk_sum_cast(p, ba, nrows, static_cast<bf16*>(a->dk), static_cast<bf16*>(a->dv), s));
     return SA_OK;
@@ -663,6 +738,16 @@ sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a,
     SA_TRY_HIP(sa::launch_cast(acc + r.n_kv_out * L.RW, a->d_cmp_kv, (size_t)(r.n_out_rows - r.n_kv_out) * L.RW,
                                p.fp16, s));
   return SA_OK;
+}
+
+}  // namespace sa
+
+extern "C" {
+
+sa_status_t sparse_attn_bwd_timed(const sa_desc_t* desc, const sa_bwd_args_t* a, void* workspace,
+                                  size_t workspace_bytes, void* stream, void* ev_main_start,
+                                  void* ev_main_stop) {
+  return sa::bwd_entry(desc, a, workspace, workspace_bytes, stream, ev_main_start, ev_main_stop, 1);
 }
 
 sa_status_t sparse_attn_bwd(const sa_desc_t* desc, const sa_bwd_args_t* a, void* workspace,

@@ -14,6 +14,11 @@
 
 #include <hip/hip_runtime.h>
 
+namespace sa {
+sa_status_t bwd_entry(const sa_desc_t* desc, const sa_bwd_args_t* a, void* workspace, size_t workspace_bytes,
+                      void* stream, void* ev_main_start, void* ev_main_stop, int allow_side);
+}
+
 namespace {
 
 constexpr size_t kScratchBytes = size_t(128) << 20;   // 128 MiB per GPU
@@ -67,10 +72,11 @@ sa_status_t sparse_attn_bwd_noalloc(const sa_desc_t* desc, const sa_bwd_args_t* 
   void* ws = nullptr;
   st = scratch_address(dev, &ws);
   if (st != SA_OK) return st;
-  // the same launch sequence as sparse_attn_bwd, on the fixed workspace; it
+  // the same launch sequence as sparse_attn_bwd, every launch on the
+  // caller's stream (no library-owned stream), on the fixed workspace; it
   // clears whatever must start at zero itself (it never relies on the
   // contents a previous call left)
-  return sparse_attn_bwd(desc, args, ws, kScratchBytes, stream);
+  return sa::bwd_entry(desc, args, ws, kScratchBytes, stream, nullptr, nullptr, 0);
 }
 
 }  // extern "C"
