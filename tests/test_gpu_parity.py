@@ -98,6 +98,25 @@ def test_bwd_deterministic_mode_is_bitwise_repeatable(name):
             assert np.array_equal(runs[0][k].view(np.uint32), r[k].view(np.uint32)), k
 
 
+def test_bwd_block_side_stream_matches_caller_stream(monkeypatch):
+    """Block selection, deterministic mode: the key-major chain on the
+    library's side stream (the default) gives bitwise the outputs of every
+    launch on the caller's stream (SPARSE_ATTN_SIDE_STREAM=0), with and
+    without the L1-norm outputs."""
+    wl = SMALL["block_gqa_d128"]
+    inp = W.make_inputs(wl)
+    pb, Ob, Lb = U.oracle_fwd_rounded(inp)
+    for l1 in (False, True):
+        U.say(f"[side] block_gqa_d128 l1={int(l1)}")
+        monkeypatch.setenv("SPARSE_ATTN_SIDE_STREAM", "0")
+        ref = U.gpu_bwd(wl, inp, Ob, Lb, B.DKV_DETERMINISTIC, l1=l1)
+        monkeypatch.setenv("SPARSE_ATTN_SIDE_STREAM", "1")
+        got = U.gpu_bwd(wl, inp, Ob, Lb, B.DKV_DETERMINISTIC, l1=l1)
+        assert set(ref) == set(got)
+        for k in ref:
+            assert np.array_equal(ref[k].view(np.uint32), got[k].view(np.uint32)), k
+
+
 @pytest.mark.parametrize("mode", list(MODES))
 def test_bwd_edge_shuffled_padding_duplicates_empty_rows(mode):
     """-1 in any slot, a duplicated index, an out-of-range index, and rows
