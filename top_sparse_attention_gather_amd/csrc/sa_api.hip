@@ -679,6 +679,8 @@ sa_status_t bwd_entry(const sa_desc_t* desc, const sa_bwd_args_t* a, void* works
     if (has_slots) {
       SA_TRY_HIP(sa::launch_blk_dkv(p, ba, ks));
     }
+    // the chunk sums and cast need only the key-major pass
+    SA_TRY_HIP(sa::launch_blk_sum_cast(p, ba, nrows, static_cast<bf16*>(a->dk), static_cast<bf16*>(a->dv), ks));
     w.det = 1;
     w.dq_only = 1;
     // the timed "main" kernel of this path: the dQ pass (the larger one)
@@ -690,7 +692,6 @@ sa_status_t bwd_entry(const sa_desc_t* desc, const sa_bwd_args_t* a, void* works
       SA_TRY_HIP(hipEventRecord(side->ev_join, side->s));
       SA_TRY_HIP(hipStreamWaitEvent(s, side->ev_join, 0));
     }
-    SA_TRY_HIP(sa::launch_blk_sum_cast(p, ba, nrows, static_cast<bf16*>(a->dk), static_cast<bf16*>(a->dv), s));
     return SA_OK;
   }
   w.det = 1;
