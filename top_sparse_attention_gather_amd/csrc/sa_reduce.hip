@@ -58,23 +58,35 @@ constexpr int kBatch = 16;  // partial rows whose loads are in flight together
 // are then added in sub-group order.  Short rows (few columns) otherwise
 // leave most of the GPU idle while the longest list is walked one batch
 // after another, each batch waiting for its entries and then its rows.
-template <typename PT, bool SPLIT>
+// NSUB > 1 (rows of a wave or more, e.g. the 576-column bf16 rows of the
+// shared-KV kernel): NSUB groups of TPR threads per output row take its
+// list in interleaved batches (group q: batches q, q + NSUB, ...), and
+// their sums are added in group order through LDS.  The longest lists
+// (several thousand entries on the shared-KV workloads) otherwise set the
+// kernel's time, one batch after another.
+constexpr int kRedLds = 4096;   // floats of LDS for the NSUB > 1 group sums
+constexpr int kRedSub = 2;      // NSUB of the wide bf16 rows
+template <typename PT, bool SPLIT, int NSUB>
 __global__ void reduce_kernel(Params p, ReduceArgs r) {
+  static_assert(!SPLIT || NSUB == 1, "one split form at a time");
   constexpr int kPer = Vec8<PT>::kPer;
   const int tpr = r.RW / kPer;
-  const int grp = SPLIT ? 64 : tpr;                      // threads per output row
-  const int nsg = SPLIT ? 64 / tpr : 1;                  // sub-groups per output row
-  const int sg = SPLIT ? (int)(threadIdx.x & 63) / tpr : 0;
+  const int grp = SPLIT ? 64 : tpr * NSUB;               // threads per output row
+  const int nsg = SPLIT ? 64 / tpr : NSUB;               // sub-groups per output row
+  const int sg = SPLIT ? (int)(threadIdx.x & 63) / tpr : (int)(threadIdx.x % grp) / tpr;
   const int sub = threadIdx.x % tpr;
-  const long long lin = (long long)blockIdx.x * (blockDim.x / grp) + threadIdx.x / grp;
-  // SPLIT: lin is uniform over the wave, so whole waves leave here
-  if (lin >= r.n_out_rows || threadIdx.x / grp >= blockDim.x / grp) return;
+  const int rpb = blockDim.x / grp;                      // output rows per block
+  const long long lin = (long long)blockIdx.x * rpb + threadIdx.x / grp;
+  const bool valid = lin < r.n_out_rows && (int)(threadIdx.x / grp) < rpb;
+  // SPLIT: lin is uniform over the wave, so whole waves leave here (NSUB >
+  // 1: every thread stays for the barrier of the group sums)
+  if (NSUB == 1 && !valid) return;
   // Heavy rows first: the cmp rows (each named by the cmp slots of many
   // queries) are scheduled before the window rows (at most win_left + 1 +
   // win_right partials each), so the long sums do not form the grid's tail.
   // A bijection on the output rows; each row's summation order is unchanged.
   const long long n_cmp_out = r.n_out_rows - r.n_kv_out;
-  const long long orow = lin < n_cmp_out ? r.n_kv_out + lin : lin - n_cmp_out;
+  const long long orow = !valid ? 0 : lin < n_cmp_out ? r.n_kv_out + lin : lin - n_cmp_out;
   const int col = sub * kPer;
   const PT* part = static_cast<const PT*>(r.partial);
   float acc[kPer];
@@ -100,6 +112,7 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
   // partial row of position `pos` of chunk-local (token, kv head) row lrow
   auto offset_of = [&](long long lrow, int pos) -> long long { return (lrow * npos + pos) * r.RW + col; };
 
+  if (valid) {
   const bool is_cmp = orow >= r.n_kv_out;   // cmp rows follow the kv rows
   if (!is_cmp && p.select == kSelWindowCmp) {
     // window keys: query tokens t with t - win_left <= j <= t + win_right
@@ -129,7 +142,7 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
     // only query tokens of this chunk contribute
     tl_lo = max(tl_lo, r.t0 - L.q_base);
     tl_hi = min(tl_hi, r.t0 + r.Tc - 1 - L.q_base);
-    for (int tb = tl_lo; tb <= tl_hi; tb += kBatch) {
+    for (int tb = tl_lo + sg * kBatch; tb <= tl_hi; tb += nsg * kBatch) {
       long long off[kBatch];
       bool ok[kBatch];
 #pragma unroll
@@ -165,7 +178,7 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
       const int off = jl % p.bs;
       const int eb = r.row_ptr[bkey];
       const int ee = jl < L.kv_len ? r.row_ptr[bkey + 1] : eb;   // rows past the used ones: nothing
-      for (int e = eb; e < ee; e += kBatch) {
+      for (int e = eb + sg * kBatch; e < ee; e += nsg * kBatch) {
         long long offs[kBatch];
         bool ok[kBatch];
 #pragma unroll
@@ -203,7 +216,7 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
         // division-free form of this offset, slot + (row + 1) nwin - row0
         // npos, measured slower here: 4.1 against 3.3 ms on the window+cmp
         // varlen shape.)
-        for (int e = eb; e < ee; e += kBatch) {
+        for (int e = eb + sg * kBatch; e < ee; e += nsg * kBatch) {
           long long offs[kBatch];
           bool ok[kBatch];
 #pragma unroll
@@ -218,6 +231,7 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
       }
     }
   }
+  }   // valid
   if constexpr (SPLIT) {
     // sub-group sums in sub-group order (lane sub + q * tpr: sub-group q)
 #pragma unroll
@@ -227,6 +241,21 @@ __global__ void reduce_kernel(Params p, ReduceArgs r) {
       acc[i] = t;
     }
     if (sg != 0) return;
+  }
+  if constexpr (NSUB > 1) {
+    // group sums in group order: groups 1.. through LDS, added by group 0
+    __shared__ float red[kRedLds];
+    const int slot = (int)(threadIdx.x / grp) * (NSUB - 1);
+    if (valid && sg > 0) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) red[(slot + sg - 1) * r.RW + col + i] = acc[i];
+    }
+    __syncthreads();
+    if (!valid || sg != 0) return;
+#pragma unroll
+    for (int q = 1; q < NSUB; ++q)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] += red[(slot + q - 1) * r.RW + col + i];
   }
   float* dst = r.acc + orow * (long long)r.RW + col;
   if (r.accumulate) {
@@ -286,16 +315,22 @@ hipError_t launch_reduce(const Params& p, const ReduceArgs& r, hipStream_t s) {
   // token selection: every output row takes the CSR branch, which is the
   // one that splits its list
   const bool split = p.select == kSelToken && tpr < 64 && 64 % tpr == 0;
-  const int grp = split ? 64 : tpr;
+  // bf16 rows of more than a wave (the shared-KV kernel's 576 columns):
+  // kRedSub groups per row, when their sums fit the LDS of a block
+  const int nsub = !split && r.partial_bf16 && tpr >= 64 ? kRedSub : 1;
+  const int grp = split ? 64 : tpr * nsub;
   const int rpw = std::max(1, 512 / grp);
   const int threads = grp * rpw;
   const unsigned blocks = (unsigned)((r.n_out_rows + rpw - 1) / rpw);
+  if (nsub > 1 && rpw * (nsub - 1) * r.RW > kRedLds) return hipErrorInvalidValue;
   if (r.partial_bf16) {
-    if (split) hipLaunchKernelGGL((reduce_kernel<bf16, true>), dim3(blocks), dim3(threads), 0, s, p, r);
-    else hipLaunchKernelGGL((reduce_kernel<bf16, false>), dim3(blocks), dim3(threads), 0, s, p, r);
+    if (split) hipLaunchKernelGGL((reduce_kernel<bf16, true, 1>), dim3(blocks), dim3(threads), 0, s, p, r);
+    else if (nsub > 1)
+      hipLaunchKernelGGL((reduce_kernel<bf16, false, kRedSub>), dim3(blocks), dim3(threads), 0, s, p, r);
+    else hipLaunchKernelGGL((reduce_kernel<bf16, false, 1>), dim3(blocks), dim3(threads), 0, s, p, r);
   } else {
-    if (split) hipLaunchKernelGGL((reduce_kernel<float, true>), dim3(blocks), dim3(threads), 0, s, p, r);
-    else hipLaunchKernelGGL((reduce_kernel<float, false>), dim3(blocks), dim3(threads), 0, s, p, r);
+    if (split) hipLaunchKernelGGL((reduce_kernel<float, true, 1>), dim3(blocks), dim3(threads), 0, s, p, r);
+    else hipLaunchKernelGGL((reduce_kernel<float, false, 1>), dim3(blocks), dim3(threads), 0, s, p, r);
   }
   return hipGetLastError();
 }
