@@ -336,6 +336,19 @@ def test_bwd_parity_nsa_block_full_size_sampled(mode):
     _sampled_full_size_case(W.WORKLOADS["nsa_block_gqa"], dkv_mode=MODES[mode])
 
 
+def test_bwd_parity_nsa_block_full_size_every_row():
+    """The NSA-style block-sparse GQA workload at its full size with every
+    token contributing: every element of dq, dK and dV against the oracle
+    (O/lse from the oracle's forward, rounded to bf16), in the deterministic
+    and the atomic dK/dV modes.  The oracle runs once for both (all 8192
+    tokens, 1024 positions each)."""
+    wl = W.WORKLOADS["nsa_block_gqa"]
+    U.say(f"[full] {wl.name}: oracle forward and backward on every token")
+    case = U.oracle_case(wl, _full_inputs(wl))
+    for mode in (B.DKV_DETERMINISTIC, B.DKV_ATOMIC):
+        U.run_full_case(wl, dkv_mode=mode, oracle=case)
+
+
 MLA_MODES = dict(MODES, xcd=B.DKV_ATOMIC_XCD)
 
 
