@@ -366,6 +366,57 @@ def test_bwd_parity_mla_8k_full_size_sampled(mode):
     _sampled_full_size_case(W.WORKLOADS["mla_token_8k"], dkv_mode=MLA_MODES[mode])
 
 
+def _oracle_every_token(wl, inputs, chunk=1024):
+    """The oracle's forward and backward over every token, in token chunks
+    with a progress line after each.  The backward's outputs are sums of
+    per-token terms (dq rows of different tokens are disjoint), so the
+    chunks' results add up to the oracle's result over all tokens."""
+    pb = O.Problem(inputs)
+    T = wl.total_q
+    outs, lses = [], []
+    for t0 in range(0, T, chunk):
+        o, l = O.sparse_fwd(pb, range(t0, min(T, t0 + chunk)))
+        outs.append(o)
+        lses.append(l)
+        U.say(f"[full] {wl.name}: oracle forward {min(T, t0 + chunk)}/{T}")
+    out_ref, lse_ref = np.concatenate(outs), np.concatenate(lses)
+    Ob, Lb = O.round_fwd_outputs(out_ref, lse_ref, torch.bfloat16)
+    ref = None
+    for t0 in range(0, T, chunk):
+        part = O.sparse_bwd(pb, Ob, Lb, tokens=range(t0, min(T, t0 + chunk)))
+        if ref is None:
+            ref = part
+        else:
+            for k in ref:
+                ref[k] += part[k]
+        del part
+        U.say(f"[full] {wl.name}: oracle backward {min(T, t0 + chunk)}/{T}")
+    return out_ref, lse_ref, Ob, Lb, ref
+
+
+@pytest.mark.parametrize("name", ["mla_token_8k", "mla_cmp_sinks_varlen"])
+def test_mla_full_size_every_row(name):
+    """An MLA workload at its full size (8192 tokens at top-2048; window +
+    cmp with sinks over varlen {1024, 3000, 6000, 16000}) with every token
+    contributing: the GPU forward's O and lse on every row, and every element
+    of the backward's outputs (dq, dKV, and dCmpKV and dSinks where the
+    workload has them) in the deterministic and the atomic dK/dV modes,
+    against the oracle, which runs once per workload (~1.5-2 minutes on 16
+    threads)."""
+    wl = W.WORKLOADS[name]
+    inputs = _full_inputs(wl)
+    out_ref, lse_ref, Ob, Lb, ref = _oracle_every_token(wl, inputs)
+    dev = B.device_tensors(inputs)
+    o, lse = B.sparse_attn_fwd(B.make_desc(wl), dev)
+    torch.cuda.synchronize()
+    res = check_close(f"{wl.name}:o", o.float().cpu().numpy(), out_ref)
+    U.say(f"  {wl.name} o: max_err {res[0]:.3e} (bound {res[1]:.3e}) rel_frob {res[2]:.3e}")
+    np.testing.assert_allclose(lse.cpu().numpy(), lse_ref, rtol=0, atol=2e-5 * max(1.0, np.abs(lse_ref).max()))
+    del o, lse, dev
+    for mode in (B.DKV_DETERMINISTIC, B.DKV_ATOMIC):
+        U.run_full_case(wl, dkv_mode=mode, oracle=(inputs, Ob, Lb, ref))
+
+
 @pytest.mark.parametrize("name", ["mla_token_8k", "nsa_block_gqa", "mla_cmp_sinks_varlen"])
 def test_softmax_l1_full_size_sampled(name):
     """Softmax L1-norm outputs at full size in the deterministic launch
